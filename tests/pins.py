@@ -1,0 +1,321 @@
+"""Pins of the fp64 oracle against what the HYPIC pages and plain mathematics fix.
+
+Every check takes the path of an oracle build, so the same checks run on the
+real oracle (tests/test_oracle_pins.py) and on builds with a planted mistake
+(tests/test_oracle_mutants.py), where at least one of them must fail.
+
+Sources (page "HYPIC ... reading notes" unless noted):
+  worked example ..... ch.2 sec.2, the 1-D teaching example
+  Table 2 ............ ch.1 sec.2, Eqs. (4)-(5), Table 2
+  22 % ............... aibase news article (page 2)
+  affine summary ..... ch.2 sec.2 (T_C, S_{C|0}, F_C)
+  composition law .... ch.2 sec.2 (pairwise law, associative, not commutative)
+  Eq. (6) ............ ch.2 sec.2
+  T_i = I reduction .. ch.1 sec.2
+  family forms ....... ch.2 sec.3, Table 1
+  conv warm-up ....... ch.2 sec.6
+"""
+import json
+import os
+
+import numpy as np
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- helpers
+
+def one_unit(path, rule, gate_kind, k, v, beta, g, S_init=None):
+    """Pair (T, S0) and, if S_init is given, the end state from S_init,
+    for a single unit given as k [m, dk], v [m, dv], beta [m], g [m] / [m, dk]."""
+    k = np.ascontiguousarray(k, dtype=np.float64)[:, None, :]
+    v = np.ascontiguousarray(v, dtype=np.float64)[:, None, :]
+    m, _, dk = k.shape
+    dv = v.shape[2]
+    b = np.ascontiguousarray(beta if beta is not None else np.zeros(m), dtype=np.float64)[:, None]
+    g = np.asarray(g, dtype=np.float64)
+    g = np.ascontiguousarray(g[:, None, :] if gate_kind == "diag" else g[:, None])
+    u = oracle.Units([(0, m, 0, 0)], 1, 1, dk, dv, gate_kind)
+    T, S0 = oracle.build_units(rule, gate_kind, u, dk, dv, k, v, b, g, path)
+    end = None
+    if S_init is not None:
+        S = np.array(S_init, dtype=np.float64, copy=True)[None]
+        oracle.recur_units(rule, gate_kind, u, dk, dv, k, v, b, g, S, path=path)
+        end = S[0]
+    return T[0], S0[0], end
+
+
+def dense_transition(rule, gate_kind, k, beta, g):
+    dk = k.shape[0]
+    G = np.diag(g) if gate_kind == "diag" else g * np.eye(dk)
+    if rule == "decay":
+        return G
+    P = np.eye(dk) - beta * np.outer(k, k)
+    return P @ G if gate_kind == "diag" else g * P
+
+
+def dense_write(rule, k, v, beta):
+    return np.outer(k, v) * (beta if rule == "delta" else 1.0)
+
+
+def rand_unit(rng, rule, gate_kind, m, dk, dv, slow=False):
+    k = rng.standard_normal((m, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = rng.standard_normal((m, dv))
+    beta = rng.uniform(0.1, 0.9, m) if rule == "delta" else None
+    lo = 0.9 if slow else 0.3
+    g = rng.uniform(lo, 1.0, (m, dk) if gate_kind == "diag" else m)
+    return k, v, beta, g
+
+
+FAMILIES = [("decay", "scalar"), ("decay", "diag"), ("delta", "scalar"), ("delta", "diag")]
+
+
+# ------------------------------------------------------------------- pins
+
+def pin_worked_example(path):
+    gx = _golden("worked_example.json")
+    m = len(gx["token_decay"])
+    T, S0, end = one_unit(path, "decay", "scalar", np.ones((m, 1)),
+                          np.array(gx["token_write"])[:, None], None,
+                          np.array(gx["token_decay"]), S_init=[[gx["prefix_state"]]])
+    assert abs(T[0, 0] - gx["T_C"]) < 1e-15, T
+    assert abs(S0[0, 0] - gx["S_C0"]) < 1e-15, S0
+    S = oracle.compose(T[None, None], S0[None, None], np.array([[[gx["prefix_state"]]]]),
+                       path=path)
+    assert abs(S[0, 0, 0] - gx["composed"]) < 1e-14, S
+    assert abs(end[0, 0] - gx["composed"]) < 1e-14, end
+    parts = np.stack([np.full((1, 1, 1), gx["prefix_state"]), S0[None]])
+    naive = oracle.naive_sum(parts)
+    assert abs(naive[0, 0, 0] - gx["naive_sum"]) < 1e-14
+
+
+def _two_segment_ratio(path, gamma, n1, n2, d=8, seed=0):
+    """||Delta|| / ||S_{C1|0}|| with Delta = true - naive, from oracle runs."""
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((n1 + n2, d))
+    v = rng.standard_normal((n1 + n2, d))
+    g = np.full(n1 + n2, gamma)
+    _, S1, _ = one_unit(path, "decay", "scalar", k[:n1], v[:n1], None, g[:n1])
+    T2, S2, _ = one_unit(path, "decay", "scalar", k[n1:], v[n1:], None, g[n1:])
+    _, true, _ = one_unit(path, "decay", "scalar", k, v, None, g)
+    delta = true - (S1 + S2)
+    return np.linalg.norm(delta) / np.linalg.norm(S1), delta, T2, S1
+
+
+def pin_table2(path):
+    gx = _golden("table2_naive_error.json")
+    gamma = 1.0 - 2.0 ** -gx["gamma_exponent"]
+    for n2, printed in zip(gx["C2_len"], gx["ratio_printed"]):
+        r, _, _, _ = _two_segment_ratio(path, gamma, 300, n2)
+        assert round(r, gx["printed_decimals"]) == printed, (n2, r, printed)
+        assert abs(r - (1.0 - gamma ** n2)) < 1e-10, (n2, r)
+
+
+def pin_news_22pct(path):
+    gx = _golden("news_slow_decay_22pct.json")
+    gamma = 1.0 - 2.0 ** -gx["gamma_exponent"]
+    r, _, _, _ = _two_segment_ratio(path, gamma, 256, gx["C2_len"], seed=1)
+    assert round(100 * r) == gx["ratio_percent_printed"], r
+
+
+def pin_naive_error_identity(path):
+    """Delta = (T_{C2} - I) S_{C1|0} (Eq. (4)), for every family."""
+    rng = np.random.default_rng(2)
+    for rule, gk in FAMILIES:
+        k, v, b, g = rand_unit(rng, rule, gk, 24, 5, 3, slow=True)
+        _, S1, _ = one_unit(path, rule, gk, k[:10], v[:10], None if b is None else b[:10], g[:10])
+        T2, S2, _ = one_unit(path, rule, gk, k[10:], v[10:], None if b is None else b[10:], g[10:])
+        _, true, _ = one_unit(path, rule, gk, k, v, b, g)
+        delta = true - (S1 + S2)
+        assert np.allclose(delta, (T2 - np.eye(5)) @ S1, atol=1e-12, rtol=0), (rule, gk)
+
+
+def pin_brute_force(path):
+    """Dense products of explicitly formed T_i (ch.2 sec.2 expansion)."""
+    rng = np.random.default_rng(3)
+    for rule, gk in FAMILIES:
+        for m, dk, dv in [(1, 2, 3), (5, 3, 2), (8, 4, 4)]:
+            k, v, b, g = rand_unit(rng, rule, gk, m, dk, dv)
+            Ts = [dense_transition(rule, gk, k[t], None if b is None else b[t], g[t])
+                  for t in range(m)]
+            us = [dense_write(rule, k[t], v[t], None if b is None else b[t]) for t in range(m)]
+            T_ref = np.eye(dk)
+            for t in range(m):
+                T_ref = Ts[t] @ T_ref
+            S_ref = np.zeros((dk, dv))
+            for t in range(m):
+                P = np.eye(dk)
+                for s in range(m - 1, t, -1):   # T_m ... T_{t+1}
+                    P = P @ Ts[s]
+                S_ref += P @ us[t]
+            if m >= 2:
+                assert np.allclose(np.linalg.multi_dot(Ts[::-1]), T_ref, atol=1e-14)
+            T, S0, _ = one_unit(path, rule, gk, k, v, b, g)
+            assert np.allclose(T, T_ref, atol=1e-13, rtol=0), (rule, gk, m)
+            assert np.allclose(S0, S_ref, atol=1e-13, rtol=0), (rule, gk, m)
+
+
+def pin_affine(path):
+    """Recurrence from any S_init equals T_C S_init + S_{C|0} (F_C)."""
+    rng = np.random.default_rng(4)
+    for rule, gk in FAMILIES:
+        k, v, b, g = rand_unit(rng, rule, gk, 40, 6, 5, slow=True)
+        S_init = rng.standard_normal((6, 5))
+        T, S0, end = one_unit(path, rule, gk, k, v, b, g, S_init=S_init)
+        assert np.allclose(end, T @ S_init + S0, atol=1e-12, rtol=0), (rule, gk)
+
+
+def pin_decay_closed_forms(path):
+    """Scalar decay: T = gamma^m I, S0 = K^T diag(gamma^(m-t)) V.
+    Diagonal gate: T = diag(exp(cl_m)), S0 = (K * exp(cl_m - cl_t))^T V."""
+    rng = np.random.default_rng(5)
+    m, dk, dv = 50, 6, 4
+    k = rng.standard_normal((m, dk))
+    v = rng.standard_normal((m, dv))
+    gamma = 0.97
+    T, S0, _ = one_unit(path, "decay", "scalar", k, v, None, np.full(m, gamma))
+    w = gamma ** (m - 1 - np.arange(m))
+    assert np.allclose(T, gamma ** m * np.eye(dk), rtol=1e-13, atol=0)
+    assert np.allclose(S0, k.T @ (w[:, None] * v), rtol=1e-12, atol=1e-13)
+    g = rng.uniform(0.8, 1.0, (m, dk))
+    cl = np.cumsum(np.log(g), axis=0)
+    T, S0, _ = one_unit(path, "decay", "diag", k, v, None, g)
+    assert np.allclose(T, np.diag(np.exp(cl[-1])), rtol=1e-12, atol=0)
+    assert np.allclose(S0, (k * np.exp(cl[-1] - cl)).T @ v, rtol=1e-12, atol=1e-13)
+
+
+def pin_identity_transition(path):
+    """With T_i = I the zero-initial end states simply add (ch.1 sec.2)."""
+    rng = np.random.default_rng(6)
+    k = rng.standard_normal((30, 4))
+    v = rng.standard_normal((30, 3))
+    one = np.ones(30)
+    T, S0, _ = one_unit(path, "decay", "scalar", k, v, None, one)
+    _, S1, _ = one_unit(path, "decay", "scalar", k[:12], v[:12], None, one[:12])
+    _, S2, _ = one_unit(path, "decay", "scalar", k[12:], v[12:], None, one[12:])
+    assert np.allclose(T, np.eye(4), atol=0, rtol=0)
+    assert np.allclose(S0, k.T @ v, atol=1e-12)
+    assert np.allclose(S0, S1 + S2, atol=1e-12)
+
+
+def pin_composition_laws(path):
+    """Pairwise law, associativity, Eq. (6) and non-commutativity."""
+    rng = np.random.default_rng(7)
+    for rule, gk in FAMILIES:
+        parts = []
+        for m in (9, 13, 7):
+            k, v, b, g = rand_unit(rng, rule, gk, m, 4, 3, slow=True)
+            parts.append(one_unit(path, rule, gk, k, v, b, g)[:2])
+        (TA, BA), (TB, BB), (TC, BC) = parts
+        S_s = rng.standard_normal((4, 3))
+        seq = oracle.compose(np.array([[TA], [TB], [TC]]), np.array([[BA], [BB], [BC]]),
+                             S_s[None], path=path)[0]
+        # (C o B) o A  vs  C o (B o A), pair law (T_B T_A, T_B B_A + B_B)
+        TBA, BBA = TB @ TA, TB @ BA + BB
+        left = TC @ (TBA @ S_s + BBA) + BC
+        TCB, BCB = TC @ TB, TC @ BB + BC
+        right = TCB @ (TA @ S_s + BA) + BCB
+        eq6 = (TC @ TB @ TA) @ S_s + (TC @ TB) @ BA + TC @ BB + BC
+        for x in (left, right, eq6):
+            assert np.allclose(seq, x, atol=1e-12), (rule, gk)
+        swapped = oracle.compose(np.array([[TB], [TA], [TC]]), np.array([[BB], [BA], [BC]]),
+                                 S_s[None], path=path)[0]
+        assert np.linalg.norm(swapped - seq) > 1e-3 * np.linalg.norm(seq), (rule, gk)
+
+
+def pin_gdn_bounds(path):
+    """||k|| = 1, beta in [0,1]: ||T_i||_2 = alpha_i, hence ||T_C||_2 <= prod alpha.
+    DeltaNet with beta = 1 makes T_i a projector that annihilates k."""
+    rng = np.random.default_rng(8)
+    k, v, b, g = rand_unit(rng, "delta", "scalar", 30, 8, 4)
+    T, _, _ = one_unit(path, "delta", "scalar", k, v, b, g)
+    assert np.linalg.norm(T, 2) <= np.prod(g) * (1 + 1e-12)
+    T1, _, _ = one_unit(path, "delta", "scalar", k[:1], v[:1], np.ones(1), np.ones(1))
+    assert np.allclose(T1 @ T1, T1, atol=1e-14)
+    assert np.allclose(T1 @ k[0], 0.0, atol=1e-14)
+    assert abs(np.trace(T1) - 7.0) < 1e-13
+
+
+def pin_conv(path):
+    """Depthwise causal conv against numpy's full convolution, with history."""
+    rng = np.random.default_rng(9)
+    n, C, W = 11, 5, 4
+    x = rng.standard_normal((n, C))
+    w = rng.standard_normal((C, W))
+    hist = rng.standard_normal((W - 1, C))
+    y = oracle.causal_conv(x, w, hist, path)
+    y0 = oracle.causal_conv(x, w, None, path)
+    xe = np.concatenate([hist, x])
+    for c in range(C):
+        full = np.convolve(xe[:, c], w[c, ::-1])          # y_t = sum_j w_j x_{t-(W-1)+j}
+        assert np.allclose(y[:, c], full[W - 1:W - 1 + n], atol=1e-13)
+        full0 = np.convolve(x[:, c], w[c, ::-1])
+        assert np.allclose(y0[:, c], full0[:n], atol=1e-13)
+
+
+def pin_l2norm(path):
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((7, 3, 9))
+    y = oracle.l2norm_rows(x, path)
+    assert np.allclose(np.linalg.norm(y, axis=-1), 1.0, atol=1e-14)
+    assert np.allclose(y * np.linalg.norm(x, axis=-1, keepdims=True), x, atol=1e-14)
+
+
+def pin_compose_equals_full(path):
+    """Composition = full recompute, with conv warm-up and seams (w >= W-1),
+    and differs when the seam is narrower than the conv history (ch.2 sec.6)."""
+    import synth
+    import torch
+    for seam_w, should_match in ((8, True), (3, True), (0, False), (2, False)):
+        wl = synth.gdn(11, [40, 37, 45], 2, 2, 8, torch.float32, alpha_div=64.0,
+                       conv_w=4, seam_w=seam_w)
+        T, S0 = oracle.build_pairs(wl, path=path)
+        S = oracle.compose(T, S0, wl=wl, seams=seam_w > 0, path=path)
+        F = oracle.full_recompute(wl, path=path)
+        err = oracle.relF(S, F)
+        if should_match:
+            assert err < 1e-12, (seam_w, err)
+        else:
+            assert err > 1e-4, (seam_w, err)
+    wl = synth.gdn(12, [33, 50, 21, 64], 1, 2, 8, torch.float32, alpha_div=16.0)
+    S_init = np.random.default_rng(13).standard_normal((2, 8, 8))
+    T, S0 = oracle.build_pairs(wl, path=path)
+    S = oracle.compose(T, S0, S_init, path=path)
+    F = oracle.full_recompute(wl, S_init, path=path)
+    assert oracle.relF(S, F) < 1e-12
+
+
+def pin_readout(path):
+    """o_t = q_t^T S_t with the post-update state (Eq. (2))."""
+    rng = np.random.default_rng(14)
+    for rule, gk in FAMILIES:
+        m, dk, dv = 6, 4, 3
+        k, v, b, g = rand_unit(rng, rule, gk, m, dk, dv)
+        q = rng.standard_normal((m, 1, dk))
+        S_ref = rng.standard_normal((dk, dv))
+        S = S_ref.copy()[None]
+        o = np.zeros((m, 1, dv))
+        bb = np.zeros((m, 1)) if b is None else b[:, None].copy()
+        gg = g[:, None, :].copy() if gk == "diag" else g[:, None].copy()
+        u = oracle.Units([(0, m, 0, 0)], 1, 1, dk, dv, gk)
+        oracle.recur_units(rule, gk, u, dk, dv, np.ascontiguousarray(k[:, None]),
+                           np.ascontiguousarray(v[:, None]), bb, gg, S, q=q, o=o,
+                           off_q=[0], ldq=dk, off_o=[0], ldo=dv, path=path)
+        for t in range(m):
+            Tt = dense_transition(rule, gk, k[t], None if b is None else b[t], g[t])
+            S_ref = Tt @ S_ref + dense_write(rule, k[t], v[t], None if b is None else b[t])
+            assert np.allclose(o[t, 0], q[t, 0] @ S_ref, atol=1e-13), (rule, gk, t)
+        assert np.allclose(S[0], S_ref, atol=1e-13)
+
+
+ALL = [pin_readout, pin_worked_example, pin_table2, pin_news_22pct, pin_naive_error_identity,
+       pin_brute_force, pin_affine, pin_decay_closed_forms, pin_identity_transition,
+       pin_composition_laws, pin_gdn_bounds, pin_conv, pin_l2norm, pin_compose_equals_full]
