@@ -1,0 +1,217 @@
+/*
+ * hypic.h -- C ABI of the MI355X (gfx950) linear-attention state-caching library.
+ *
+ * The library implements the linear-layer hot path of HYPIC's
+ * position-independent caching (page "HYPIC ... reading notes"):
+ *
+ *   hypic_segment_build  the cached pair (T_C, S_{C|0}) of each cold segment:
+ *                        T_C = T_m ... T_1 and S_{C|0} = sum_t T_m...T_{t+1} u_t,
+ *                        the end state of S_i = T_i S_{i-1} + u_i from S_0 = 0
+ *                        (ch.1 sec.2 Eq. (2); ch.2 sec.2; ch.2 sec.4)
+ *   hypic_compose        S <- T_C S + S_{C|0} over the segments of a prompt, in
+ *                        prompt order (ch.2 sec.2, Eq. (6)), optionally with the
+ *                        seam window of every inner segment folded in first
+ *                        (ch.2 secs.5-6)
+ *   hypic_seam_advance   advance running states over a seam window: the first w
+ *                        tokens of an inner segment recomputed from the prefix
+ *                        state, with the causal-conv warm-up from the previous
+ *                        segment's tail rows (ch.2 secs.5-6)
+ *
+ * Transition families (ch.2 sec.3, Table 1), chosen by (rule, gate_kind):
+ *   DECAY + HEAD_CONST : T_i = gamma_h I,      u_i = k_i v_i^T  (RetNet)     T_C scalar
+ *   DECAY + SCALAR     : T_i = a_i I,          u_i = k_i v_i^T  (Mamba2)     T_C scalar
+ *   DECAY + DIAG       : T_i = diag(g_i),      u_i = k_i v_i^T  (GLA)        T_C diagonal
+ *   DELTA + SCALAR     : T_i = a_i(I - b_i k_i k_i^T), u_i = b_i k_i v_i^T
+ *                        (GDN; DeltaNet is a_i = 1)                           T_C dense
+ *
+ * Conventions shared by every call
+ *   - Every data pointer is a DEVICE pointer owned by the caller; arrays are
+ *     contiguous, row-major, leading index first.  Tables named "HOST" are
+ *     host arrays read before the call returns.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and never synchronise.  The library never allocates or frees
+ *     device memory; scratch is the caller's workspace (hypic_workspace_size).
+ *   - Argument errors are returned synchronously as negative hypic_status and
+ *     nothing is launched.  Launch failures return HYPIC_E_HIP.  A device fault
+ *     surfaces at the caller's next synchronisation.
+ *   - Nothing is printed and no exception crosses the boundary.  Calls are
+ *     thread-safe; calls that overlap on one device write only their own
+ *     outputs.
+ *   - Supported head dimensions: d_k = d_v in {16, 32, 64, 128}.  Other shapes
+ *     return HYPIC_E_UNSUPPORTED.  Pointers must be 16-byte aligned.
+ *   - States, transitions and pair pools are fp32.  Inputs are fp32 or bf16.
+ *     Precision: fp32 inputs are computed with fp32 matrix products (relative
+ *     Frobenius error ~1e-6); bf16 inputs use fp16 matrix-core operands with
+ *     fp32 accumulation and power-of-two block scaling (~3e-4 on S, <=1.5e-3 on
+ *     dense T_C for 4096-token segments).
+ */
+#ifndef HYPIC_H
+#define HYPIC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HYPIC_OK = 0,
+    HYPIC_E_INVALID = -1,      /* null pointer, negative or inconsistent size     */
+    HYPIC_E_UNSUPPORTED = -2,  /* valid request this build does not implement    */
+    HYPIC_E_WORKSPACE = -3,    /* workspace missing or smaller than required     */
+    HYPIC_E_HIP = -4,          /* a HIP runtime call or kernel launch failed     */
+    HYPIC_E_DEVICE = -5        /* current device is not a gfx950 GPU             */
+} hypic_status;
+
+typedef enum { HYPIC_F32 = 0, HYPIC_BF16 = 1 } hypic_dtype;
+typedef enum { HYPIC_RULE_DECAY = 0, HYPIC_RULE_DELTA = 1 } hypic_rule;
+typedef enum {
+    HYPIC_GATE_HEAD_CONST = 0, /* gate [h_v] fp32, one constant per value head   */
+    HYPIC_GATE_SCALAR = 1,     /* gate [N, h_v], one scalar per token and head   */
+    HYPIC_GATE_DIAG = 2        /* gate [N, h_v, d_k], one vector per token, head */
+} hypic_gate;
+typedef enum { HYPIC_T_SCALAR = 0, HYPIC_T_DIAG = 1, HYPIC_T_DENSE = 2 } hypic_tform;
+typedef enum {
+    HYPIC_PREC_FP32 = 0,       /* fp32 matrix products                           */
+    HYPIC_PREC_SPLIT = 1       /* fp32 operands split into bf16 hi+lo, three
+                                  products per term (relative error ~1e-5)       */
+} hypic_prec;
+
+/* Segments per kernel launch; longer tables are processed in several launches. */
+#define HYPIC_MAX_SEG_PER_LAUNCH 128
+
+/*
+ * hypic_segment_build -- the cached pair of each segment (ch.2 secs.2 and 4).
+ *
+ * Token arrays hold N rows in token order; each pair covers the tokens
+ * [seg_start[s], seg_start[s] + seg_len[s]) of those rows.  For an inner
+ * segment the range is the body after the seam window; for the first segment
+ * of a prompt it is the whole segment.
+ *
+ *   k      [N, h_k, d_k]  keys (raw conv inputs when conv_w > 0), in_dtype
+ *   v      [N, h_v, d_v]  values (raw conv inputs when conv_w > 0), in_dtype
+ *   beta   [N, h_v]       write strength in [0,1] (DELTA only, else NULL), in_dtype
+ *   gate   per gate_kind, values in (0,1]; in_dtype, except HEAD_CONST: fp32
+ *   GQA: value head h reads key head h / (h_v / h_k); h_v % h_k == 0.
+ *
+ *   conv_w     0: k, v are final.  2..4: k, v are raw rows of a depthwise causal
+ *              conv of width conv_w (y_t = sum_j w[c][j] x_{t-conv_w+1+j}, no bias,
+ *              no activation, weights conv_wk [h_k*d_k, conv_w] and
+ *              conv_wv [h_v*d_v, conv_w] fp32).  Rows before conv_from[s] read
+ *              as zero (a segment prefilled on its own).
+ *   conv_from  HOST [n_seg] (conv_w > 0 only): first row the conv may read.
+ *   k_l2norm   1: divide each key (after the conv) by its L2 norm.
+ *
+ *   T_out   [n_seg, h_v, 1 | d_k | d_k*d_k] fp32 by T form (scalar / diag / dense)
+ *   S0_out  [n_seg, h_v, d_k, d_v] fp32
+ *
+ * Workspace: hypic_workspace_size(desc, HYPIC_WS_BUILD) bytes (0 without conv
+ * or key normalisation; ws may then be NULL).  Empty ranges give T = I, S0 = 0.
+ * Errors: HYPIC_E_INVALID (null pointers, negative lengths, h_v % h_k != 0),
+ * HYPIC_E_UNSUPPORTED (dimensions, DECAY+DIAG with conv, DELTA+DIAG),
+ * HYPIC_E_WORKSPACE, HYPIC_E_HIP.
+ */
+typedef struct {
+    int32_t rule, gate_kind, in_dtype;
+    int32_t n_seg;
+    const int64_t *seg_start;  /* HOST [n_seg] */
+    const int64_t *seg_len;    /* HOST [n_seg] */
+    int32_t h_k, h_v, d_k, d_v;
+    const void *k, *v, *beta, *gate;
+    int32_t conv_w, k_l2norm;
+    const int64_t *conv_from;  /* HOST [n_seg] or NULL when conv_w == 0 */
+    const float *conv_wk, *conv_wv;
+    float *T_out, *S0_out;
+} hypic_build_desc;
+
+hypic_status hypic_segment_build(const hypic_build_desc *d, void *ws, size_t ws_bytes,
+                                 void *stream);
+
+/*
+ * Seam windows (ch.2 secs.5-6).  Window i holds the first w tokens of an inner
+ * segment and the conv_w-1 raw rows that end the previous segment (its cached
+ * tail conv state).  Only the gated-delta family (rule DELTA, scalar gate).
+ *
+ *   xk     [n_win, w, h_k, d_k]  raw (conv_w > 0) or final keys, in_dtype
+ *   xv     [n_win, w, h_v, d_v]  raw or final values, in_dtype
+ *   tail_k [n_win, conv_w-1, h_k, d_k], tail_v [n_win, conv_w-1, h_v, d_v]
+ *          (conv_w > 1 only), in_dtype
+ *   conv_wk [h_k*d_k, conv_w], conv_wv [h_v*d_v, conv_w] fp32 (conv_w > 0)
+ *   beta, alpha [n_win, w, h_v] in_dtype
+ *   q      optional [n_win, w, h_k, d_k] final queries (in_dtype);
+ *   o      optional [n_win, w, h_v, d_v] fp32 read-outs o_t = q_t^T S_t with the
+ *          post-update state (Eq. (2)); q and o are both set or both NULL.
+ *   T_w    optional [n_win, h_v, d_k, d_k] fp32 window transition
+ *   S_w0   optional [n_win, h_v, d_k, d_v] fp32 window zero-initial end state
+ *   1 <= w <= 64.
+ */
+typedef struct {
+    int32_t rule, in_dtype;
+    int32_t w, conv_w, k_l2norm;
+    int32_t h_k, h_v, d_k, d_v;
+    int32_t n_win;
+    const void *xk, *xv, *tail_k, *tail_v;
+    const float *conv_wk, *conv_wv;
+    const void *beta, *alpha;
+    const void *q;
+    float *o, *T_w, *S_w0;
+} hypic_seam_desc;
+
+/*
+ * hypic_seam_advance -- S_inout [h_v, d_k, d_v] fp32 advances over windows
+ * 0..n_win-1 in order (normally n_win = 1).  Computes the window's transition
+ * and zero-initial state and folds them into S (equal, up to rounding, to
+ * running the w tokens one by one).  Errors: HYPIC_E_INVALID,
+ * HYPIC_E_UNSUPPORTED (rule, dimensions, w > 64), HYPIC_E_HIP.
+ */
+hypic_status hypic_seam_advance(const hypic_seam_desc *d, float *S_inout, void *stream);
+
+/*
+ * hypic_compose -- fold cached pairs into a running state (Eq. (6)):
+ *   S = S_init (or 0);  for i in 0..n-1:  [seam window i-1 if i >= 1]
+ *                                         S <- T[order[i]] S + S0[order[i]]
+ *
+ *   T_pool   [n_slots, h_v, 1 | d_k | d_k*d_k] fp32 by tform
+ *   S0_pool  [n_slots, h_v, d_k, d_v] fp32
+ *   order    HOST [n]: pool slot of the i-th segment in prompt order
+ *   S_init   [h_v, d_k, d_v] fp32, or NULL for the zero state
+ *   S_out    [h_v, d_k, d_v] fp32; may equal S_init
+ *   seams    NULL, or windows for positions 1..n-1 (seams->n_win == n-1,
+ *            seams->w <= 16), dense tform only; seams->q/o/T_w/S_w0 must be
+ *            NULL here
+ *   prec     HYPIC_PREC_FP32 or HYPIC_PREC_SPLIT for the dense product
+ *
+ * Workspace: hypic_workspace_size(desc, HYPIC_WS_COMPOSE) bytes.
+ * Errors: HYPIC_E_INVALID, HYPIC_E_UNSUPPORTED, HYPIC_E_WORKSPACE, HYPIC_E_HIP.
+ */
+typedef struct {
+    int32_t tform, prec;
+    int32_t h_v, d_k, d_v;
+    int32_t n;
+    int32_t n_slots;           /* slots in the pools; every order[i] < n_slots */
+    const int32_t *order;      /* HOST [n] */
+    const float *T_pool, *S0_pool;
+    const float *S_init;
+    float *S_out;
+    const hypic_seam_desc *seams;
+} hypic_compose_desc;
+
+hypic_status hypic_compose(const hypic_compose_desc *d, void *ws, size_t ws_bytes,
+                           void *stream);
+
+#define HYPIC_WS_BUILD 0
+#define HYPIC_WS_COMPOSE 1
+/* Workspace bytes a call with this descriptor needs (0 if none). */
+size_t hypic_workspace_size(const void *desc, int which);
+
+/* Static description of a status code. */
+const char *hypic_status_string(hypic_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t hypic_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HYPIC_H */

@@ -1,0 +1,294 @@
+// abi.hip -- the extern "C" boundary of libhypic: argument validation,
+// workspace sizing and kernel dispatch.  See include/hypic.h for the contract.
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "hypic.h"
+#include "launch.h"
+
+using namespace hy;
+
+namespace {
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t esize(int dtype) { return dtype == HYPIC_BF16 ? 2 : 4; }
+
+// gfx950 check, cached per device ordinal
+hypic_status device_check()
+{
+    static std::mutex mu;
+    static int state[64];   // 0 unknown, 1 ok, 2 wrong architecture
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return HYPIC_E_HIP;
+    if (dev < 0 || dev >= 64) return HYPIC_E_DEVICE;
+    std::lock_guard<std::mutex> lk(mu);
+    if (state[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return HYPIC_E_HIP;
+        state[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    }
+    return state[dev] == 1 ? HYPIC_OK : HYPIC_E_DEVICE;
+}
+
+hypic_status from_hip(hipError_t e) { return e == hipSuccess ? HYPIC_OK : HYPIC_E_HIP; }
+
+bool build_needs_prep(const hypic_build_desc *d) { return d->conv_w > 0 || d->k_l2norm; }
+
+int64_t build_rows(const hypic_build_desc *d)
+{
+    int64_t n = 0;
+    for (int s = 0; s < d->n_seg; ++s) n += d->seg_len[s];
+    return n;
+}
+
+size_t build_ws_bytes(const hypic_build_desc *d)
+{
+    if (!build_needs_prep(d)) return 0;
+    const int64_t rows = build_rows(d);
+    const size_t kb = (size_t)rows * d->h_k * d->d_k * sizeof(float);
+    const size_t vb = (size_t)rows * d->h_v * d->d_v * sizeof(float);
+    return ((kb + 255) & ~(size_t)255) + vb;
+}
+
+hypic_status validate_build(const hypic_build_desc *d)
+{
+    if (!d) return HYPIC_E_INVALID;
+    if (d->n_seg < 0) return HYPIC_E_INVALID;
+    if (d->n_seg > 0 && (!d->seg_start || !d->seg_len)) return HYPIC_E_INVALID;
+    if (d->h_k <= 0 || d->h_v <= 0 || d->h_v % d->h_k != 0) return HYPIC_E_INVALID;
+    if (d->in_dtype != HYPIC_F32 && d->in_dtype != HYPIC_BF16) return HYPIC_E_INVALID;
+    if (d->rule != HYPIC_RULE_DECAY && d->rule != HYPIC_RULE_DELTA) return HYPIC_E_INVALID;
+    if (d->gate_kind < HYPIC_GATE_HEAD_CONST || d->gate_kind > HYPIC_GATE_DIAG) return HYPIC_E_INVALID;
+    if (d->conv_w < 0 || d->conv_w > 4) return HYPIC_E_INVALID;
+    if (d->d_k != d->d_v || !dim_ok(d->d_k)) return HYPIC_E_UNSUPPORTED;
+    if (d->rule == HYPIC_RULE_DELTA && d->gate_kind != HYPIC_GATE_SCALAR) return HYPIC_E_UNSUPPORTED;
+    if (d->rule == HYPIC_RULE_DECAY && build_needs_prep(d)) return HYPIC_E_UNSUPPORTED;
+    if (!d->k || !d->v || !d->gate || !d->T_out || !d->S0_out) return HYPIC_E_INVALID;
+    if (d->rule == HYPIC_RULE_DELTA && !d->beta) return HYPIC_E_INVALID;
+    if (!aligned16(d->k) || !aligned16(d->v) || !aligned16(d->T_out) || !aligned16(d->S0_out))
+        return HYPIC_E_INVALID;
+    if (d->conv_w > 0 && (!d->conv_from || !d->conv_wk || !d->conv_wv)) return HYPIC_E_INVALID;
+    for (int s = 0; s < d->n_seg; ++s) {
+        if (d->seg_start[s] < 0 || d->seg_len[s] < 0 || d->seg_len[s] > INT32_MAX) return HYPIC_E_INVALID;
+        if (d->conv_w > 0 && (d->conv_from[s] < 0 || d->conv_from[s] > d->seg_start[s])) return HYPIC_E_INVALID;
+    }
+    return HYPIC_OK;
+}
+
+hypic_status validate_seams(const hypic_seam_desc *s, int h_v, int D, int max_w)
+{
+    if (!s) return HYPIC_E_INVALID;
+    if (s->rule != HYPIC_RULE_DELTA) return HYPIC_E_UNSUPPORTED;
+    if (s->in_dtype != HYPIC_F32 && s->in_dtype != HYPIC_BF16) return HYPIC_E_INVALID;
+    if (s->h_v != h_v || s->d_k != D || s->d_v != D) return HYPIC_E_INVALID;
+    if (s->h_k <= 0 || s->h_v % s->h_k != 0) return HYPIC_E_INVALID;
+    if (s->w < 1) return HYPIC_E_INVALID;
+    if (s->w > max_w) return HYPIC_E_UNSUPPORTED;
+    if (s->conv_w < 0 || s->conv_w > 4) return HYPIC_E_INVALID;
+    if (!s->xk || !s->xv || !s->beta || !s->alpha) return HYPIC_E_INVALID;
+    if (s->conv_w > 0 && (!s->conv_wk || !s->conv_wv)) return HYPIC_E_INVALID;
+    if (s->conv_w > 1 && (!s->tail_k || !s->tail_v)) return HYPIC_E_INVALID;
+    if ((s->q == nullptr) != (s->o == nullptr)) return HYPIC_E_INVALID;
+    return HYPIC_OK;
+}
+
+SeamArgs seam_args(const hypic_seam_desc *s)
+{
+    SeamArgs a;
+    a.xk = s->xk; a.xv = s->xv; a.tail_k = s->tail_k; a.tail_v = s->tail_v;
+    a.conv_wk = s->conv_wk; a.conv_wv = s->conv_wv;
+    a.beta = s->beta; a.alpha = s->alpha; a.q = s->q;
+    a.o = s->o; a.T_w = s->T_w; a.S_w0 = s->S_w0;
+    a.w = s->w; a.conv_w = s->conv_w; a.k_l2norm = s->k_l2norm; a.h_k = s->h_k; a.h_v = s->h_v;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t hypic_version(void) { return 100; }
+
+const char *hypic_status_string(hypic_status s)
+{
+    switch (s) {
+    case HYPIC_OK: return "ok";
+    case HYPIC_E_INVALID: return "invalid argument";
+    case HYPIC_E_UNSUPPORTED: return "unsupported configuration";
+    case HYPIC_E_WORKSPACE: return "workspace missing or too small";
+    case HYPIC_E_HIP: return "HIP runtime error";
+    case HYPIC_E_DEVICE: return "device is not gfx950";
+    default: return "unknown status";
+    }
+}
+
+size_t hypic_workspace_size(const void *desc, int which)
+{
+    if (!desc) return 0;
+    if (which == HYPIC_WS_BUILD) {
+        const hypic_build_desc *d = static_cast<const hypic_build_desc *>(desc);
+        if (validate_build(d) != HYPIC_OK) return 0;
+        return build_ws_bytes(d);
+    }
+    return 0;
+}
+
+hypic_status hypic_segment_build(const hypic_build_desc *d, void *ws, size_t ws_bytes, void *stream)
+{
+    hypic_status st = validate_build(d);
+    if (st != HYPIC_OK) return st;
+    const size_t need = build_ws_bytes(d);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return HYPIC_E_WORKSPACE;
+    if (d->n_seg == 0) return HYPIC_OK;
+    st = device_check();
+    if (st != HYPIC_OK) return st;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const int D = d->d_k;
+    const int in_kind = d->in_dtype == HYPIC_BF16 ? IN_BF16 : IN_F32;
+    const bool prep = build_needs_prep(d);
+    float *wk = nullptr, *wvv = nullptr;
+    if (prep) {
+        const int64_t rows = build_rows(d);
+        wk = static_cast<float *>(ws);
+        const size_t kb = (size_t)rows * d->h_k * D * sizeof(float);
+        wvv = reinterpret_cast<float *>(static_cast<char *>(ws) + ((kb + 255) & ~(size_t)255));
+    }
+    int64_t packed = 0;
+    for (int s0 = 0; s0 < d->n_seg; s0 += kMaxSeg) {
+        const int nb = std::min(kMaxSeg, d->n_seg - s0);
+        const size_t tsz = d->rule == HYPIC_RULE_DELTA ? (size_t)D * D
+                         : (d->gate_kind == HYPIC_GATE_DIAG ? (size_t)D : 1);
+        float *T_out = d->T_out + (size_t)s0 * d->h_v * tsz;
+        float *S0_out = d->S0_out + (size_t)s0 * d->h_v * D * D;
+        if (d->rule == HYPIC_RULE_DELTA) {
+            DeltaArgs a;
+            memset(&a, 0, sizeof(a));
+            a.beta = d->beta; a.alpha = d->gate;
+            a.T_out = T_out; a.S0_out = S0_out;
+            a.h_k = d->h_k; a.h_v = d->h_v;
+            a.n_seg = nb;
+            int64_t rows_b = 0;
+            for (int i = 0; i < nb; ++i) {
+                a.gtok0[i] = d->seg_start[s0 + i];
+                a.len[i] = (int32_t)d->seg_len[s0 + i];
+                a.tok0[i] = prep ? packed + rows_b : d->seg_start[s0 + i];
+                rows_b += d->seg_len[s0 + i];
+            }
+            if (prep) {
+                ConvArgs c;
+                memset(&c, 0, sizeof(c));
+                c.W = d->conv_w;
+                c.n_seg = nb;
+                for (int i = 0; i < nb; ++i) {
+                    c.tok0[i] = d->seg_start[s0 + i];
+                    c.from[i] = d->conv_w > 0 ? d->conv_from[s0 + i] : d->seg_start[s0 + i];
+                    c.out0[i] = a.tok0[i] - packed;
+                    c.len[i] = a.len[i];
+                }
+                c.x = d->k; c.w = d->conv_wk; c.out = wk + packed * d->h_k * D; c.H = d->h_k;
+                c.l2norm = d->k_l2norm;
+                if ((st = from_hip(launch_conv(c, D, in_kind, rows_b, hs))) != HYPIC_OK) return st;
+                c.x = d->v; c.w = d->conv_wv; c.out = wvv + packed * d->h_v * D; c.H = d->h_v;
+                c.l2norm = 0;
+                if ((st = from_hip(launch_conv(c, D, in_kind, rows_b, hs))) != HYPIC_OK) return st;
+                a.k = wk; a.v = wvv;
+                a.ldk = (int64_t)d->h_k * D; a.ldv = (int64_t)d->h_v * D;
+                packed += rows_b;
+            } else {
+                a.k = d->k; a.v = d->v;
+                a.ldk = (int64_t)d->h_k * D; a.ldv = (int64_t)d->h_v * D;
+            }
+            const int kv_kind = prep ? IN_F32 : in_kind;
+            st = from_hip(launch_build_delta(a, D, kv_kind, in_kind, d->in_dtype == HYPIC_BF16,
+                                             nb * d->h_v, hs));
+        } else {
+            DecayArgs a;
+            memset(&a, 0, sizeof(a));
+            a.k = d->k; a.v = d->v; a.gate = d->gate;
+            a.T_out = T_out; a.S0_out = S0_out;
+            a.h_k = d->h_k; a.h_v = d->h_v; a.gate_kind = d->gate_kind;
+            a.n_seg = nb;
+            for (int i = 0; i < nb; ++i) {
+                a.tok0[i] = d->seg_start[s0 + i];
+                a.len[i] = (int32_t)d->seg_len[s0 + i];
+            }
+            st = from_hip(launch_build_decay(a, D, in_kind, nb * d->h_v, hs));
+        }
+        if (st != HYPIC_OK) return st;
+    }
+    return HYPIC_OK;
+}
+
+hypic_status hypic_compose(const hypic_compose_desc *d, void *ws, size_t ws_bytes, void *stream)
+{
+    (void)ws; (void)ws_bytes;
+    if (!d) return HYPIC_E_INVALID;
+    if (d->tform < HYPIC_T_SCALAR || d->tform > HYPIC_T_DENSE) return HYPIC_E_INVALID;
+    if (d->prec != HYPIC_PREC_FP32 && d->prec != HYPIC_PREC_SPLIT) return HYPIC_E_INVALID;
+    if (d->h_v <= 0 || d->n < 0) return HYPIC_E_INVALID;
+    if (d->d_k != d->d_v || !dim_ok(d->d_k)) return HYPIC_E_UNSUPPORTED;
+    if (!d->S_out || !aligned16(d->S_out) || (d->S_init && !aligned16(d->S_init))) return HYPIC_E_INVALID;
+    if (d->n > 0) {
+        if (!d->order || !d->T_pool || !d->S0_pool || d->n_slots <= 0) return HYPIC_E_INVALID;
+        if (!aligned16(d->T_pool) || !aligned16(d->S0_pool)) return HYPIC_E_INVALID;
+        for (int i = 0; i < d->n; ++i)
+            if (d->order[i] < 0 || d->order[i] >= d->n_slots) return HYPIC_E_INVALID;
+    }
+    const int D = d->d_k;
+    int in_kind = IN_F32;
+    if (d->seams) {
+        if (d->tform != HYPIC_T_DENSE) return HYPIC_E_UNSUPPORTED;
+        hypic_status st = validate_seams(d->seams, d->h_v, D, 16);
+        if (st != HYPIC_OK) return st;
+        if (d->seams->n_win != std::max(0, d->n - 1)) return HYPIC_E_INVALID;
+        if (d->seams->q || d->seams->o || d->seams->T_w || d->seams->S_w0) return HYPIC_E_INVALID;
+        in_kind = d->seams->in_dtype == HYPIC_BF16 ? IN_BF16 : IN_F32;
+    }
+    hypic_status st = device_check();
+    if (st != HYPIC_OK) return st;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    ComposeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.T_pool = d->T_pool; a.S0_pool = d->S0_pool;
+    a.h_v = d->h_v;
+    a.has_seams = d->seams != nullptr;
+    if (d->seams) a.seam = seam_args(d->seams);
+    if (d->n == 0) {
+        a.S_in = d->S_init; a.S_out = d->S_out; a.n = 0;
+        return from_hip(launch_compose(a, D, HYPIC_T_SCALAR, d->prec, in_kind, hs));
+    }
+    for (int b = 0; b < d->n; b += kMaxSeg) {
+        a.n = std::min(kMaxSeg, d->n - b);
+        a.first_pos = b;
+        a.S_in = b == 0 ? d->S_init : d->S_out;
+        a.S_out = d->S_out;
+        for (int i = 0; i < a.n; ++i) a.order[i] = d->order[b + i];
+        if ((st = from_hip(launch_compose(a, D, d->tform, d->prec, in_kind, hs))) != HYPIC_OK) return st;
+    }
+    return HYPIC_OK;
+}
+
+hypic_status hypic_seam_advance(const hypic_seam_desc *d, float *S_inout, void *stream)
+{
+    if (!d || !S_inout || !aligned16(S_inout)) return HYPIC_E_INVALID;
+    if (d->d_k != d->d_v || !dim_ok(d->d_k)) return HYPIC_E_UNSUPPORTED;
+    if (d->h_v <= 0) return HYPIC_E_INVALID;
+    hypic_status st = validate_seams(d, d->h_v, d->d_k, 64);
+    if (st != HYPIC_OK) return st;
+    if (d->n_win < 0) return HYPIC_E_INVALID;
+    if (d->n_win == 0) return HYPIC_OK;
+    st = device_check();
+    if (st != HYPIC_OK) return st;
+    ComposeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.h_v = d->h_v;
+    a.seam = seam_args(d);
+    const int in_kind = d->in_dtype == HYPIC_BF16 ? IN_BF16 : IN_F32;
+    return from_hip(launch_seam(a, d->d_k, in_kind, S_inout, d->n_win,
+                                reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,122 @@
+// common.h -- device helpers shared by the gfx950 kernels of libhypic.
+//
+// Matrix-core fragments (wave64, 16x16 output tiles), as used throughout:
+//   16x16x32 f16/bf16 : lane l holds A[l&15][k(l>>4, e)], B[k(l>>4, e)][l&15], e = 0..7
+//   16x16x4  f32      : lane l holds A[l&15][k(l>>4)],    B[k(l>>4)][l&15]
+//   accumulator       : lane l, register i holds D[4*(l>>4) + i][l&15]
+// The reduction index k only has to agree between A and B, so every product
+// picks the k-order that makes its operands cheap to fetch:
+//   natural     k = 8g + e (16x16x32) or k = g*(K/4) + s (16x16x4, step s),
+//   from-acc    a B operand taken straight from two accumulator tiles of the
+//               previous product: k = 4g + (e & 3) + 16*(e >> 2); for 16x16x4,
+//               step (tile t, register i) has k = 16t + 4g + i.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hy {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+struct bf16_t { uint16_t bits; };   // storage type of bf16 inputs
+
+__device__ __forceinline__ f4 mma(h8 a, h8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mma(b8 a, b8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mma(float a, float b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---- input element access (bf16 inputs are widened exactly) ----------------
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x.bits << 16); }
+__device__ __forceinline__ float ld1(const float *p) { return *p; }
+__device__ __forceinline__ float ld1(const bf16_t *p) { return to_f32(*p); }
+
+// 8 consecutive elements (16-byte aligned for bf16, 32-byte for f32)
+__device__ __forceinline__ void ld8(const bf16_t *p, float (&x)[8]) {
+    uint4 u = *reinterpret_cast<const uint4 *>(p);
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void ld8(const float *p, float (&x)[8]) {
+    float4 a = reinterpret_cast<const float4 *>(p)[0];
+    float4 b = reinterpret_cast<const float4 *>(p)[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// ---- bf16 hi/lo split of an fp32 value (x ~= hi + lo, |x - hi - lo| <~ 2^-17|x|)
+__device__ __forceinline__ void split_bf16(float x, __bf16 &hi, __bf16 &lo) {
+    hi = (__bf16)x;
+    lo = (__bf16)(x - (float)hi);
+}
+
+// ---- wave64 reductions and scans -------------------------------------------
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+__device__ __forceinline__ double wave_sum_f64(double x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+// exclusive suffix sum over the 64 lanes: returns sum_{j > lane} x_j
+__device__ __forceinline__ float wave_suffix_excl(float x) {
+    const int l = threadIdx.x & 63;
+    float s = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        float y = __shfl_down(s, o, 64);
+        if (l + o < 64) s += y;
+    }
+    return s - x;
+}
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ float wave_prefix_incl(float x) {
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        float y = __shfl_up(x, o, 64);
+        if (l >= o) x += y;
+    }
+    return x;
+}
+
+// Power-of-two exponent that brings m (>= 0) into [0.5, 1); 0 for m == 0 or non-finite.
+__device__ __forceinline__ int pow2_exponent(float m) {
+    if (!(m > 0.f) || !(m < INFINITY)) return 0;
+    int e;
+    (void)frexpf(m, &e);
+    return e;
+}
+
+// 2^e * x for a double exponent e, exact split into integer and fraction;
+// underflows to (signed) zero below the float range.
+__device__ __forceinline__ float scale_pow2(float x, double e) {
+    if (e < -400.0) return 0.f * x;
+    double fl = floor(e);
+    float fr = (float)(e - fl);
+    return ldexpf(x * exp2f(fr), (int)fl);
+}
+
+}  // namespace hy

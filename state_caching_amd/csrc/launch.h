@@ -1,0 +1,88 @@
+// launch.h -- kernel argument blocks and launchers shared by the ABI layer and
+// the kernel translation units of libhypic (host and device visible).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hypic.h"
+
+namespace hy {
+
+constexpr int kMaxSeg = HYPIC_MAX_SEG_PER_LAUNCH;
+
+// Input element kinds of a launch.
+enum InKind : int { IN_F32 = 0, IN_BF16 = 1 };
+
+// Chunkwise gated-delta build, one workgroup per (segment, value head).
+struct DeltaArgs {
+    const void *k, *v;          // [rows, h_k, D] / [rows, h_v, D], element kind kv_kind
+    const void *beta, *alpha;   // [N, h_v], element kind g_kind
+    float *T_out, *S0_out;      // at the launch's first segment
+    int h_k, h_v;
+    int64_t ldk, ldv;           // row strides of k and v in elements
+    int n_seg;
+    int64_t tok0[kMaxSeg];      // first row of each range in k / v
+    int64_t gtok0[kMaxSeg];     // first row of each range in beta / alpha
+    int32_t len[kMaxSeg];
+};
+
+// Decay-family build (scalar or diagonal gates), one workgroup per
+// (segment, value head, column group).
+struct DecayArgs {
+    const void *k, *v, *gate;   // gate: [N, h_v] scalar, [N, h_v, D] diag, [h_v] fp32 const
+    float *T_out, *S0_out;
+    int h_k, h_v;
+    int gate_kind;              // HYPIC_GATE_*
+    int n_seg;
+    int64_t tok0[kMaxSeg];
+    int32_t len[kMaxSeg];
+};
+
+// Causal conv (+ key L2 normalisation) of the rows a build reads, into a
+// packed fp32 workspace.
+struct ConvArgs {
+    const void *x;              // [N, H, D] raw rows
+    const float *w;             // [H*D, W]
+    float *out;                 // packed [sum len, H, D]
+    int H, W, l2norm;
+    int n_seg;
+    int64_t tok0[kMaxSeg];      // first row of each range
+    int64_t from[kMaxSeg];      // first row the conv may read
+    int64_t out0[kMaxSeg];      // first packed output row of each range
+    int32_t len[kMaxSeg];
+};
+
+// Seam windows (gated delta).  Per window i the rows are
+//   xk[i] [w, h_k, D], tail_k[i] [W-1, h_k, D], beta/alpha[i] [w, h_v].
+struct SeamArgs {
+    const void *xk, *xv, *tail_k, *tail_v;
+    const float *conv_wk, *conv_wv;
+    const void *beta, *alpha, *q;
+    float *o, *T_w, *S_w0;
+    int w, conv_w, k_l2norm, h_k, h_v;
+};
+
+// Dense / diagonal / scalar composition over a prompt's segments.
+struct ComposeArgs {
+    const float *T_pool, *S0_pool;
+    const float *S_in;          // [h_v, D, D] or null (zero state)
+    float *S_out;
+    int h_v, n;
+    int first_pos;              // prompt position of order[0] (seam i uses window first_pos+i-1)
+    int has_seams;
+    SeamArgs seam;
+    int32_t order[kMaxSeg];
+};
+
+hipError_t launch_build_delta(const DeltaArgs &a, int D, int kv_kind, int g_kind, bool f16,
+                              int n_units, hipStream_t st);
+hipError_t launch_build_decay(const DecayArgs &a, int D, int in_kind, int n_units,
+                              hipStream_t st);
+hipError_t launch_conv(const ConvArgs &a, int D, int in_kind, int64_t total_rows,
+                       hipStream_t st);
+hipError_t launch_compose(const ComposeArgs &a, int D, int tform, int prec, int in_kind,
+                          hipStream_t st);
+hipError_t launch_seam(const ComposeArgs &a, int D, int in_kind, float *S, int n_win,
+                       hipStream_t st);
+
+}  // namespace hy

@@ -1,0 +1,77 @@
+"""Host-side sequencing of a synthetic workload through libhypic.
+
+Marshalling only: segment tables, gathering of seam-window and tail rows by
+indexing, device placement.  The arithmetic of the method runs in the
+library's kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import (BF16, F32, GATE_DIAG, GATE_HEAD_CONST, GATE_SCALAR, PREC_FP32, PREC_SPLIT,
+               RULE_DECAY, RULE_DELTA, Seams, compose, segment_build, tform_of)
+
+_RULE = {"decay": RULE_DECAY, "delta": RULE_DELTA}
+_GATE = {"head_const": GATE_HEAD_CONST, "scalar": GATE_SCALAR, "diag": GATE_DIAG}
+
+
+class DeviceWorkload:
+    """A synth.Workload's tensors on one device, plus its segment tables."""
+
+    def __init__(self, wl, device="cuda"):
+        self.wl = wl
+        self.device = torch.device(device)
+        mv = lambda t: None if t is None else t.to(self.device).contiguous()
+        self.k, self.v, self.beta, self.gate = mv(wl.k), mv(wl.v), mv(wl.beta), mv(wl.gate)
+        self.conv_wk, self.conv_wv = mv(wl.conv_wk), mv(wl.conv_wv)
+        self.rule = _RULE[wl.rule]
+        self.gate_kind = _GATE[wl.gate_kind]
+        self.tform = tform_of(self.rule, self.gate_kind)
+        self.prec = PREC_FP32 if wl.dtype == torch.float32 else PREC_SPLIT
+        body = wl.body_ranges()
+        self.seg_start = [s for s, _ in body]
+        self.seg_len = [e - s for s, e in body]
+        off = wl.seg_off()
+        self.conv_from = [off[j] for j in range(wl.n_seg)]
+        self.seams: Optional[Seams] = self._gather_seams() if wl.seam_w > 0 else None
+
+    def _gather_seams(self) -> Seams:
+        wl = self.wl
+        starts = [s for s, _ in wl.window_ranges()]
+        w, W = wl.seam_w, wl.conv_w
+        idx = torch.tensor([s + t for s in starts for t in range(w)], device=self.device)
+        n_win = len(starts)
+
+        def rows(x, ix, n_per):
+            return x.index_select(0, ix).reshape(n_win, n_per, *x.shape[1:]).contiguous()
+
+        sm = Seams(xk=rows(self.k, idx, w), xv=rows(self.v, idx, w),
+                   beta=rows(self.beta, idx, w), alpha=rows(self.gate, idx, w),
+                   conv_w=W, k_l2norm=1 if W > 0 else 0,
+                   conv_wk=self.conv_wk, conv_wv=self.conv_wv)
+        if W > 1:
+            tix = torch.tensor([s - (W - 1) + t for s in starts for t in range(W - 1)],
+                               device=self.device)
+            sm.tail_k = rows(self.k, tix, W - 1)
+            sm.tail_v = rows(self.v, tix, W - 1)
+        return sm
+
+    def build(self, segs=None, stream=None):
+        """(T, S0) of the bodies (all segments, or the listed indices)."""
+        segs = list(range(self.wl.n_seg)) if segs is None else list(segs)
+        conv = self.wl.conv_w
+        return segment_build(self.rule, self.gate_kind, self.k, self.v, self.beta, self.gate,
+                             [self.seg_start[j] for j in segs], [self.seg_len[j] for j in segs],
+                             conv_w=conv, conv_wk=self.conv_wk if conv else None,
+                             conv_wv=self.conv_wv if conv else None,
+                             conv_from=[self.conv_from[j] for j in segs] if conv else None,
+                             k_l2norm=1 if conv else 0, stream=stream)
+
+    def compose(self, T, S0, S_init=None, order=None, seams=True, prec=None, S_out=None,
+                stream=None):
+        order = list(range(S0.shape[0])) if order is None else list(order)
+        return compose(T, S0, order, S_init=S_init, tform=self.tform,
+                       prec=self.prec if prec is None else prec,
+                       seams=self.seams if seams else None, S_out=S_out, stream=stream)

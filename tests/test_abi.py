@@ -1,0 +1,157 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad
+arguments synchronously with the documented status codes (CPU only: every
+call below fails validation before any HIP call)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hypic.h")
+
+
+@pytest.fixture(scope="module")
+def sca():
+    import state_caching_amd as m
+    m.library()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:const\s+)?\w+\s*\*?\s*(hypic_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("hypic_segment_build", "hypic_compose", "hypic_seam_advance",
+              "hypic_workspace_size", "hypic_status_string", "hypic_version"):
+        assert n in names, names
+
+
+def test_library_exports_every_declared_symbol(sca):
+    out = subprocess.run(["nm", "-D", "--defined-only", sca.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(hypic_\w+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+
+
+def test_status_strings(sca):
+    L = sca.library()
+    assert L.hypic_status_string(0) == b"ok"
+    assert b"invalid" in L.hypic_status_string(-1)
+    assert L.hypic_version() >= 100
+
+
+def _build_desc(sca, **over):
+    ss = (ctypes.c_int64 * 2)(0, 64)
+    sl = (ctypes.c_int64 * 2)(64, 64)
+    kw = dict(rule=sca.RULE_DELTA, gate_kind=sca.GATE_SCALAR, in_dtype=sca.BF16, n_seg=2,
+              seg_start=ctypes.cast(ss, sca._pi64), seg_len=ctypes.cast(sl, sca._pi64),
+              h_k=2, h_v=4, d_k=128, d_v=128, k=16, v=16, beta=16, gate=16,
+              conv_w=0, k_l2norm=0, conv_from=None, conv_wk=None, conv_wv=None,
+              T_out=16, S0_out=16)
+    kw.update(over)
+    d = sca.BuildDesc(**kw)
+    d._keep = (ss, sl)
+    return d
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(h_v=3), -1),                       # h_v % h_k != 0
+    (dict(k=None), -1),
+    (dict(beta=None), -1),                   # delta rule needs beta
+    (dict(d_k=96, d_v=96), -2),
+    (dict(d_k=64, d_v=128), -2),
+    (dict(gate_kind=2), -2),                 # delta + diagonal gate (KDA) not built
+    (dict(in_dtype=7), -1),
+    (dict(k=8), -1),                         # misaligned pointer
+    (dict(conv_w=5), -1),
+    (dict(conv_w=4), -1),                    # conv without conv_from / weights
+    (dict(rule=0, conv_w=0, k_l2norm=1), -2),  # decay family with key normalisation
+])
+def test_build_validation(sca, over, code):
+    d = _build_desc(sca, **over)
+    assert sca.library().hypic_segment_build(ctypes.byref(d), None, 0, None) == code
+
+
+def test_build_negative_length(sca):
+    d = _build_desc(sca)
+    sl = (ctypes.c_int64 * 2)(64, -1)
+    d.seg_len = ctypes.cast(sl, sca._pi64)
+    assert sca.library().hypic_segment_build(ctypes.byref(d), None, 0, None) == -1
+
+
+def test_build_workspace_required_for_conv(sca):
+    cf = (ctypes.c_int64 * 2)(0, 64)
+    d = _build_desc(sca, conv_w=4, conv_from=ctypes.cast(cf, sca._pi64), conv_wk=16, conv_wv=16,
+                    k_l2norm=1)
+    need = sca.library().hypic_workspace_size(ctypes.byref(d), sca.WS_BUILD)
+    assert need == 128 * 2 * 128 * 4 + 128 * 4 * 128 * 4
+    assert sca.library().hypic_segment_build(ctypes.byref(d), None, 0, None) == -3
+    assert sca.library().hypic_workspace_size(ctypes.byref(_build_desc(sca)), sca.WS_BUILD) == 0
+
+
+def _compose_desc(sca, order=(0, 1), **over):
+    o = (ctypes.c_int32 * max(1, len(order)))(*order)
+    kw = dict(tform=sca.T_DENSE, prec=sca.PREC_SPLIT, h_v=4, d_k=128, d_v=128, n=len(order),
+              n_slots=2, order=ctypes.cast(o, sca._pi32), T_pool=16, S0_pool=16, S_init=None,
+              S_out=16, seams=None)
+    kw.update(over)
+    d = sca.ComposeDesc(**kw)
+    d._keep = o
+    return d
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(tform=5), -1), (dict(prec=3), -1), (dict(h_v=0), -1), (dict(n=-1), -1),
+    (dict(S_out=None), -1), (dict(T_pool=None), -1), (dict(n_slots=1), -1),
+    (dict(d_k=48, d_v=48), -2), (dict(S_out=20), -1),
+])
+def test_compose_validation(sca, over, code):
+    d = _compose_desc(sca, **over)
+    assert sca.library().hypic_compose(ctypes.byref(d), None, 0, None) == code
+
+
+def test_compose_seam_validation(sca):
+    sd = sca.SeamDesc(rule=sca.RULE_DELTA, in_dtype=sca.BF16, w=8, conv_w=4, k_l2norm=1, h_k=4,
+                      h_v=4, d_k=128, d_v=128, n_win=1, xk=16, xv=16, tail_k=16, tail_v=16,
+                      conv_wk=16, conv_wv=16, beta=16, alpha=16)
+    L = sca.library()
+    d = _compose_desc(sca, seams=ctypes.pointer(sd))
+    sd.w = 17                                     # fused windows hold at most 16 tokens
+    assert L.hypic_compose(ctypes.byref(d), None, 0, None) == -2
+    sd.w = 8
+    sd.n_win = 2                                  # must be n - 1
+    assert L.hypic_compose(ctypes.byref(d), None, 0, None) == -1
+    sd.n_win = 1
+    sd.tail_k = None                              # conv of width 4 needs the tail rows
+    assert L.hypic_compose(ctypes.byref(d), None, 0, None) == -1
+    sd.tail_k = 16
+    sd.rule = sca.RULE_DECAY
+    assert L.hypic_compose(ctypes.byref(d), None, 0, None) == -2
+    d2 = _compose_desc(sca, tform=sca.T_DIAG, seams=ctypes.pointer(sd))
+    sd.rule = sca.RULE_DELTA
+    assert L.hypic_compose(ctypes.byref(d2), None, 0, None) == -2
+
+
+def test_seam_validation(sca):
+    L = sca.library()
+    sd = sca.SeamDesc(rule=sca.RULE_DELTA, in_dtype=sca.F32, w=65, conv_w=0, k_l2norm=0, h_k=1,
+                      h_v=2, d_k=64, d_v=64, n_win=1, xk=16, xv=16, beta=16, alpha=16)
+    assert L.hypic_seam_advance(ctypes.byref(sd), 16, None) == -2      # w > 64
+    sd.w = 8
+    assert L.hypic_seam_advance(ctypes.byref(sd), None, None) == -1
+    sd.q = 16                                                            # q without o
+    assert L.hypic_seam_advance(ctypes.byref(sd), 16, None) == -1
+
+
+def test_binding_rejects_out_of_range_rows(sca):
+    k = torch.zeros(10, 1, 16)
+    with pytest.raises(ValueError):
+        sca.segment_build(sca.RULE_DELTA, sca.GATE_SCALAR, k, torch.zeros(10, 1, 16),
+                          torch.zeros(10, 1), torch.ones(10, 1), [5], [6])

@@ -1,0 +1,277 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerance (relative Frobenius error per (segment, head) unit, on T_C and on
+S): 1e-5 for fp32 inputs, 2e-3 for bf16 inputs with fp32 state.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import TOL, case, expand_T, max_relF, need_gpu, np64
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import state_caching_amd as sca
+    from state_caching_amd.runner import DeviceWorkload
+    return sca, DeviceWorkload
+
+
+def _check_build(wl, segs=None, heads=None, tol=None, T=None, S0=None, label=""):
+    """GPU pairs (all segments) against oracle pairs on the sampled units."""
+    sca, DW = _lib()
+    tol = TOL[wl.dtype] if tol is None else tol
+    dw = DW(wl)
+    case(f"build {wl.name} {label}")
+    if T is None:
+        T, S0 = dw.build()
+        torch.cuda.synchronize()
+    segs = list(range(wl.n_seg)) if segs is None else segs
+    heads = list(range(wl.h_v)) if heads is None else heads
+    Tr, Sr = oracle.build_pairs(wl, segs=segs, heads=heads)
+    Tg = expand_T(np64(T), dw.tform, wl.d_k)[segs][:, heads]
+    Sg = np64(S0)[segs][:, heads]
+    eT = max_relF(Tg, Tr, 2)
+    eS = max_relF(Sg, Sr, 2)
+    print(f"  {wl.name}: max relF T {eT:.3e}  S {eS:.3e}", flush=True)
+    assert eS <= tol, (eS, tol)
+    assert eT <= tol, (eT, tol)
+    return dw, T, S0
+
+
+# ----------------------------------------------------------- reference configs
+
+def test_cfg0_gdn_fp32_build_compose():
+    need_gpu()
+    wl = synth.config(0)
+    dw, T, S0 = _check_build(wl)
+    case("compose cfg0")
+    S = dw.compose(T, S0)
+    torch.cuda.synchronize()
+    Tr, Sr = oracle.build_pairs(wl)
+    S_or = oracle.compose(Tr, Sr)
+    full = oracle.full_recompute(wl)
+    e = oracle.relF(np64(S), S_or)
+    print(f"  compose relF {e:.3e}; oracle compose vs full {oracle.relF(S_or, full):.1e}")
+    assert e <= 1e-5
+    assert oracle.relF(np64(S), full) <= 1e-5
+
+
+def test_cfg1_retnet_fp32_build_compose_naive():
+    need_gpu()
+    wl = synth.config(1)
+    dw, T, S0 = _check_build(wl)
+    case("compose cfg1 (scalar T)")
+    S = dw.compose(T, S0)
+    torch.cuda.synchronize()
+    Tr, Sr = oracle.build_pairs(wl)
+    S_or = oracle.compose(Tr, Sr)
+    assert oracle.relF(np64(S), S_or) <= 1e-5
+    naive = oracle.naive_sum(np64(S0))
+    err = oracle.relF(naive, S_or)
+    print(f"  naive-sum error vs composed state: {err:.4f}")
+    # head 5 (gamma = 1 - 2^-10): Table 2's ratio at 256 tokens from the GPU pairs
+    S1 = np64(S0)[0, 5]
+    two = np64(T)[1, 5] * S1 + np64(S0)[1, 5]
+    r = np.linalg.norm(two - (S1 + np64(S0)[1, 5])) / np.linalg.norm(S1)
+    assert round(r, 3) == 0.221
+
+
+def test_cfg2_gla_bf16_build():
+    need_gpu()
+    wl = synth.config(2)
+    dw, T, S0 = _check_build(wl)
+    case("compose cfg2 (diag T)")
+    S = dw.compose(T, S0)
+    torch.cuda.synchronize()
+    Tr, Sr = oracle.build_pairs(wl)
+    assert oracle.relF(np64(S), oracle.compose(Tr, Sr)) <= 2e-3
+
+
+def test_cfg2b_gla_slow_build():
+    need_gpu()
+    _check_build(synth.companion("2b"), segs=[0, 5], heads=[0, 7, 15])
+
+
+def test_cfg3_gdn_gqa_sampled():
+    need_gpu()
+    wl = synth.config(3)
+    dw, T, S0 = _check_build(wl, segs=[0, 7], heads=[0, 1, 31], label="(sampled units)")
+    case("compose cfg3")
+    S = dw.compose(T, S0)
+    torch.cuda.synchronize()
+    heads = [3]
+    Tr, Sr = oracle.build_pairs(wl, heads=heads)
+    S_or = oracle.compose(Tr, Sr)
+    e = oracle.relF(np64(S)[heads], S_or)
+    print(f"  compose relF (head 3) {e:.3e}")
+    assert e <= 2e-3
+
+
+def test_cfg3b_gdn_slow_sampled():
+    need_gpu()
+    _check_build(synth.companion("3b"), segs=[2], heads=[4, 5], label="(sampled units)")
+
+
+# ------------------------------------------------------------- shape coverage
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_delta_shapes_ragged(d, dtype):
+    need_gpu()
+    wl = synth.gdn(20 + d, [0, 1, 63, 65, 130, 200], 2, 4, d, dtype, alpha_div=32.0)
+    _check_build(wl, label=f"d={d}")
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("kind", ["retnet", "gla", "gla_slow"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_decay_shapes_ragged(d, kind, dtype):
+    need_gpu()
+    lens = [0, 1, 63, 65, 130, 257]
+    if kind == "retnet":
+        wl = synth.retnet(30 + d, lens, 3, d, dtype=dtype)
+    else:
+        wl = synth.gla(40 + d, lens, 3, d, dtype=dtype, literal=(kind == "gla"))
+    _check_build(wl, label=f"d={d}")
+
+
+def test_mamba2_scalar_gate():
+    """Per-token scalar gate with the decay rule (Mamba2 form)."""
+    need_gpu()
+    import dataclasses
+    base = synth.gdn(50, [100, 77], 2, 2, 64, torch.bfloat16, alpha_div=8.0)
+    wl = dataclasses.replace(base, rule="decay", beta=None, name="mamba2-like")
+    _check_build(wl)
+
+
+def test_deltanet_no_decay():
+    """DeltaNet: gate 1 everywhere; T_C is the pure product of the rank-one erases."""
+    need_gpu()
+    import dataclasses
+    base = synth.gdn(51, [300, 129], 2, 2, 64, torch.bfloat16)
+    wl = dataclasses.replace(base, gate=torch.ones_like(base.gate), name="deltanet")
+    _check_build(wl)
+
+
+# ---------------------------------------------------------------- compose only
+
+@pytest.mark.parametrize("tform,prec", [("dense", 0), ("dense", 1), ("diag", 0), ("scalar", 0)])
+@pytest.mark.parametrize("d", [16, 64, 128])
+def test_compose_prebuilt_pairs(tform, prec, d):
+    need_gpu()
+    sca, _ = _lib()
+    T, S0 = synth.random_pairs(60 + d, 9, 3, d, d, tform=tform)
+    S_init = synth.random_state(61, 3, d, d)
+    order = [4, 0, 8, 2, 2, 7, 1]
+    tf = {"scalar": 0, "diag": 1, "dense": 2}[tform]
+    case(f"compose prebuilt {tform} prec={prec} d={d}")
+    S = sca.compose(T.cuda(), S0.cuda(), order, S_init=S_init.cuda(), tform=tf, prec=prec)
+    torch.cuda.synchronize()
+    Td = expand_T(np64(T), tf, d)
+    ref = oracle.compose(Td[order], np64(S0)[order], np64(S_init))
+    e = oracle.relF(np64(S), ref)
+    print(f"  relF {e:.3e}")
+    assert e <= (1e-5 if prec == 0 else 2e-5)
+
+
+def test_compose_in_place_and_long_chain():
+    """S_out aliasing S_init, and more segments than one launch holds."""
+    need_gpu()
+    sca, _ = _lib()
+    d = 64
+    T, S0 = synth.random_pairs(70, 5, 2, d, d, tform="dense", rho=0.95)
+    order = [i % 5 for i in range(300)]
+    S = synth.random_state(71, 2, d, d).cuda()
+    S_ref_init = np64(S)
+    case("compose in place, 300 segments")
+    sca.compose(T.cuda(), S0.cuda(), order, S_init=S, S_out=S, tform=2, prec=0)
+    torch.cuda.synchronize()
+    ref = oracle.compose(np64(T)[order], np64(S0)[order], S_ref_init)
+    assert oracle.relF(np64(S), ref) <= 1e-5
+
+
+def test_compose_empty():
+    need_gpu()
+    sca, _ = _lib()
+    T, S0 = synth.random_pairs(72, 2, 2, 32, 32)
+    S_init = synth.random_state(73, 2, 32, 32).cuda()
+    S = sca.compose(T.cuda(), S0.cuda(), [], S_init=S_init)
+    assert torch.equal(S, S_init)
+    S = sca.compose(T.cuda(), S0.cuda(), [])
+    assert float(S.abs().max()) == 0.0
+
+
+# ------------------------------------------------------------------- seams
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_seam_standalone_outputs(dtype):
+    need_gpu()
+    sca, DW = _lib()
+    d, h = 64, 2
+    wl = synth.gdn(80, [40, 30], 1, h, d, dtype, alpha_div=16.0, conv_w=4, seam_w=8)
+    dw = DW(wl)
+    rng = np.random.default_rng(81)
+    S_init = synth.random_state(82, h, d, d)
+    q = synth._round(rng.standard_normal((1, 8, 1, d)) / np.sqrt(d), dtype)
+    sm = dw.seams
+    sm.q = q.cuda()
+    sm.o = torch.zeros((1, 8, h, d), dtype=torch.float32, device="cuda")
+    sm.T_w = torch.zeros((1, h, d, d), dtype=torch.float32, device="cuda")
+    sm.S_w0 = torch.zeros((1, h, d, d), dtype=torch.float32, device="cuda")
+    S = S_init.clone().cuda()
+    case(f"seam standalone {dtype}")
+    sca.seam_advance(S, sm)
+    torch.cuda.synchronize()
+    s, e = wl.window_ranges()[0]
+    sl = oracle.Slice(wl, s, e)
+    u = sl.units()
+    S_ref = np64(S_init).copy()
+    o_ref = np.zeros((8, h, d))
+    qa = np64(q)[0]
+    oracle.recur_units(wl.rule, sl.gate_kind, u, d, d, sl.k, sl.v, sl.beta, sl.g, S_ref,
+                       q=np.ascontiguousarray(qa), o=o_ref, off_q=u.off_k, ldq=u.ldk,
+                       off_o=u.off_v, ldo=u.ldv)
+    Tw, Sw = oracle.build_units(wl.rule, sl.gate_kind, u, d, d, sl.k, sl.v, sl.beta, sl.g)
+    tol = 1e-5   # the window runs in fp32 arithmetic for every input dtype
+    errs = (oracle.relF(np64(S), S_ref), oracle.relF(np64(sm.o)[0], o_ref),
+            max_relF(np64(sm.T_w)[0], Tw, 1), max_relF(np64(sm.S_w0)[0], Sw, 1))
+    print("  seam relF S %.2e o %.2e T_w %.2e S_w0 %.2e" % errs)
+    assert max(errs) <= tol
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_cfg4_like_small_pipeline(dtype):
+    """Conv + seams, small: pairs built from raw rows, composed with seams, against
+    the oracle's composition and against full recompute."""
+    need_gpu()
+    wl = synth.gdn(90, [70, 64, 100, 65, 90], 2, 2, 32, dtype, alpha_div=64.0, conv_w=4,
+                   seam_w=8)
+    dw, T, S0 = _check_build(wl)
+    case(f"compose with seams {dtype}")
+    S = dw.compose(T, S0)
+    torch.cuda.synchronize()
+    Tr, Sr = oracle.build_pairs(wl)
+    S_or = oracle.compose(Tr, Sr, wl=wl, seams=True)
+    full = oracle.full_recompute(wl)
+    e1, e2 = oracle.relF(np64(S), S_or), oracle.relF(np64(S), full)
+    print(f"  compose relF vs oracle {e1:.3e}, vs full recompute {e2:.3e}")
+    assert e1 <= TOL[dtype] and e2 <= TOL[dtype]
+
+
+def test_cfg4_sampled():
+    need_gpu()
+    wl = synth.config(4)
+    dw, T, S0 = _check_build(wl, segs=[0, 1, 99], heads=[0, 17], label="(sampled units)")
+    case("compose cfg4 with 99 seams")
+    S = dw.compose(T, S0)
+    torch.cuda.synchronize()
+    heads = [9]
+    Tr, Sr = oracle.build_pairs(wl, heads=heads)
+    S_or = oracle.compose(Tr, Sr, wl=wl, heads=heads, seams=True)
+    e = oracle.relF(np64(S)[heads], S_or)
+    print(f"  compose relF (head 9) {e:.3e}")
+    assert e <= 2e-3
