@@ -1,0 +1,240 @@
+"""Benchmark of the linear-attention state-caching hot path on one MI355X.
+
+Step (the headline): a cold 32768-token prompt of 8 segments x 4096 tokens,
+gated delta rule with 32 value heads over 16 key heads, d = 128, bf16 inputs:
+build the cached pair (T_C, S_{C|0}) of every (segment, head), then compose
+the 8 pairs into the prompt's end state.  value = prompt tokens per second.
+
+Second leg (reported under "compose"): a ~100k-token prompt of 100 segments x
+1024 tokens, 32 heads, d = 128, composed from pre-built fp32 pairs with a
+w = 8 seam window (width-4 causal conv warm-up) at each of the 99 inner
+segments.  value = segment compositions per second.
+
+Inputs are synthetic (seeded), resident in HBM before timing starts.  The
+per-kernel averages behind the roofline figures come from HIP events on the
+stream the kernels run on.  ``cpu_baseline`` times the fp64 CPU oracle on a
+bounded sample of the headline workload.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--leg build|compose|all]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "segment-build tokens/s + compositions/s per GPU, % of MFMA/HBM roofline"
+PEAK_MFMA_F16 = 2500.0     # TFLOP/s, MI355X dense fp16/bf16 matrix cores
+PEAK_HBM = 8000.0          # GB/s, MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def build_flops(n_tokens, h_v, d_k, d_v):
+    # algorithmic work of the gated-delta build: 4 d_k (d_k + d_v) flop per token per value head
+    return 4.0 * d_k * (d_k + d_v) * n_tokens * h_v
+
+
+def build_bytes(wl):
+    el = 2 if "bf16" in str(wl.dtype) else 4
+    n = wl.n_tokens
+    inputs = n * (wl.h_k * wl.d_k + wl.h_v * wl.d_v + 2 * wl.h_v) * el
+    outputs = wl.n_seg * wl.h_v * (wl.d_k * wl.d_k + wl.d_k * wl.d_v) * 4
+    return inputs + outputs
+
+
+def compose_bytes(wl):
+    """Algorithmic bytes of a dense compose with seams: every pair read once,
+    each seam window's raw rows, tails and gates read once, conv weights once,
+    the state written once."""
+    el = 2
+    n, H, d = wl.n_seg, wl.h_v, wl.d_k
+    pairs = n * H * (d * d + d * d) * 4
+    n_win = n - 1
+    W = wl.conv_w
+    seam = n_win * (wl.seam_w * (wl.h_k * d + H * d + 2 * H) + (W - 1) * (wl.h_k * d + H * d)) * el
+    weights = (wl.h_k * d + H * d) * W * 4
+    return pairs + seam + weights + H * d * d * 4
+
+
+def compose_flops(wl):
+    n, H, d = wl.n_seg, wl.h_v, wl.d_k
+    return 2.0 * d * d * d * n * H
+
+
+def time_leg(fn, steps, warmup, torch, events):
+    """Run fn() warmup + steps times; returns (wall ms per step, per-kernel ms lists)."""
+    for _ in range(warmup):
+        fn(None)
+    torch.cuda.synchronize()
+    per = {k: [] for k in events}
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for k in events}
+        fn(ev)
+        recs.append(ev)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    for ev in recs:
+        for k, (a, b) in ev.items():
+            per[k].append(a.elapsed_time(b))
+    return wall, per
+
+
+def cpu_baseline(wl, target_s=12.0):
+    """The fp64 oracle on a bounded sample of (segment, head) build units."""
+    import numpy as np
+    import oracle
+    oracle.build()
+    thr = oracle.threads()
+    units = [(s, h) for s in range(wl.n_seg) for h in range(wl.h_v)]
+    # one unit first to size the sample
+    t0 = time.perf_counter()
+    oracle.build_pairs(wl, segs=[0], heads=[0])
+    t1 = time.perf_counter() - t0
+    n = int(max(thr, min(len(units), thr * max(1, round(target_s / max(t1, 1e-3))))))
+    n = max(1, min(n, len(units)))
+    rng = np.random.default_rng(0)
+    pick = [units[i] for i in sorted(rng.choice(len(units), n, replace=False))]
+    by_seg = {}
+    for s, h in pick:
+        by_seg.setdefault(s, []).append(h)
+    t0 = time.perf_counter()
+    for s, hs in by_seg.items():
+        oracle.build_pairs(wl, segs=[s], heads=hs)
+    dt = time.perf_counter() - t0
+    frac = n / len(units)
+    tok_s = frac * wl.n_tokens / dt
+    return {"value": tok_s, "unit": "tokens/s", "cores": thr, "kind": "oracle",
+            "sample": f"{n} of {len(units)} (segment, value-head) pair builds of the headline "
+                      f"workload (4096 tokens each, fp64 token-by-token, two runs per pair), "
+                      f"{dt:.1f} s wall on {thr} threads; tokens/s scaled by {n}/{len(units)}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--leg", choices=["build", "compose", "all"], default="all")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import synth
+    from state_caching_amd.runner import DeviceWorkload
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    dev = torch.device("cuda:0")
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16-in/fp16-mfma/fp32-acc", "data": "synthetic"}
+
+    if args.calib_copy:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    if args.leg in ("build", "all"):
+        log("generating the 32k-token cold prompt (8 x 4096, 32/16 heads, d=128, bf16)")
+        wl3 = synth.config(3)
+        dw3 = DeviceWorkload(wl3, dev)
+        T = torch.empty((wl3.n_seg, wl3.h_v, 128, 128), dtype=torch.float32, device=dev)
+        S0 = torch.empty_like(T)
+        S = torch.empty((wl3.h_v, 128, 128), dtype=torch.float32, device=dev)
+        from state_caching_amd import segment_build, compose
+
+        def step(ev):
+            if ev: ev["build"][0].record()
+            segment_build(dw3.rule, dw3.gate_kind, dw3.k, dw3.v, dw3.beta, dw3.gate,
+                          dw3.seg_start, dw3.seg_len, T_out=T, S0_out=S0)
+            if ev: ev["build"][1].record(); ev["compose"][0].record()
+            compose(T, S0, list(range(wl3.n_seg)), tform=dw3.tform, prec=dw3.prec, S_out=S)
+            if ev: ev["compose"][1].record()
+
+        log(f"timing {args.steps} steps (+{args.warmup} warm-up)")
+        wall, per = time_leg(step, args.steps, args.warmup, torch, ["build", "compose"])
+        kb = sum(per["build"]) / len(per["build"])
+        kc = sum(per["compose"]) / len(per["compose"])
+        fl = build_flops(wl3.n_tokens, wl3.h_v, wl3.d_k, wl3.d_v)
+        ach = fl / (kb * 1e-3) / 1e12
+        out.update({
+            "value": wl3.n_tokens / (wall * 1e-3), "unit": "tokens/s",
+            "ms_per_step": wall,
+            "config": {"workload": "cold prompt, gated delta (GDN), 32768 tokens = 8 segments x 4096, "
+                                   "32 value heads over 16 key heads (GQA), d_k = d_v = 128, bf16 "
+                                   "inputs, fp32 pairs: build all (segment, head) pairs then compose",
+                       "segments": wl3.n_seg, "seg_len": 4096, "h_v": wl3.h_v, "h_k": wl3.h_k,
+                       "d": 128, "in_dtype": "bf16"},
+            "roofline": {"bound": "mfma", "kernel": "build_delta_kernel<128,fp16>",
+                         "achieved": ach, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
+                         "frac": ach / PEAK_MFMA_F16, "traffic": None,
+                         "kernel_ms": kb, "algorithmic_flop": fl,
+                         "algorithmic_bytes": build_bytes(wl3)},
+            "build_tokens_per_s": wl3.n_tokens / (kb * 1e-3),
+            "build_pairs_per_s": wl3.n_seg * wl3.h_v / (kb * 1e-3),
+            "compose_cold_ms": kc,
+        })
+        del dw3, T, S0, S
+        torch.cuda.empty_cache()
+
+    if args.leg in ("compose", "all"):
+        log("generating the 100 x 1024-token prompt with conv and seams (32 heads, d=128, bf16)")
+        wl4 = synth.config(4)
+        dw4 = DeviceWorkload(wl4, dev)
+        T4, S04 = dw4.build()          # pre-built pairs (not timed)
+        S4 = torch.empty((wl4.h_v, 128, 128), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        from state_caching_amd import compose
+
+        order = list(range(wl4.n_seg))
+
+        def step4(ev):
+            if ev: ev["compose"][0].record()
+            compose(T4, S04, order, tform=dw4.tform, prec=dw4.prec, seams=dw4.seams, S_out=S4)
+            if ev: ev["compose"][1].record()
+
+        wall4, per4 = time_leg(step4, args.steps, args.warmup, torch, ["compose"])
+        k4 = sum(per4["compose"]) / len(per4["compose"])
+        by = compose_bytes(wl4)
+        gbs = by / (k4 * 1e-3) / 1e9
+        comp = {"workload": "hot prompt, gated delta, 100 segments x 1024 tokens, 32 heads, d = 128, "
+                            "pre-built fp32 pairs, w = 8 seam window with width-4 conv at 99 inner segments",
+                "compositions_per_s": wl4.n_seg / (k4 * 1e-3),
+                "head_compositions_per_s": wl4.n_seg * wl4.h_v / (k4 * 1e-3),
+                "ms_per_compose": k4, "wall_ms_per_step": wall4,
+                "roofline": {"bound": "hbm", "kernel": "compose_dense_kernel<128,split,seams>",
+                             "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
+                             "frac": gbs / PEAK_HBM, "traffic": None,
+                             "algorithmic_bytes": by,
+                             "mfma_tflops": compose_flops(wl4) / (k4 * 1e-3) / 1e12}}
+        out["compose"] = comp
+        if "value" not in out:
+            out.update({"value": comp["compositions_per_s"], "unit": "compositions/s",
+                        "ms_per_step": wall4,
+                        "config": {"workload": comp["workload"]}, "roofline": comp["roofline"]})
+
+    if not args.no_cpu:
+        log("timing the fp64 oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(synth.config(3))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

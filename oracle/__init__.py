@@ -257,15 +257,14 @@ class Slice:
         if wl.conv_w > 0:
             self.k, self.v = _conv_inputs(wl, start, end, heads, kheads, conv_from, path)
         else:
-            self.k = np.ascontiguousarray(_f64(wl.k)[start:end][:, kheads])
-            self.v = np.ascontiguousarray(_f64(wl.v)[start:end][:, heads])
-        self.beta = (np.ascontiguousarray(_f64(wl.beta)[start:end][:, heads])
+            self.k = np.ascontiguousarray(_f64(wl.k[start:end])[:, kheads])
+            self.v = np.ascontiguousarray(_f64(wl.v[start:end])[:, heads])
+        self.beta = (np.ascontiguousarray(_f64(wl.beta[start:end])[:, heads])
                      if wl.beta is not None else None)
-        g = _f64(wl.gate)
         if wl.gate_kind == "head_const":
-            self.g = np.ascontiguousarray(g[heads])
+            self.g = np.ascontiguousarray(_f64(wl.gate)[heads])
         else:
-            self.g = np.ascontiguousarray(g[start:end][:, heads])
+            self.g = np.ascontiguousarray(_f64(wl.gate[start:end])[:, heads])
 
     def units(self, ranges=None):
         ranges = [(0, self.n)] if ranges is None else ranges
@@ -288,13 +287,13 @@ def _conv_inputs(wl, start, end, heads, kheads, conv_from, path):
     conv_from = max(conv_from, start - (W - 1))
 
     def run(x_all, w_all, hs, d):
-        x = _f64(x_all)[:, hs].reshape(x_all.shape[0], len(hs) * d)
+        x = _f64(x_all[conv_from:end])[:, hs].reshape(end - conv_from, len(hs) * d)
         w = _f64(w_all).reshape(-1, d, W)[hs].reshape(len(hs) * d, W)
         hist = np.zeros((W - 1, len(hs) * d))
         have = start - conv_from
         if have > 0:
-            hist[W - 1 - have:] = x[conv_from:start]
-        return causal_conv(x[start:end], w, hist, path).reshape(n, len(hs), d)
+            hist[W - 1 - have:] = x[:have]
+        return causal_conv(x[have:], w, hist, path).reshape(n, len(hs), d)
 
     yk = l2norm_rows(run(wl.k, wl.conv_wk, kheads, wl.d_k), path)
     yv = run(wl.v, wl.conv_wv, heads, wl.d_v)
