@@ -48,7 +48,8 @@ build_decay_kernel(const DecayArgs a)
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;
     const int ngrp = D / NC;
-    const int unit = blockIdx.x / ngrp, grp = blockIdx.x % ngrp;
+    const int lb = xcd_logical_block(blockIdx.x, gridDim.x);   // column groups of a unit share an XCD
+    const int unit = lb / ngrp, grp = lb % ngrp;
     const int s = unit / a.h_v, h = unit % a.h_v;
     const int kh = h / (a.h_v / a.h_k);
     const int len = a.len[s];
@@ -110,7 +111,7 @@ build_decay_kernel(const DecayArgs a)
     if (nch > 0) fetch(0);
 
     for (int c = 0; c < nch; ++c) {
-        __syncthreads();
+        lds_barrier();
         // local suffix sums of this part
         float run = 0.f;
         float sfx[TP];
@@ -124,7 +125,7 @@ build_decay_kernel(const DecayArgs a)
         for (int p = 0; p < VPASS; ++p)
 #pragma unroll
             for (int e = 0; e < 8; ++e) sm.VT[vcol + e][vrow + VROWS * p] = (AT)vr[p][e];
-        __syncthreads();
+        lds_barrier();
         float off = 0.f, tot = 0.f;
 #pragma unroll
         for (int p = 0; p < P; ++p) {
@@ -154,7 +155,7 @@ build_decay_kernel(const DecayArgs a)
         }
         (void)tot;
         if (c + 1 < nch) fetch(c + 1);
-        __syncthreads();
+        lds_barrier();
 
         // S <- diag(gam) S + Khat^T V for this wave's 16 columns
 #pragma unroll

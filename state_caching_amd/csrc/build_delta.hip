@@ -73,7 +73,7 @@ build_delta_kernel(const DeltaArgs a)
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;
-    const int unit = blockIdx.x;
+    const int unit = xcd_logical_block(blockIdx.x, gridDim.x);   // value heads of one key head share an XCD
     const int s = unit / a.h_v, h = unit % a.h_v;
     const int kh = h / (a.h_v / a.h_k);
     const int len = a.len[s];
@@ -101,10 +101,11 @@ build_delta_kernel(const DeltaArgs a)
                 X[mt][jn][i] = (n < MT && 16 * mt + 4 * g + i == 16 * n + r16) ? 1.f : 0.f;
     }
 
-    // register prefetch of one chunk: rows prow and prow + 32, columns pcol..pcol+7
+    // register prefetch of one chunk (kept raw until staged): rows prow and
+    // prow + 32, columns pcol..pcol+7
     constexpr int CPR = D / 8;
     const int prow = tid / CPR, pcol = 8 * (tid % CPR);
-    float kr[2][8], vr[2][8];
+    typename Raw8<TKV>::type kraw[2], vraw[2];
     float br = 0.f, ar = 1.f;
     auto fetch = [&](int c) {
         const int t0 = 64 * c;
@@ -112,11 +113,11 @@ build_delta_kernel(const DeltaArgs a)
         for (int p = 0; p < 2; ++p) {
             const int t = t0 + prow + 32 * p;
             if (t < len) {
-                ld8(kp + (int64_t)t * a.ldk + pcol, kr[p]);
-                ld8(vp + (int64_t)t * a.ldv + pcol, vr[p]);
+                ld_raw8(kp + (int64_t)t * a.ldk + pcol, kraw[p]);
+                ld_raw8(vp + (int64_t)t * a.ldv + pcol, vraw[p]);
             } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) { kr[p][e] = 0.f; vr[p][e] = 0.f; }
+                zero_raw8(kraw[p]);
+                zero_raw8(vraw[p]);
             }
         }
         if (w == 0) {
@@ -130,16 +131,22 @@ build_delta_kernel(const DeltaArgs a)
             }
         }
     };
+    float kr[2][8], vr[2][8];
 
     const int nch = (len + 63) / 64;
-    double cl_tot = 0.0;   // log2 of the segment's gate product
+    double cl_lane = 0.0;  // wave 0: log2 of the gate product of this lane's tokens, all chunks
     if (nch > 0) fetch(0);
 
     for (int c = 0; c < nch; ++c) {
-        __syncthreads();   // readers of the previous chunk are done
+        lds_barrier();   // readers of the previous chunk are done
 
         // ---- stage the chunk: keys, gates ---------------------------------
         {
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                widen8(kraw[p], kr[p]);
+                widen8(vraw[p], vr[p]);
+            }
             float vm = 0.f;
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
@@ -161,13 +168,13 @@ build_delta_kernel(const DeltaArgs a)
             if (w == 0) {
                 const float l2 = log2f(ar);
                 const float sfx = wave_suffix_excl(l2);    // log2 prod_{s>t} a_s
-                const double tot = wave_sum_f64((double)l2);
+                cl_lane += (double)l2;
                 sm.beta[lane] = br;
                 sm.bd[lane] = br * exp2f(sfx);
-                if (lane == 0) sm.chunk_l2 = tot;
+                if (lane == 0) sm.chunk_l2 = (double)(sfx + l2);   // whole-chunk total
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- values (scaled), Gram ------------------------------------------
         int sv = 0;
@@ -181,9 +188,7 @@ build_delta_kernel(const DeltaArgs a)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) sm.VT[pcol + e][prow + 32 * p] = (OT)(vr[p][e] * vsc);
         }
-        const double cl_chunk = sm.chunk_l2;
-        cl_tot += cl_chunk;
-        const float gb = scale_pow2(1.f, cl_chunk);
+        const float gb = scale_pow2(1.f, sm.chunk_l2);
         if (c + 1 < nch) fetch(c + 1);
 
         for (int q = w; q < 10; q += NW) {
@@ -215,7 +220,7 @@ build_delta_kernel(const DeltaArgs a)
                 sm.Gm[rr][cc] = (cc < rr) ? sm.beta[rr] * acc[i] : 0.f;
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- M = (I + Gm)^-1: diagonal 16x16 blocks by forward substitution ----
         if (w == 0) {
@@ -231,7 +236,7 @@ build_delta_kernel(const DeltaArgs a)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sm.Mm[o + r][o + cc] = x[r];
         }
-        __syncthreads();
+        lds_barrier();
         // 32x32 blocks: M10 = -M11 (L10 M00)
         for (int p = w; p < 2; p += NW) {
             const int o0 = 32 * p, o1 = 32 * p + 16;
@@ -247,7 +252,7 @@ build_delta_kernel(const DeltaArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i) sm.Mm[o1 + 4 * g + i][o0 + r16] = -m[i];
         }
-        __syncthreads();
+        lds_barrier();
         // 64x64: rows 32..63, columns of tile tj: M[hi][lo] = -M[hi][hi] (L[hi][lo] M[lo][lo])
         for (int tj = w; tj < 2; tj += NW) {
             f4 y2 = zero4(), y3 = zero4();
@@ -273,7 +278,7 @@ build_delta_kernel(const DeltaArgs a)
                 sm.Mm[48 + 4 * g + i][16 * tj + r16] = -m3[i];
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- W = M diag(b) K: wave w produces key-column tile w ---------------
         {
@@ -304,7 +309,7 @@ build_delta_kernel(const DeltaArgs a)
                 for (int i = 0; i < 4; ++i) sm.Wb[16 * ti + 4 * g + i][16 * td + r16] = (OT)acc[i];
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- state update of this wave's two column tiles ----------------------
 #pragma unroll
@@ -435,6 +440,13 @@ build_delta_kernel(const DeltaArgs a)
     }
 
     // ---- outputs: T_C = 2^(sig + log2 prod a) Tbar, S_{C|0} = 2^sig Shat ------
+    // the segment's gate product, summed in fp64 over every token
+    if (w == 0) {
+        const double tot = wave_sum_f64(cl_lane);
+        if (lane == 0) sm.chunk_l2 = tot;
+    }
+    lds_barrier();
+    const double cl_tot = sm.chunk_l2;
     float *Tu = a.T_out + (int64_t)unit * D * D;
     float *Su = a.S0_out + (int64_t)unit * D * D;
 #pragma unroll
@@ -471,25 +483,17 @@ static hipError_t launch_one(const DeltaArgs &a, int n_units, hipStream_t st)
     return hipGetLastError();
 }
 
-// The fp16 operand path is used for d >= 64.  Below that a 64-token chunk
-// erases most of the key space, Tbar - K^T (W Tbar) cancels heavily and fp16
-// rounding of W, Tbar and E is amplified, so small heads use fp32 products.
+// bf16 inputs use the fp16-operand pipelined kernel (build_delta_f16.hip) for
+// d >= 64.  Below that a 64-token chunk erases most of the key space, so
+// Tbar - K^T (W Tbar) cancels heavily and fp16 rounding of W, Tbar and E is
+// amplified: small heads, like fp32 inputs, use fp32 products here.
 template <int D>
 static hipError_t launch_d(const DeltaArgs &a, int kv_kind, int g_kind, bool f16, int n_units,
                            hipStream_t st)
 {
-    if (D < 64) {
-        if (kv_kind == IN_BF16 && g_kind == IN_BF16) return launch_one<D, false, bf16_t, bf16_t>(a, n_units, st);
-        if (kv_kind == IN_F32 && g_kind == IN_BF16) return launch_one<D, false, float, bf16_t>(a, n_units, st);
-        if (kv_kind == IN_F32 && g_kind == IN_F32) return launch_one<D, false, float, float>(a, n_units, st);
-        return hipErrorInvalidValue;
-    }
-    if (f16) {
-        if (kv_kind == IN_BF16 && g_kind == IN_BF16) return launch_one<D, true, bf16_t, bf16_t>(a, n_units, st);
-        if (kv_kind == IN_F32 && g_kind == IN_BF16) return launch_one<D, true, float, bf16_t>(a, n_units, st);
-        if (kv_kind == IN_F32 && g_kind == IN_F32) return launch_one<D, true, float, float>(a, n_units, st);
-        return hipErrorInvalidValue;
-    }
+    if (f16 && D >= 64) return launch_build_delta_f16(a, D, kv_kind, g_kind, n_units, st);
+    if (kv_kind == IN_BF16 && g_kind == IN_BF16) return launch_one<D, false, bf16_t, bf16_t>(a, n_units, st);
+    if (kv_kind == IN_F32 && g_kind == IN_BF16) return launch_one<D, false, float, bf16_t>(a, n_units, st);
     if (kv_kind == IN_F32 && g_kind == IN_F32) return launch_one<D, false, float, float>(a, n_units, st);
     return hipErrorInvalidValue;
 }

@@ -1,0 +1,528 @@
+// build_delta_f16.hip -- chunkwise gated-delta build with fp16 matrix-core
+// operands, for d_k = d_v in {64, 128} (HYPIC reading notes: the cached pair
+// of a segment, ch.2 secs.2 and 4; the gated-delta family, ch.2 sec.3 Table 1).
+//
+// Same algebra as build_delta.hip (the compact-WY chunk update, carrying
+// X = [Tbar | S] through chunks of 64 tokens), organised as a two-stage
+// software pipeline inside one workgroup per (segment, value head):
+//
+//   prep waves  (4)    : chunk c+1 -- stage K, V, gates; Gram K K^T; the unit
+//                        lower-triangular inverse M; W = M diag(b) K and
+//                        U = M diag(b dec) V into LDS
+//   state waves (d/32) : chunk c   -- E = U - W Xhat, Xhat += K^T E on the
+//                        wave's four 16-column tiles of X
+//
+// Four LDS barriers per chunk; the state waves put a quarter of their matrix
+// work into every phase so the matrix cores stay busy while the prep waves
+// run their latency-bound steps.  Xhat is kept in power-of-two units per
+// column tile (renormalised every 4 chunks, or when the value scale runs
+// ahead of the state), so every computed fp16 operand stays in range.
+#include "common.h"
+#include "launch.h"
+
+namespace hy {
+
+template <int D>
+struct F16Cfg {
+    static constexpr int NS = D / 32;         // state waves, four column tiles each
+    static constexpr int TPW = 4;             // column tiles of X per state wave
+    static constexpr int NP = 4;              // prep waves
+    static constexpr int NT = 64 * (NS + NP);
+    static constexpr int MT = D / 16;
+    static constexpr int KB = D / 32;
+    static constexpr int LDT = 72;            // KT row stride (halves), token-major within a row
+    static constexpr int LDW = D + 8;         // nW / Ks row stride (halves)
+    static constexpr int LDU = 68;            // UT row stride (floats)
+    static constexpr int LDG = 68;
+    static constexpr int PASSES = D / 32;     // prep staging passes of 16 rows
+};
+
+template <int D>
+struct F16Smem {
+    using C = F16Cfg<D>;
+    _Float16 KT[2][D][C::LDT];   // keys, dim-major, token groups XOR-swizzled per row
+    _Float16 nW[64][C::LDW];     // -W = -M diag(b) K, token-major
+    float UT[D][C::LDU];         // U^T (value column-major), in units of 2^sv
+    _Float16 VT[D][C::LDT];      // V * 2^-sv, dim-major, swizzled like KT
+    _Float16 Ks[64][C::LDW];     // keys, token-major (Gram)
+    float Gm[64][C::LDG];        // b_r k_r.k_s for s < r; the inverse of each diagonal
+                                 // 16x16 block is kept transposed in its upper triangle
+    _Float16 M1[64][72];         // M diag(b)
+    _Float16 M2[64][72];         // M diag(b dec)
+    float beta[64], bd[64];
+    float gb[2];                 // chunk gate product, per pipeline slot
+    int sv[2];                   // value scale exponent, per pipeline slot
+    float wmax[4];
+    double cl_tot;
+};
+
+// XOR swizzle of 8-token groups within a dim-major row (spreads transposed stores over banks)
+__device__ __forceinline__ int swz(int d, int t) { return t ^ (((d >> 3) & 7) << 3); }
+
+__constant__ int kOffTi[6] = {1, 2, 2, 3, 3, 3};
+__constant__ int kOffTj[6] = {0, 0, 1, 0, 1, 2};
+
+template <int D, typename TKV, typename TG>
+__global__ void __launch_bounds__((F16Cfg<D>::NT))
+build_delta_f16_kernel(const DeltaArgs a)
+{
+    using C = F16Cfg<D>;
+    constexpr int NS = C::NS, MT = C::MT, KB = C::KB;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    F16Smem<D> &sm = *reinterpret_cast<F16Smem<D> *>(smem_raw);
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int unit = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int s = unit / a.h_v, h = unit % a.h_v;
+    const int kh = h / (a.h_v / a.h_k);
+    const int len = a.len[s];
+    const int nch = (len + 63) / 64;
+    const bool is_prep = w >= NS;
+
+    // upper tile blocks of M1/M2 are never written
+    for (int idx = tid; idx < 64 * 64; idx += C::NT) {
+        const int r = idx >> 6, c = idx & 63;
+        if ((c >> 4) > (r >> 4)) { sm.M1[r][c] = (_Float16)0; sm.M2[r][c] = (_Float16)0; }
+    }
+
+    // Warp-specialised roles.  Both loops run nch + 1 iterations of four
+    // barriers each, so every barrier meets all waves; prep runs one chunk ahead.
+    if (is_prep) {
+        // ------------------------------------------------------------ prep state
+        const int ptid = tid - 64 * NS, pw = w - NS;
+        constexpr int CPR = D / 8;
+        const int prow = (ptid >= 0 ? ptid : 0) / CPR, pcol = 8 * ((ptid >= 0 ? ptid : 0) % CPR);
+        constexpr int RPP = 256 / CPR;             // rows per pass
+        const TKV *kp = reinterpret_cast<const TKV *>(a.k) + a.tok0[s] * a.ldk + (int64_t)kh * D;
+        const TKV *vp = reinterpret_cast<const TKV *>(a.v) + a.tok0[s] * a.ldv + (int64_t)h * D;
+        const TG *bp = reinterpret_cast<const TG *>(a.beta) + a.gtok0[s] * a.h_v + h;
+        const TG *ap = reinterpret_cast<const TG *>(a.alpha) + a.gtok0[s] * a.h_v + h;
+        typename Raw8<TKV>::type kraw[C::PASSES], vraw[C::PASSES];
+        float br = 0.f, ar = 1.f;
+        double cl_lane = 0.0;
+        auto fetch_k = [&](int c) {
+#pragma unroll
+            for (int p = 0; p < C::PASSES; ++p) {
+                const int t = 64 * c + prow + RPP * p;
+                if (t < len) ld_raw8(kp + (int64_t)t * a.ldk + pcol, kraw[p]);
+                else zero_raw8(kraw[p]);
+            }
+            if (pw == 0) {
+                const int t = 64 * c + lane;
+                if (t < len) { br = ld1(bp + (int64_t)t * a.h_v); ar = ld1(ap + (int64_t)t * a.h_v); }
+                else { br = 0.f; ar = 1.f; }
+            }
+        };
+        auto fetch_v = [&](int c) {
+#pragma unroll
+            for (int p = 0; p < C::PASSES; ++p) {
+                const int t = 64 * c + prow + RPP * p;
+                if (t < len) ld_raw8(vp + (int64_t)t * a.ldv + pcol, vraw[p]);
+                else zero_raw8(vraw[p]);
+            }
+        };
+        if (nch > 0) { fetch_k(0); fetch_v(0); }
+
+
+        for (int it = 0; it <= nch; ++it) {
+            const int cp = it;
+            const bool dop = cp < nch;
+            const int bp_ = cp & 1;
+            // ===================== phase 1: stage keys and gates of cp | E tile 0
+            if (dop) {
+                float vm = 0.f;
+#pragma unroll
+                for (int p = 0; p < C::PASSES; ++p) {
+                    float kx[8], vx[8];
+                    widen8(kraw[p], kx);
+                    widen8(vraw[p], vx);
+                    const int t = prow + RPP * p;
+                    h8 kk;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        kk[e] = (_Float16)kx[e];
+                        sm.KT[bp_][pcol + e][swz(pcol + e, t)] = kk[e];
+                        vm = fmaxf(vm, fabsf(vx[e]));
+                    }
+                    *reinterpret_cast<h8 *>(&sm.Ks[t][pcol]) = kk;
+                }
+                vm = wave_max(vm);
+                if (lane == 0) sm.wmax[pw] = vm;
+                if (pw == 0) {
+                    const float l2 = log2f(ar);
+                    const float sfx = wave_suffix_excl(l2);
+                    cl_lane += (double)l2;
+                    sm.beta[lane] = br;
+                    sm.bd[lane] = br * exp2f(sfx);
+                    if (lane == 0) sm.gb[bp_] = exp2f(sfx + l2);
+                }
+                if (cp + 1 < nch) fetch_k(cp + 1);
+            }
+            lds_barrier();
+            // ===================== phase 2: V^, Gram, diagonal inverses | update tile 0
+            if (dop) {
+                // value scale of chunk cp; V^ = V * 2^-sv into VT
+                {
+                    const float vm = fmaxf(fmaxf(sm.wmax[0], sm.wmax[1]), fmaxf(sm.wmax[2], sm.wmax[3]));
+                    const int sv = pow2_exponent(vm);
+                    if (pw == 0 && lane == 0) sm.sv[bp_] = sv;
+                    const float vsc = exp2f(-(float)sv);
+#pragma unroll
+                    for (int p = 0; p < C::PASSES; ++p) {
+                        float vx[8];
+                        widen8(vraw[p], vx);
+                        const int t = prow + RPP * p;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) sm.VT[pcol + e][swz(pcol + e, t)] = (_Float16)(vx[e] * vsc);
+                    }
+                    if (cp + 1 < nch) fetch_v(cp + 1);
+                }
+                // diagonal Gram tile b = pw, then the inverse of I + A'_bb by forward
+                // substitution.  A'_bb is written transposed into the block's upper
+                // triangle (column q of A' is then one contiguous row), and the
+                // inverse M_bb overwrites it, also transposed, when done.
+                {
+                    const int b = pw, o = 16 * b;
+                    f4 acc = zero4();
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) {
+                        const h8 A = *reinterpret_cast<const h8 *>(&sm.Ks[o + r16][32 * kb + 8 * g]);
+                        acc = mma(A, A, acc);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int rr = 4 * g + i;   // A'[rr][r16] for r16 < rr, stored at [r16][rr]
+                        if (r16 < rr) sm.Gm[o + r16][o + rr] = sm.beta[o + rr] * acc[i];
+                    }
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    if (lane < 16) {
+                        const int c = lane;
+                        float x[16];
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
+                        float4 nxt[4], cur[4];
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) nxt[v] = *reinterpret_cast<const float4 *>(&sm.Gm[o][o + 4 * v]);
+#pragma unroll
+                        for (int q = 0; q < 15; ++q) {
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) cur[v] = nxt[v];
+                            asm volatile("" ::: "memory");
+                            if (q + 1 < 15) {
+#pragma unroll
+                                for (int v = 0; v < 4; ++v)
+                                    nxt[v] = *reinterpret_cast<const float4 *>(&sm.Gm[o + q + 1][o + 4 * v]);
+                            }
+                            asm volatile("" ::: "memory");
+                            const float colv[16] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w,
+                                                    cur[1].x, cur[1].y, cur[1].z, cur[1].w,
+                                                    cur[2].x, cur[2].y, cur[2].z, cur[2].w,
+                                                    cur[3].x, cur[3].y, cur[3].z, cur[3].w};
+#pragma unroll
+                            for (int r = q + 1; r < 16; ++r) x[r] -= colv[r] * x[q];
+                        }
+                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                        // M_bb[r][c] (r >= c) kept at Gm[o + c][o + r]
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            if (r >= c) sm.Gm[o + c][o + r] = x[r];
+                    }
+                }
+                // off-diagonal Gram tiles
+                for (int q = pw; q < 6; q += 4) {
+                    const int ti = kOffTi[q], tj = kOffTj[q];
+                    f4 acc = zero4();
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) {
+                        const h8 A = *reinterpret_cast<const h8 *>(&sm.Ks[16 * ti + r16][32 * kb + 8 * g]);
+                        const h8 B = *reinterpret_cast<const h8 *>(&sm.Ks[16 * tj + r16][32 * kb + 8 * g]);
+                        acc = mma(A, B, acc);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int rr = 16 * ti + 4 * g + i;
+                        sm.Gm[rr][16 * tj + r16] = sm.beta[rr] * acc[i];
+                    }
+                }
+            }
+            lds_barrier();
+            // ===================== phase 3: M column chains | E tile 1
+            if (dop) {
+                const int j = pw;   // column block of M this wave completes (indices unrolled)
+                f4 Mc[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    Mc[i] = zero4();
+                    if (i == j) {   // M_jj in accumulator layout: rows 4g + r, column r16
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int row = 4 * g + r;
+                            Mc[i][r] = (r16 <= row) ? sm.Gm[16 * i + r16][16 * i + row] : 0.f;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int i = 1; i < 4; ++i) {
+                    if (i > j) {
+                        f4 acc = zero4();
+#pragma unroll
+                        for (int t = 0; t < i; ++t) {
+                            if (t >= j) {
+#pragma unroll
+                                for (int r = 0; r < 4; ++r)
+                                    acc = mma(sm.Gm[16 * i + r16][16 * t + 4 * g + r], Mc[t][r], acc);
+                            }
+                        }
+                        f4 m = zero4();
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int k = 4 * g + r;   // M_ii[r16][k], zero above the diagonal
+                            const float mik = (k <= r16) ? sm.Gm[16 * i + k][16 * i + r16] : 0.f;
+                            m = mma(mik, acc[r], m);
+                        }
+                        Mc[i] = -m;
+                    }
+                }
+                const float bcol = sm.beta[16 * j + r16], bdcol = sm.bd[16 * j + r16];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (i >= j) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            sm.M1[16 * i + 4 * g + r][16 * j + r16] = (_Float16)(Mc[i][r] * bcol);
+                            sm.M2[16 * i + 4 * g + r][16 * j + r16] = (_Float16)(Mc[i][r] * bdcol);
+                        }
+                    }
+                }
+            }
+            lds_barrier();
+            // ===================== phase 4: W and U of chunk cp | update tile 1 =
+            if (dop) {
+                // W = M diag(b) K (stored negated), key-column tiles {pw, pw + 4, ...}
+                for (int td = pw; td < MT; td += 4) {
+                    const int d = 16 * td + r16;
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti) {
+                        f4 acc = zero4();
+                        const int kbmax = (16 * ti + 15) / 32;
+                        for (int kb = 0; kb <= kbmax; ++kb) {
+                            const h8 A = *reinterpret_cast<const h8 *>(&sm.M1[16 * ti + r16][32 * kb + 8 * g]);
+                            const h8 B = *reinterpret_cast<const h8 *>(&sm.KT[bp_][d][swz(d, 32 * kb + 8 * g)]);
+                            acc = mma(A, B, acc);
+                        }
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sm.nW[16 * ti + 4 * g + i][16 * td + r16] = (_Float16)(-acc[i]);
+                    }
+                }
+                // U = M diag(b dec) V^ for value-column tiles {pw, pw + 4, ...}
+                for (int tc = pw; tc < MT; tc += 4) {
+                    const int cc = 16 * tc + r16;
+                    h8 Bv[2];
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+                        Bv[kb] = *reinterpret_cast<const h8 *>(&sm.VT[cc][swz(cc, 32 * kb + 8 * g)]);
+                    f4 U[4];
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti) {
+                        U[ti] = zero4();
+                        const int kbmax = (16 * ti + 15) / 32;
+                        for (int kb = 0; kb <= kbmax; ++kb) {
+                            const h8 A = *reinterpret_cast<const h8 *>(&sm.M2[16 * ti + r16][32 * kb + 8 * g]);
+                            U[ti] = mma(A, Bv[kb], U[ti]);
+                        }
+                    }
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti)
+                        *reinterpret_cast<float4 *>(&sm.UT[cc][16 * ti + 4 * g]) =
+                            make_float4(U[ti][0], U[ti][1], U[ti][2], U[ti][3]);
+                }
+            }
+            lds_barrier();
+        }
+
+        if (pw == 0) {
+            const double tot = wave_sum_f64(cl_lane);
+            if (lane == 0) sm.cl_tot = tot;
+        }
+        lds_barrier();
+    } else {
+        // ----------------------------------------------------------- state state
+        f4 X[MT][C::TPW];
+        float sig[C::TPW] = {0.f, 0.f, 0.f, 0.f};
+        h8 Eb[2][2];   // E of two column tiles as fp16 B operands (token blocks 0-31, 32-63)
+        {
+#pragma unroll
+            for (int jn = 0; jn < C::TPW; ++jn) {
+                const int n = C::TPW * w + jn;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        X[mt][jn][i] = (n < MT && 16 * mt + 4 * g + i == 16 * n + r16) ? 1.f : 0.f;
+            }
+        }
+
+
+        for (int it = 0; it <= nch; ++it) {
+            const int cs = it - 1;
+            const bool dos = cs >= 0;
+            const int bs_ = cs & 1;
+            // Xhat <- Xhat * 2^(sig - target): new unit from the block max, never below
+            // 2^(sv - 4) for S (keeps E = U 2^(sv - sig) - W Xhat within fp16 range)
+            auto renorm = [&](int jn, bool isS, float svs) {
+                float xm = 0.f;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) xm = fmaxf(xm, fabsf(X[mt][jn][i]));
+                xm = wave_max(xm);
+                float target = (float)pow2_exponent(xm) + sig[jn];
+                if (xm == 0.f) target = isS ? svs : sig[jn];
+                if (isS && target < svs - 4.f) target = svs - 4.f;
+                const float f = exp2f(sig[jn] - target);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) X[mt][jn] *= f;
+                sig[jn] = target;
+            };
+            auto state_e = [&](int jn, int sl) {
+                const int n = C::TPW * w + jn;
+                const bool isS = n >= MT;
+                if (isS) {
+                    const float gbv = sm.gb[bs_];
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) X[mt][jn] *= gbv;
+                }
+                f4 E[4];
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) E[ti] = zero4();
+                if (isS && cs == 0) sig[jn] = (float)sm.sv[bs_];   // S starts at 0: take the value scale
+                if (isS && (float)sm.sv[bs_] > sig[jn] + 4.f) renorm(jn, true, (float)sm.sv[bs_]);
+                if (isS) {
+                    const float usc = exp2f((float)sm.sv[bs_] - sig[jn]);
+                    const int cc = 16 * (n - MT) + r16;
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti) {
+                        const float4 u = *reinterpret_cast<const float4 *>(&sm.UT[cc][16 * ti + 4 * g]);
+                        E[ti] = f4{u.x, u.y, u.z, u.w} * usc;
+                    }
+                }
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    h8 B;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        B[i] = (_Float16)X[2 * kb][jn][i];
+                        B[4 + i] = (_Float16)X[2 * kb + 1][jn][i];
+                    }
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti) {
+                        const h4 lo = *reinterpret_cast<const h4 *>(&sm.nW[16 * ti + r16][32 * kb + 4 * g]);
+                        const h4 hi = *reinterpret_cast<const h4 *>(&sm.nW[16 * ti + r16][32 * kb + 16 + 4 * g]);
+                        h8 A;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) { A[e] = lo[e]; A[4 + e] = hi[e]; }
+                        E[ti] = mma(A, B, E[ti]);
+                    }
+                }
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        Eb[sl][kb][i] = (_Float16)E[2 * kb][i];
+                        Eb[sl][kb][4 + i] = (_Float16)E[2 * kb + 1][i];
+                    }
+            };
+            // X += K^T E for two column tiles at once (they share the K^T fragments);
+            // rows in two halves so only half of the fragments are live at a time
+            auto state_u2 = [&](int j0, int s0, int j1, int s1) {
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    asm volatile("" ::: "memory");
+#pragma unroll
+                    for (int mh = 0; mh < MT / 2; ++mh) {
+                        const int mt = half * (MT / 2) + mh;
+                        const int d = 16 * mt + r16;
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) {
+                            const h4 lo = *reinterpret_cast<const h4 *>(&sm.KT[bs_][d][swz(d, 32 * kb + 4 * g)]);
+                            const h4 hi = *reinterpret_cast<const h4 *>(&sm.KT[bs_][d][swz(d, 32 * kb + 16 + 4 * g)]);
+                            h8 A;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) { A[e] = lo[e]; A[4 + e] = hi[e]; }
+                            X[mt][j0] = mma(A, Eb[s0][kb], X[mt][j0]);
+                            X[mt][j1] = mma(A, Eb[s1][kb], X[mt][j1]);
+                        }
+                    }
+                }
+            };
+            auto state_u = [&](int jn) {   // periodic renormalisation
+                const int n = C::TPW * w + jn;
+                if ((cs & 3) == 3) renorm(jn, n >= MT, (float)sm.sv[bs_]);
+            };
+            if (dos) { state_e(0, 0); state_e(1, 1); }
+            lds_barrier();
+            if (dos) { state_u2(0, 0, 1, 1); state_u(0); state_u(1); }
+            lds_barrier();
+            if (dos) { state_e(2, 0); state_e(3, 1); }
+            lds_barrier();
+            if (dos) { state_u2(2, 0, 3, 1); state_u(2); state_u(3); }
+            lds_barrier();
+        }
+
+        lds_barrier();
+        {
+            const double cl_tot = sm.cl_tot;
+            float *Tu = a.T_out + (int64_t)unit * D * D;
+            float *Su = a.S0_out + (int64_t)unit * D * D;
+#pragma unroll
+            for (int jn = 0; jn < C::TPW; ++jn) {
+                const int n = C::TPW * w + jn;
+                const bool isS = n >= MT;
+                const double e = (double)sig[jn] + (isS ? 0.0 : cl_tot);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 16 * mt + 4 * g + i;
+                        const float val = scale_pow2(X[mt][jn][i], e);
+                        if (isS) Su[row * D + 16 * (n - MT) + r16] = val;
+                        else     Tu[row * D + 16 * n + r16] = val;
+                    }
+            }
+        }
+    }
+}
+
+template <int D, typename TKV, typename TG>
+hipError_t launch_f16_one(const DeltaArgs &a, int n_units, hipStream_t st)
+{
+    const size_t smem = sizeof(F16Smem<D>);
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&build_delta_f16_kernel<D, TKV, TG>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    hipLaunchKernelGGL((build_delta_f16_kernel<D, TKV, TG>), dim3(n_units), dim3(F16Cfg<D>::NT), smem, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_build_delta_f16(const DeltaArgs &a, int D, int kv_kind, int g_kind, int n_units,
+                                  hipStream_t st)
+{
+    const bool kvb = kv_kind == IN_BF16, gbf = g_kind == IN_BF16;
+    if (D == 128) {
+        if (kvb && gbf) return launch_f16_one<128, bf16_t, bf16_t>(a, n_units, st);
+        if (!kvb && gbf) return launch_f16_one<128, float, bf16_t>(a, n_units, st);
+        if (!kvb && !gbf) return launch_f16_one<128, float, float>(a, n_units, st);
+    } else if (D == 64) {
+        if (kvb && gbf) return launch_f16_one<64, bf16_t, bf16_t>(a, n_units, st);
+        if (!kvb && gbf) return launch_f16_one<64, float, bf16_t>(a, n_units, st);
+        if (!kvb && !gbf) return launch_f16_one<64, float, float>(a, n_units, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace hy

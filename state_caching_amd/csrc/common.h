@@ -58,6 +58,52 @@ __device__ __forceinline__ void ld8(const float *p, float (&x)[8]) {
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
+// Raw 8-element vectors as loaded from global memory; widened when staged,
+// so a register prefetch does not wait for its data at the load.
+struct raw8_bf16 { uint4 u; };
+struct raw8_f32 { float4 a, b; };
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> { typedef raw8_bf16 type; };
+template <> struct Raw8<float> { typedef raw8_f32 type; };
+
+__device__ __forceinline__ void ld_raw8(const bf16_t *p, raw8_bf16 &r) { r.u = *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void ld_raw8(const float *p, raw8_f32 &r) {
+    r.a = reinterpret_cast<const float4 *>(p)[0];
+    r.b = reinterpret_cast<const float4 *>(p)[1];
+}
+__device__ __forceinline__ void zero_raw8(raw8_bf16 &r) { r.u = make_uint4(0u, 0u, 0u, 0u); }
+__device__ __forceinline__ void zero_raw8(raw8_f32 &r) { r.a = make_float4(0.f, 0.f, 0.f, 0.f); r.b = r.a; }
+__device__ __forceinline__ void widen8(const raw8_bf16 &r, float (&x)[8]) {
+    const uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void widen8(const raw8_f32 &r, float (&x)[8]) {
+    x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+    x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs of the chip, each with
+// its own L2.  Remap the hardware block id so that consecutive logical ids run
+// on one XCD (they then share operands through that L2).  Identity when the
+// grid is not a multiple of 8.
+__device__ __forceinline__ int xcd_logical_block(int b, int nblocks) {
+    if (nblocks % 8 != 0) return b;
+    return (b % 8) * (nblocks / 8) + b / 8;
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
+// and meets the other waves, but leaves global loads in flight, so register
+// prefetches issued before it keep streaming.  (The full __syncthreads also
+// drains every outstanding global load.)  The memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ---- bf16 hi/lo split of an fp32 value (x ~= hi + lo, |x - hi - lo| <~ 2^-17|x|)
 __device__ __forceinline__ void split_bf16(float x, __bf16 &hi, __bf16 &lo) {
     hi = (__bf16)x;

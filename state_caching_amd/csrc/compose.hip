@@ -43,7 +43,9 @@ compose_dense_kernel(const ComposeArgs a)
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;
     const int nblk = D / 16;
-    const int h = blockIdx.x / nblk, c0 = 16 * (blockIdx.x % nblk);
+    // the column blocks of one head run on one XCD and share T through its L2
+    const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int h = lb / nblk, c0 = 16 * (lb % nblk);
     const int64_t hoff = (int64_t)h * D * D;
 
     for (int idx = tid; idx < 16 * D; idx += C::NT) {
@@ -87,7 +89,7 @@ compose_dense_kernel(const ComposeArgs a)
     if (a.n > 0) fetch(0, Acur, Scur);
     for (int j = 0; j < a.n; ++j) {
         if (j + 1 < a.n) fetch(j + 1, Anext, Snext);
-        __syncthreads();
+        lds_barrier();
         if constexpr (SEAMS) {
             const int pos = a.first_pos + j;
             if (a.has_seams && pos >= 1) {
@@ -139,7 +141,7 @@ compose_dense_kernel(const ComposeArgs a)
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     for (int idx = tid; idx < 16 * D; idx += C::NT) {
         const int cc = idx / D, d = idx % D;
         a.S_out[hoff + (int64_t)d * D + c0 + cc] = sm.ST[cur][cc][d];
@@ -188,7 +190,7 @@ __global__ void __launch_bounds__(256) seam_kernel(const ComposeArgs a, float *S
     }
     const SeamArgs &sa = a.seam;
     for (int win = 0; win < n_win; ++win) {
-        __syncthreads();
+        lds_barrier();
         seam_prep<D, 64, TIN>(ws, sa, win, h, c0);
         // window pair: T_w[:, cols of this block] and S_w0[:, cols]
         if (sa.T_w) {
@@ -211,7 +213,7 @@ __global__ void __launch_bounds__(256) seam_kernel(const ComposeArgs a, float *S
         }
         seam_apply<D, 64, TIN>(ws, &ST[0][0], D + 4, sa, win, h, c0);
     }
-    __syncthreads();
+    lds_barrier();
     for (int idx = tid; idx < 16 * D; idx += blockDim.x) {
         const int cc = idx / D, d = idx % D;
         S[hoff + (int64_t)d * D + c0 + cc] = ST[cc][d];

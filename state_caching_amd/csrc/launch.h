@@ -76,6 +76,8 @@ struct ComposeArgs {
 
 hipError_t launch_build_delta(const DeltaArgs &a, int D, int kv_kind, int g_kind, bool f16,
                               int n_units, hipStream_t st);
+hipError_t launch_build_delta_f16(const DeltaArgs &a, int D, int kv_kind, int g_kind, int n_units,
+                                  hipStream_t st);
 hipError_t launch_build_decay(const DecayArgs &a, int D, int in_kind, int n_units,
                               hipStream_t st);
 hipError_t launch_conv(const ConvArgs &a, int D, int in_kind, int64_t total_rows,

@@ -103,7 +103,7 @@ __device__ void seam_prep(WinSmem<D, WMAX> &ws, const SeamArgs &a, int win, int 
         }
         if (lane == 0) ws.gw = scale_pow2(1.f, tot);
     }
-    __syncthreads();
+    lds_barrier();
     if (a.k_l2norm) {
         for (int t = wv; t < w; t += nwv) {
             float ss = 0.f;
@@ -112,7 +112,7 @@ __device__ void seam_prep(WinSmem<D, WMAX> &ws, const SeamArgs &a, int win, int 
             const float inv = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
             for (int d = lane; d < D; d += 64) ws.K[t][d] *= inv;
         }
-        __syncthreads();
+        lds_barrier();
     }
     // G (strictly lower, scaled by b_r)
     for (int idx = tid; idx < w * w; idx += nt) {
@@ -122,7 +122,7 @@ __device__ void seam_prep(WinSmem<D, WMAX> &ws, const SeamArgs &a, int win, int 
             for (int d = 0; d < D; ++d) acc += ws.K[r][d] * ws.K[c][d];
         ws.G[r][c] = ws.beta[r] * acc;
     }
-    __syncthreads();
+    lds_barrier();
     // M = (I + G)^-1 by forward substitution, one column per lane
     if (tid < w) {
         const int c = tid;
@@ -132,7 +132,7 @@ __device__ void seam_prep(WinSmem<D, WMAX> &ws, const SeamArgs &a, int win, int 
             ws.M[r][c] = acc;
         }
     }
-    __syncthreads();
+    lds_barrier();
     for (int idx = tid; idx < w * D; idx += nt) {
         const int t = idx / D, d = idx % D;
         float acc = 0.f;
@@ -145,7 +145,7 @@ __device__ void seam_prep(WinSmem<D, WMAX> &ws, const SeamArgs &a, int win, int 
         for (int q = 0; q <= t; ++q) acc += ws.M[t][q] * ws.beta[q] * ws.dec[q] * ws.V[q][cc];
         ws.U[t][cc] = acc;
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // Apply the prepared window to the state block ST[16][ldst] (in place).
@@ -169,7 +169,7 @@ __device__ void seam_apply(WinSmem<D, WMAX> &ws, float *ST, int ldst, const Seam
         const int kh = h / (a.h_v / a.h_k);
         const int64_t ldk = (int64_t)a.h_k * D;
         const TIN *qp = reinterpret_cast<const TIN *>(a.q) + (int64_t)win * w * ldk + (int64_t)kh * D;
-        __syncthreads();
+        lds_barrier();
         for (int idx = tid; idx < w * w; idx += nt) {
             const int t = idx / w, s = idx % w;
             float acc = 0.f;
@@ -177,7 +177,7 @@ __device__ void seam_apply(WinSmem<D, WMAX> &ws, float *ST, int ldst, const Seam
                 for (int d = 0; d < D; ++d) acc += ld1(qp + (int64_t)t * ldk + d) * ws.K[s][d];
             ws.G[t][s] = acc;
         }
-        __syncthreads();
+        lds_barrier();
         float *op = a.o + (int64_t)win * w * a.h_v * D + (int64_t)h * D + c0;
         for (int idx = tid; idx < w * 16; idx += nt) {
             const int t = idx / 16, cc = idx % 16;
@@ -194,7 +194,7 @@ __device__ void seam_apply(WinSmem<D, WMAX> &ws, float *ST, int ldst, const Seam
             op[(int64_t)t * a.h_v * D + cc] = gt * (qs - corr) + wr;
         }
     }
-    __syncthreads();
+    lds_barrier();
     // S' = gw S + K^T E
     for (int idx = tid; idx < D * 16; idx += nt) {
         const int cc = idx / D, d = idx % D;
@@ -202,7 +202,7 @@ __device__ void seam_apply(WinSmem<D, WMAX> &ws, float *ST, int ldst, const Seam
         for (int t = 0; t < w; ++t) acc += ws.K[t][d] * ws.E[t][cc];
         ST[cc * ldst + d] = acc;
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 }  // namespace hy
