@@ -256,7 +256,8 @@ class Seams:
 
 def compose(T_pool: torch.Tensor, S0_pool: torch.Tensor, order: Sequence[int],
             S_init: Optional[torch.Tensor] = None, tform: int = T_DENSE, prec: int = PREC_SPLIT,
-            seams: Optional[Seams] = None, S_out: Optional[torch.Tensor] = None, stream=None):
+            seams: Optional[Seams] = None, S_out: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None, stream=None):
     """S = fold_i (S <- T[order[i]] S + S0[order[i]]), seams before positions 1.."""
     n_slots, h_v, d_k, d_v = S0_pool.shape
     if tuple(T_pool.shape) != t_shape(tform, n_slots, h_v, d_k):
@@ -277,7 +278,12 @@ def compose(T_pool: torch.Tensor, S0_pool: torch.Tensor, order: Sequence[int],
                     order=ctypes.cast(ordr, _pi32), T_pool=_ptr(T_pool), S0_pool=_ptr(S0_pool),
                     S_init=_ptr(S_init), S_out=_ptr(S_out),
                     seams=ctypes.pointer(sd) if sd is not None else None)
-    _check(_lib().hypic_compose(ctypes.byref(d), None, 0, _stream(stream)), "hypic_compose")
+    L = _lib()
+    need = L.hypic_workspace_size(ctypes.byref(d), WS_COMPOSE)
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=S0_pool.device)
+    wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(L.hypic_compose(ctypes.byref(d), _ptr(workspace), wsz, _stream(stream)), "hypic_compose")
     return S_out
 
 

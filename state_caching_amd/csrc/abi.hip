@@ -95,6 +95,19 @@ hypic_status validate_seams(const hypic_seam_desc *s, int h_v, int D, int max_w)
     return HYPIC_OK;
 }
 
+// dense split compose for d in {64, 128} takes the pipelined kernel
+bool compose_uses_split(const hypic_compose_desc *d)
+{
+    return d->tform == HYPIC_T_DENSE && d->prec == HYPIC_PREC_SPLIT &&
+           (d->d_k == 64 || d->d_k == 128);
+}
+
+size_t compose_ws_bytes(const hypic_compose_desc *d)
+{
+    if (!d->seams || !compose_uses_split(d) || d->n <= 1) return 0;
+    return (size_t)seam_ops_floats(d->d_k, d->seams->w, d->n - 1, d->h_v) * sizeof(float);
+}
+
 SeamArgs seam_args(const hypic_seam_desc *s)
 {
     SeamArgs a;
@@ -132,6 +145,12 @@ size_t hypic_workspace_size(const void *desc, int which)
         const hypic_build_desc *d = static_cast<const hypic_build_desc *>(desc);
         if (validate_build(d) != HYPIC_OK) return 0;
         return build_ws_bytes(d);
+    }
+    if (which == HYPIC_WS_COMPOSE) {
+        const hypic_compose_desc *d = static_cast<const hypic_compose_desc *>(desc);
+        if (d->d_k != d->d_v || !dim_ok(d->d_k) || d->n < 0 || d->h_v <= 0) return 0;
+        if (d->seams && (d->seams->w < 1 || d->seams->w > 16)) return 0;
+        return compose_ws_bytes(d);
     }
     return 0;
 }
@@ -224,7 +243,6 @@ hypic_status hypic_segment_build(const hypic_build_desc *d, void *ws, size_t ws_
 
 hypic_status hypic_compose(const hypic_compose_desc *d, void *ws, size_t ws_bytes, void *stream)
 {
-    (void)ws; (void)ws_bytes;
     if (!d) return HYPIC_E_INVALID;
     if (d->tform < HYPIC_T_SCALAR || d->tform > HYPIC_T_DENSE) return HYPIC_E_INVALID;
     if (d->prec != HYPIC_PREC_FP32 && d->prec != HYPIC_PREC_SPLIT) return HYPIC_E_INVALID;
@@ -247,6 +265,8 @@ hypic_status hypic_compose(const hypic_compose_desc *d, void *ws, size_t ws_byte
         if (d->seams->q || d->seams->o || d->seams->T_w || d->seams->S_w0) return HYPIC_E_INVALID;
         in_kind = d->seams->in_dtype == HYPIC_BF16 ? IN_BF16 : IN_F32;
     }
+    const size_t need = compose_ws_bytes(d);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return HYPIC_E_WORKSPACE;
     hypic_status st = device_check();
     if (st != HYPIC_OK) return st;
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
@@ -256,6 +276,12 @@ hypic_status hypic_compose(const hypic_compose_desc *d, void *ws, size_t ws_byte
     a.h_v = d->h_v;
     a.has_seams = d->seams != nullptr;
     if (d->seams) a.seam = seam_args(d->seams);
+    const bool split = compose_uses_split(d);
+    float *ops = nullptr;
+    if (split && a.has_seams && d->n > 1) {
+        ops = static_cast<float *>(ws);
+        if ((st = from_hip(launch_seam_ops(a, D, in_kind, d->n - 1, ops, hs))) != HYPIC_OK) return st;
+    }
     if (d->n == 0) {
         a.S_in = d->S_init; a.S_out = d->S_out; a.n = 0;
         return from_hip(launch_compose(a, D, HYPIC_T_SCALAR, d->prec, in_kind, hs));
@@ -266,7 +292,9 @@ hypic_status hypic_compose(const hypic_compose_desc *d, void *ws, size_t ws_byte
         a.S_in = b == 0 ? d->S_init : d->S_out;
         a.S_out = d->S_out;
         for (int i = 0; i < a.n; ++i) a.order[i] = d->order[b + i];
-        if ((st = from_hip(launch_compose(a, D, d->tform, d->prec, in_kind, hs))) != HYPIC_OK) return st;
+        st = split ? from_hip(launch_compose_split(a, D, ops, hs))
+                   : from_hip(launch_compose(a, D, d->tform, d->prec, in_kind, hs));
+        if (st != HYPIC_OK) return st;
     }
     return HYPIC_OK;
 }

@@ -86,5 +86,10 @@ hipError_t launch_compose(const ComposeArgs &a, int D, int tform, int prec, int 
                           hipStream_t st);
 hipError_t launch_seam(const ComposeArgs &a, int D, int in_kind, float *S, int n_win,
                        hipStream_t st);
+// split-bf16 dense compose for d in {64, 128}, seam windows from precomputed operators
+int64_t seam_ops_floats(int D, int w, int n_win, int h_v);
+hipError_t launch_seam_ops(const ComposeArgs &a, int D, int in_kind, int n_win, float *ops,
+                           hipStream_t st);
+hipError_t launch_compose_split(const ComposeArgs &a, int D, const float *ops, hipStream_t st);
 
 }  // namespace hy

@@ -21,10 +21,10 @@
 
 namespace hy {
 
-template <int D, int WMAX>
+template <int D, int WMAX, int NC = 16>
 struct WinSmem {
     static constexpr int LD = D + 4;
-    static constexpr int LC = 16 + 4;
+    static constexpr int LC = NC + 4;
     float K[WMAX][LD];     // keys after conv / normalisation
     float W[WMAX][LD];     // M diag(b) K
     float V[WMAX][LC];     // values of this column block
@@ -46,9 +46,10 @@ __device__ __forceinline__ float win_row(const TIN *x, const TIN *tail, int t, i
     return ld1(tail + (int64_t)(Wc - 1 + t) * row_stride + col);
 }
 
-// Window prep: everything that does not depend on the state.
-template <int D, int WMAX, typename TIN>
-__device__ void seam_prep(WinSmem<D, WMAX> &ws, const SeamArgs &a, int win, int h, int c0)
+// Window prep: everything that does not depend on the state (value columns
+// [c0, c0 + NC) of head h).
+template <int D, int WMAX, typename TIN, int NC = 16>
+__device__ void seam_prep(WinSmem<D, WMAX, NC> &ws, const SeamArgs &a, int win, int h, int c0)
 {
     const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wv = tid >> 6, nwv = nt >> 6;
     const int w = a.w, Wc = a.conv_w;
@@ -72,8 +73,8 @@ __device__ void seam_prep(WinSmem<D, WMAX> &ws, const SeamArgs &a, int win, int 
         }
         ws.K[t][d] = y;
     }
-    for (int idx = tid; idx < w * 16; idx += nt) {
-        const int t = idx / 16, cc = idx % 16;
+    for (int idx = tid; idx < w * NC; idx += nt) {
+        const int t = idx / NC, cc = idx % NC;
         const int64_t col = (int64_t)h * D + c0 + cc;
         float y;
         if (Wc > 0) {
@@ -139,8 +140,8 @@ __device__ void seam_prep(WinSmem<D, WMAX> &ws, const SeamArgs &a, int win, int 
         for (int q = 0; q <= t; ++q) acc += ws.M[t][q] * ws.beta[q] * ws.K[q][d];
         ws.W[t][d] = acc;
     }
-    for (int idx = tid; idx < w * 16; idx += nt) {
-        const int t = idx / 16, cc = idx % 16;
+    for (int idx = tid; idx < w * NC; idx += nt) {
+        const int t = idx / NC, cc = idx % NC;
         float acc = 0.f;
         for (int q = 0; q <= t; ++q) acc += ws.M[t][q] * ws.beta[q] * ws.dec[q] * ws.V[q][cc];
         ws.U[t][cc] = acc;
@@ -151,7 +152,7 @@ __device__ void seam_prep(WinSmem<D, WMAX> &ws, const SeamArgs &a, int win, int 
 // Apply the prepared window to the state block ST[16][ldst] (in place).
 // With read-outs (q != null) also writes o for this window and column block.
 template <int D, int WMAX, typename TIN>
-__device__ void seam_apply(WinSmem<D, WMAX> &ws, float *ST, int ldst, const SeamArgs &a, int win,
+__device__ void seam_apply(WinSmem<D, WMAX, 16> &ws, float *ST, int ldst, const SeamArgs &a, int win,
                            int h, int c0)
 {
     const int tid = threadIdx.x, nt = blockDim.x;
@@ -203,6 +204,35 @@ __device__ void seam_apply(WinSmem<D, WMAX> &ws, float *ST, int ldst, const Seam
         ST[cc * ldst + d] = acc;
     }
     lds_barrier();
+}
+
+// Workspace record of one (window, head): the window's operators, fp32.
+//   K  [w][D]  keys after conv and normalisation
+//   W  [w][D]  M diag(b) K
+//   UT [D][w]  (M diag(b dec) V)^T, value column-major
+//   gw         gate product over the window
+template <int D>
+__host__ __device__ __forceinline__ int64_t winop_floats(int w) { return (int64_t)3 * w * D + 4; }
+
+// One workgroup per (window, head): window operators into the workspace.
+template <int D, typename TIN>
+__global__ void __launch_bounds__(256) seam_ops_kernel(const SeamArgs a, float *ops)
+{
+    __shared__ WinSmem<D, 16, D> ws;
+    const int win = blockIdx.x / a.h_v, h = blockIdx.x % a.h_v;
+    seam_prep<D, 16, TIN, D>(ws, a, win, h, 0);
+    const int w = a.w;
+    float *o = ops + ((int64_t)win * a.h_v + h) * winop_floats<D>(w);
+    for (int idx = threadIdx.x; idx < w * D; idx += blockDim.x) {
+        const int t = idx / D, d = idx % D;
+        o[idx] = ws.K[t][d];
+        o[w * D + idx] = ws.W[t][d];
+    }
+    for (int idx = threadIdx.x; idx < w * D; idx += blockDim.x) {
+        const int cc = idx / w, t = idx % w;
+        o[2 * w * D + idx] = ws.U[t][cc];
+    }
+    if (threadIdx.x == 0) o[3 * w * D] = ws.gw;
 }
 
 }  // namespace hy
