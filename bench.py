@@ -18,8 +18,10 @@ bounded sample of the headline workload.
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--leg build|compose|all]
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -29,6 +31,55 @@ sys.path.insert(0, ROOT)
 METRIC = "segment-build tokens/s + compositions/s per GPU, % of MFMA/HBM roofline"
 PEAK_MFMA_F16 = 2500.0     # TFLOP/s, MI355X dense fp16/bf16 matrix cores
 PEAK_HBM = 8000.0          # GB/s, MI355X HBM3E
+
+# HBM traffic per launch comes from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+# summarised in profiles/hbm_counters.md; a row counts only while the digest of
+# the kernel's sources still matches the one recorded with the counters.
+CSRC = os.path.join(ROOT, "state_caching_amd", "csrc")
+KERNEL_SOURCES = {
+    "build_delta_f16_kernel": ["build_delta_f16.hip", "common.h", "launch.h"],
+    "seam_ops_kernel": ["seam.h", "compose_split.hip", "common.h", "launch.h"],
+    "compose_split_kernel": ["compose_split.hip", "seam.h", "common.h", "launch.h"],
+}
+
+
+def source_digest(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:12]
+
+
+def counter_traffic(kernels, workload_tag):
+    """Scaled HBM bytes per launch summed over `kernels`, or None when any row
+    is missing or was taken on sources that have changed since."""
+    path = os.path.join(ROOT, "profiles", "hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    rows = {}
+    fetch_scale = write_scale = None
+    with open(path) as f:
+        for line in f:
+            m = re.match(r"^fetch_scale:\s*([0-9.]+)\s*$", line)
+            if m: fetch_scale = float(m.group(1))
+            m = re.match(r"^write_scale:\s*([0-9.]+)\s*$", line)
+            if m: write_scale = float(m.group(1))
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) == 6 and cells[0] in KERNEL_SOURCES:
+                try:
+                    rows[(cells[0], cells[1])] = (cells[2], float(cells[3]), float(cells[4]))
+                except ValueError:
+                    pass
+    if fetch_scale is None or write_scale is None:
+        return None
+    total = 0.0
+    for k in kernels:
+        r = rows.get((k, workload_tag))
+        if r is None or r[0] != source_digest(k):
+            return None
+        total += (r[1] * fetch_scale + r[2] * write_scale) * 1024.0
+    return total
 
 
 def log(msg):
@@ -41,7 +92,8 @@ def build_flops(n_tokens, h_v, d_k, d_v):
 
 
 def build_bytes(wl):
-    el = 2 if "bf16" in str(wl.dtype) else 4
+    import torch
+    el = 2 if wl.dtype == torch.bfloat16 else 4
     n = wl.n_tokens
     inputs = n * (wl.h_k * wl.d_k + wl.h_v * wl.d_v + 2 * wl.h_v) * el
     outputs = wl.n_seg * wl.h_v * (wl.d_k * wl.d_k + wl.d_k * wl.d_v) * 4
@@ -182,9 +234,10 @@ def main():
                                    "inputs, fp32 pairs: build all (segment, head) pairs then compose",
                        "segments": wl3.n_seg, "seg_len": 4096, "h_v": wl3.h_v, "h_k": wl3.h_k,
                        "d": 128, "in_dtype": "bf16"},
-            "roofline": {"bound": "mfma", "kernel": "build_delta_kernel<128,fp16>",
+            "roofline": {"bound": "mfma", "kernel": "build_delta_f16_kernel<128,bf16,bf16>",
                          "achieved": ach, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
-                         "frac": ach / PEAK_MFMA_F16, "traffic": None,
+                         "frac": ach / PEAK_MFMA_F16,
+                         "traffic": counter_traffic(["build_delta_f16_kernel"], "cfg3"),
                          "kernel_ms": kb, "algorithmic_flop": fl,
                          "algorithmic_bytes": build_bytes(wl3)},
             "build_tokens_per_s": wl3.n_tokens / (kb * 1e-3),
@@ -219,9 +272,11 @@ def main():
                 "compositions_per_s": wl4.n_seg / (k4 * 1e-3),
                 "head_compositions_per_s": wl4.n_seg * wl4.h_v / (k4 * 1e-3),
                 "ms_per_compose": k4, "wall_ms_per_step": wall4,
-                "roofline": {"bound": "hbm", "kernel": "compose_dense_kernel<128,split,seams>",
+                "roofline": {"bound": "hbm",
+                             "kernel": "hypic_compose = seam_ops_kernel<128> + compose_split_kernel<128,seams>",
                              "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
-                             "frac": gbs / PEAK_HBM, "traffic": None,
+                             "frac": gbs / PEAK_HBM,
+                             "traffic": counter_traffic(["seam_ops_kernel", "compose_split_kernel"], "cfg4"),
                              "algorithmic_bytes": by,
                              "mfma_tflops": compose_flops(wl4) / (k4 * 1e-3) / 1e12}}
         out["compose"] = comp
