@@ -206,33 +206,182 @@ __device__ void seam_apply(WinSmem<D, WMAX, 16> &ws, float *ST, int ldst, const 
     lds_barrier();
 }
 
-// Workspace record of one (window, head): the window's operators, fp32.
-//   K  [w][D]  keys after conv and normalisation
-//   W  [w][D]  M diag(b) K
-//   UT [D][w]  (M diag(b dec) V)^T, value column-major
-//   gw         gate product over the window
+// Workspace record of one (window, head): the window's operators, fp32, with
+// the token count padded to wp = w rounded up to 4 (padding rows are zero):
+//   W  [wp][D]  M diag(b) K                       (token-major)
+//   KT [D][wp]  keys after conv and normalisation (dimension-major)
+//   UT [D][wp]  (M diag(b dec) V)^T               (value column-major)
+//   gw          gate product over the window
+__host__ __device__ __forceinline__ int winop_wp(int w) { return (w + 3) & ~3; }
 template <int D>
-__host__ __device__ __forceinline__ int64_t winop_floats(int w) { return (int64_t)3 * w * D + 4; }
+__host__ __device__ __forceinline__ int64_t winop_floats(int w) { return (int64_t)3 * winop_wp(w) * D + 4; }
 
-// One workgroup per (window, head): window operators into the workspace.
-template <int D, typename TIN>
-__global__ void __launch_bounds__(256) seam_ops_kernel(const SeamArgs a, float *ops)
+// One wave per (window, value head): every operator of the window, with the
+// key and value rows held in registers (C = D/64 columns per lane) and the
+// small w x w factors in LDS.  WM (8 or 16) bounds w; every loop over tokens
+// runs to WM with rows beyond w zero, so reductions interleave without branches.
+template <int D, int WM, typename TIN>
+__global__ void __launch_bounds__(64) seam_ops_kernel(const SeamArgs a, float *ops)
 {
-    __shared__ WinSmem<D, 16, D> ws;
+    constexpr int C = D / 64, XR = WM + 3, NP = WM * (WM - 1) / 2;
+    __shared__ float G[WM][WM + 1];   // b_r k_r.k_s, s < r
+    __shared__ float M[WM][WM + 1];   // (I + G)^-1, unit lower triangular
+    __shared__ float bq[WM], bd[WM];  // b_q and b_q dec_q
+    const int lane = threadIdx.x;
     const int win = blockIdx.x / a.h_v, h = blockIdx.x % a.h_v;
-    seam_prep<D, 16, TIN, D>(ws, a, win, h, 0);
-    const int w = a.w;
+    const int w = a.w, Wc = a.conv_w, wp = winop_wp(w);
+    const int kh = h / (a.h_v / a.h_k);
+    const int64_t ldk = (int64_t)a.h_k * D, ldv = (int64_t)a.h_v * D;
+    const TIN *xk = reinterpret_cast<const TIN *>(a.xk) + (int64_t)win * w * ldk + (int64_t)kh * D;
+    const TIN *xv = reinterpret_cast<const TIN *>(a.xv) + (int64_t)win * w * ldv + (int64_t)h * D;
+    const TIN *tk = Wc > 1 ? reinterpret_cast<const TIN *>(a.tail_k) + (int64_t)win * (Wc - 1) * ldk + (int64_t)kh * D : nullptr;
+    const TIN *tv = Wc > 1 ? reinterpret_cast<const TIN *>(a.tail_v) + (int64_t)win * (Wc - 1) * ldv + (int64_t)h * D : nullptr;
     float *o = ops + ((int64_t)win * a.h_v + h) * winop_floats<D>(w);
-    for (int idx = threadIdx.x; idx < w * D; idx += blockDim.x) {
-        const int t = idx / D, d = idx % D;
-        o[idx] = ws.K[t][d];
-        o[w * D + idx] = ws.W[t][d];
+
+    // gates first (their loads overlap the row loads): b, suffix decay, window product
+    float gb = 0.f, gl2 = 0.f;
+    if (lane < w) {
+        gb = ld1(reinterpret_cast<const TIN *>(a.beta) + ((int64_t)win * w + lane) * a.h_v + h);
+        gl2 = log2f(ld1(reinterpret_cast<const TIN *>(a.alpha) + ((int64_t)win * w + lane) * a.h_v + h));
     }
-    for (int idx = threadIdx.x; idx < w * D; idx += blockDim.x) {
-        const int cc = idx / w, t = idx % w;
-        o[2 * w * D + idx] = ws.U[t][cc];
+
+    // keys and values after the causal conv: the extended rows (Wc - 1 tail rows,
+    // then the window) are loaded once; x_s sits in extended row s + Wc - 1, so
+    // tap j of output t reads row t + j
+    float K[WM][C], V[WM][C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int d = lane + 64 * c;
+        const int nh = Wc > 1 ? Wc - 1 : 0;
+        float xk_[XR], xv_[XR];
+#pragma unroll
+        for (int r = 0; r < XR; ++r) {
+            // row address selected (no branch): tail row, window row, or past the
+            // window (clamped to the last row and masked to 0)
+            const int tt = r - nh;
+            const bool in = tt < w;
+            const int ti = in ? tt : w - 1;
+            const TIN *pk = ti >= 0 ? xk + (int64_t)ti * ldk : tk + (int64_t)(nh + ti) * ldk;
+            const TIN *pv = ti >= 0 ? xv + (int64_t)ti * ldv : tv + (int64_t)(nh + ti) * ldv;
+            const float kx = ld1(pk + d), vx = ld1(pv + d);
+            xk_[r] = in ? kx : 0.f;
+            xv_[r] = in ? vx : 0.f;
+        }
+        float wk[4] = {0.f, 0.f, 0.f, 0.f}, wvv[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < Wc; ++j) {
+            wk[j] = a.conv_wk[((int64_t)kh * D + d) * Wc + j];
+            wvv[j] = a.conv_wv[((int64_t)h * D + d) * Wc + j];
+        }
+#pragma unroll
+        for (int t = 0; t < WM; ++t) {
+            float yk = 0.f, yv = 0.f;
+            if (Wc > 0) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    yk += wk[j] * xk_[t + j];   // taps beyond Wc have weight 0
+                    yv += wvv[j] * xv_[t + j];
+                }
+            } else {
+                yk = xk_[t];
+                yv = xv_[t];
+            }
+            K[t][c] = t < w ? yk : 0.f;
+            V[t][c] = t < w ? yv : 0.f;
+        }
     }
-    if (threadIdx.x == 0) o[3 * w * D] = ws.gw;
+    if (a.k_l2norm) {
+        float ss[WM];
+#pragma unroll
+        for (int t = 0; t < WM; ++t) {
+            ss[t] = 0.f;
+#pragma unroll
+            for (int c = 0; c < C; ++c) ss[t] += K[t][c] * K[t][c];
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1)
+#pragma unroll
+            for (int t = 0; t < WM; ++t) ss[t] += __shfl_xor(ss[t], m);
+#pragma unroll
+        for (int t = 0; t < WM; ++t) {
+            const float inv = ss[t] > 0.f ? 1.f / sqrtf(ss[t]) : 0.f;
+#pragma unroll
+            for (int c = 0; c < C; ++c) K[t][c] *= inv;
+        }
+    }
+    {
+        const float sfx = wave_suffix_excl(gl2);
+        const double tot = wave_sum_f64((double)gl2);
+        if (lane < WM) {
+            bq[lane] = gb;
+            bd[lane] = gb * exp2f(sfx);
+        }
+        if (lane == 0) o[(int64_t)3 * wp * D] = scale_pow2(1.f, tot);
+    }
+    // Gram pairs r > q, all reduced together
+    {
+        float dot[NP];
+#pragma unroll
+        for (int r = 1, p = 0; r < WM; ++r)
+#pragma unroll
+            for (int q = 0; q < r; ++q, ++p) {
+                dot[p] = 0.f;
+#pragma unroll
+                for (int c = 0; c < C; ++c) dot[p] += K[r][c] * K[q][c];
+            }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1)
+#pragma unroll
+            for (int p = 0; p < NP; ++p) dot[p] += __shfl_xor(dot[p], m);
+        __syncthreads();   // bq visible
+        if (lane == 0) {
+#pragma unroll
+            for (int r = 1, p = 0; r < WM; ++r)
+#pragma unroll
+                for (int q = 0; q < r; ++q, ++p) G[r][q] = bq[r] * dot[p];
+        }
+    }
+    __syncthreads();
+    // M = (I + G)^-1: lane c < WM owns column c; rows of G are broadcast reads
+    if (lane < WM) {
+        const int c = lane;
+        float mc[WM];
+#pragma unroll
+        for (int r = 0; r < WM; ++r) {
+            float acc = (r == c) ? 1.f : 0.f;
+#pragma unroll
+            for (int q = 0; q < r; ++q) acc -= (q >= c ? G[r][q] : 0.f) * mc[q];
+            mc[r] = r >= c ? acc : 0.f;
+            M[r][c] = mc[r];
+        }
+    }
+    __syncthreads();
+    float *oW = o, *oKT = o + (int64_t)wp * D, *oUT = o + (int64_t)2 * wp * D;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int d = lane + 64 * c;
+        float Wd[WM], Ud[WM];
+#pragma unroll
+        for (int t = 0; t < WM; ++t) {
+            float sw = 0.f, su = 0.f;
+#pragma unroll
+            for (int q = 0; q <= t; ++q) {
+                const float m = M[t][q];
+                sw += m * bq[q] * K[q][c];
+                su += m * bd[q] * V[q][c];
+            }
+            Wd[t] = t < w ? sw : 0.f;
+            Ud[t] = t < w ? su : 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < WM; ++t)
+            if (t < wp) oW[(int64_t)t * D + d] = Wd[t];
+#pragma unroll
+        for (int t4 = 0; t4 < WM; t4 += 4)
+            if (t4 < wp) {
+                *reinterpret_cast<float4 *>(oKT + (int64_t)d * wp + t4) = make_float4(K[t4][c], K[t4 + 1][c], K[t4 + 2][c], K[t4 + 3][c]);
+                *reinterpret_cast<float4 *>(oUT + (int64_t)d * wp + t4) = make_float4(Ud[t4], Ud[t4 + 1], Ud[t4 + 2], Ud[t4 + 3]);
+            }
+    }
 }
 
 }  // namespace hy
