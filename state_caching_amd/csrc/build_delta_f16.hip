@@ -30,8 +30,8 @@ struct F16Cfg {
     static constexpr int NT = 64 * (NS + NP);
     static constexpr int MT = D / 16;
     static constexpr int KB = D / 32;
-    static constexpr int LDT = 72;            // KT row stride (halves), token-major within a row
-    static constexpr int LDW = D + 8;         // nW / Ks row stride (halves)
+    static constexpr int LDT = 72;            // row stride (halves) of token-contiguous rows
+    static constexpr int LDW = D + 8;         // Ks / Vs row stride (halves)
     static constexpr int LDU = 68;            // UT row stride (floats)
     static constexpr int LDG = 68;
     static constexpr int PASSES = D / 32;     // prep staging passes of 16 rows
@@ -40,15 +40,15 @@ struct F16Cfg {
 template <int D>
 struct F16Smem {
     using C = F16Cfg<D>;
-    _Float16 KT[2][D][C::LDT];   // keys, dim-major, token groups XOR-swizzled per row
-    _Float16 nW[64][C::LDW];     // -W = -M diag(b) K, token-major
+    _Float16 Ks[2][64][C::LDW];  // keys, token-major, per pipeline slot (K^T operands
+                                 // come from transposed loads of these rows)
+    _Float16 nWT[D][C::LDT];     // -W^T = -(M diag(b) K)^T, token-contiguous rows
     float UT[D][C::LDU];         // U^T (value column-major), in units of 2^sv
-    _Float16 VT[D][C::LDT];      // V * 2^-sv, dim-major, swizzled like KT
-    _Float16 Ks[64][C::LDW];     // keys, token-major (Gram)
+    _Float16 Vs[64][C::LDW];     // V * 2^-sv, token-major
     float Gm[64][C::LDG];        // b_r k_r.k_s for s < r; the inverse of each diagonal
                                  // 16x16 block is kept transposed in its upper triangle
-    _Float16 M1[64][72];         // M diag(b)
-    _Float16 M2[64][72];         // M diag(b dec)
+    _Float16 M1T[64][C::LDT];    // (M diag(b))^T
+    _Float16 M2T[64][C::LDT];    // (M diag(b dec))^T
     float beta[64], bd[64];
     float gb[2];                 // chunk gate product, per pipeline slot
     int sv[2];                   // value scale exponent, per pipeline slot
@@ -56,8 +56,21 @@ struct F16Smem {
     double cl_tot;
 };
 
-// XOR swizzle of 8-token groups within a dim-major row (spreads transposed stores over banks)
-__device__ __forceinline__ int swz(int d, int t) { return t ^ (((d >> 3) & 7) << 3); }
+typedef short s4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s4v lds_s4v;
+
+// Four consecutive reduction indices of a matrix-core operand whose lane index
+// (row m of A or column n of B) runs along LDS rows: storage S[k][x], x
+// contiguous.  The 16 lanes of each lane group receive S[k0 + e][x0 + lane%16],
+// e = 0..3 (k0 may differ between groups), through the LDS transpose load:
+// lane j of a group supplies the 4-element block at S[k0 + j/4][x0 + 4 (j%4)].
+__device__ __forceinline__ h4 ld_tr4(const _Float16 *S, int ld, int k0, int x0, int lane)
+{
+    const int j = lane & 15;
+    const _Float16 *p = S + (k0 + (j >> 2)) * ld + x0 + 4 * (j & 3);
+    return __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v *)p));
+}
+__device__ __forceinline__ h8 cat8(h4 lo, h4 hi) { return h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}; }
 
 __constant__ int kOffTi[6] = {1, 2, 2, 3, 3, 3};
 __constant__ int kOffTj[6] = {0, 0, 1, 0, 1, 2};
@@ -80,10 +93,10 @@ build_delta_f16_kernel(const DeltaArgs a)
     const int nch = (len + 63) / 64;
     const bool is_prep = w >= NS;
 
-    // upper tile blocks of M1/M2 are never written
+    // M1T/M2T blocks above the diagonal (of M) are never written
     for (int idx = tid; idx < 64 * 64; idx += C::NT) {
-        const int r = idx >> 6, c = idx & 63;
-        if ((c >> 4) > (r >> 4)) { sm.M1[r][c] = (_Float16)0; sm.M2[r][c] = (_Float16)0; }
+        const int r = idx >> 6, c = idx & 63;   // M[r][c] at [c][r]
+        if ((c >> 4) > (r >> 4)) { sm.M1T[c][r] = (_Float16)0; sm.M2T[c][r] = (_Float16)0; }
     }
 
     // Warp-specialised roles.  Both loops run nch + 1 iterations of four
@@ -142,10 +155,9 @@ build_delta_f16_kernel(const DeltaArgs a)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         kk[e] = (_Float16)kx[e];
-                        sm.KT[bp_][pcol + e][swz(pcol + e, t)] = kk[e];
                         vm = fmaxf(vm, fabsf(vx[e]));
                     }
-                    *reinterpret_cast<h8 *>(&sm.Ks[t][pcol]) = kk;
+                    *reinterpret_cast<h8 *>(&sm.Ks[bp_][t][pcol]) = kk;
                 }
                 vm = wave_max(vm);
                 if (lane == 0) sm.wmax[pw] = vm;
@@ -173,8 +185,10 @@ build_delta_f16_kernel(const DeltaArgs a)
                         float vx[8];
                         widen8(vraw[p], vx);
                         const int t = prow + RPP * p;
+                        h8 vv;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) sm.VT[pcol + e][swz(pcol + e, t)] = (_Float16)(vx[e] * vsc);
+                        for (int e = 0; e < 8; ++e) vv[e] = (_Float16)(vx[e] * vsc);
+                        *reinterpret_cast<h8 *>(&sm.Vs[t][pcol]) = vv;
                     }
                     if (cp + 1 < nch) fetch_v(cp + 1);
                 }
@@ -187,7 +201,7 @@ build_delta_f16_kernel(const DeltaArgs a)
                     f4 acc = zero4();
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) {
-                        const h8 A = *reinterpret_cast<const h8 *>(&sm.Ks[o + r16][32 * kb + 8 * g]);
+                        const h8 A = *reinterpret_cast<const h8 *>(&sm.Ks[bp_][o + r16][32 * kb + 8 * g]);
                         acc = mma(A, A, acc);
                     }
 #pragma unroll
@@ -235,8 +249,8 @@ build_delta_f16_kernel(const DeltaArgs a)
                     f4 acc = zero4();
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) {
-                        const h8 A = *reinterpret_cast<const h8 *>(&sm.Ks[16 * ti + r16][32 * kb + 8 * g]);
-                        const h8 B = *reinterpret_cast<const h8 *>(&sm.Ks[16 * tj + r16][32 * kb + 8 * g]);
+                        const h8 A = *reinterpret_cast<const h8 *>(&sm.Ks[bp_][16 * ti + r16][32 * kb + 8 * g]);
+                        const h8 B = *reinterpret_cast<const h8 *>(&sm.Ks[bp_][16 * tj + r16][32 * kb + 8 * g]);
                         acc = mma(A, B, acc);
                     }
 #pragma unroll
@@ -287,12 +301,15 @@ build_delta_f16_kernel(const DeltaArgs a)
                 const float bcol = sm.beta[16 * j + r16], bdcol = sm.bd[16 * j + r16];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    if (i >= j) {
+                    if (i >= j) {   // M[16i + 4g + r][16j + r16] at [16j + r16][16i + 4g + r]
+                        h4 m1, m2;
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            sm.M1[16 * i + 4 * g + r][16 * j + r16] = (_Float16)(Mc[i][r] * bcol);
-                            sm.M2[16 * i + 4 * g + r][16 * j + r16] = (_Float16)(Mc[i][r] * bdcol);
+                            m1[r] = (_Float16)(Mc[i][r] * bcol);
+                            m2[r] = (_Float16)(Mc[i][r] * bdcol);
                         }
+                        *reinterpret_cast<h4 *>(&sm.M1T[16 * j + r16][16 * i + 4 * g]) = m1;
+                        *reinterpret_cast<h4 *>(&sm.M2T[16 * j + r16][16 * i + 4 * g]) = m2;
                     }
                 }
             }
@@ -307,12 +324,17 @@ build_delta_f16_kernel(const DeltaArgs a)
                         f4 acc = zero4();
                         const int kbmax = (16 * ti + 15) / 32;
                         for (int kb = 0; kb <= kbmax; ++kb) {
-                            const h8 A = *reinterpret_cast<const h8 *>(&sm.M1[16 * ti + r16][32 * kb + 8 * g]);
-                            const h8 B = *reinterpret_cast<const h8 *>(&sm.KT[bp_][d][swz(d, 32 * kb + 8 * g)]);
+                            const int k0 = 32 * kb + 8 * g;
+                            const h8 A = cat8(ld_tr4(&sm.M1T[0][0], C::LDT, k0, 16 * ti, lane),
+                                              ld_tr4(&sm.M1T[0][0], C::LDT, k0 + 4, 16 * ti, lane));
+                            const h8 B = cat8(ld_tr4(&sm.Ks[bp_][0][0], C::LDW, k0, 16 * td, lane),
+                                              ld_tr4(&sm.Ks[bp_][0][0], C::LDW, k0 + 4, 16 * td, lane));
                             acc = mma(A, B, acc);
                         }
+                        h4 nw;   // -W[16 ti + 4g + i][d] at nWT[d][16 ti + 4g + i]
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) sm.nW[16 * ti + 4 * g + i][16 * td + r16] = (_Float16)(-acc[i]);
+                        for (int i = 0; i < 4; ++i) nw[i] = (_Float16)(-acc[i]);
+                        *reinterpret_cast<h4 *>(&sm.nWT[d][16 * ti + 4 * g]) = nw;
                     }
                 }
                 // U = M diag(b dec) V^ for value-column tiles {pw, pw + 4, ...}
@@ -321,14 +343,17 @@ build_delta_f16_kernel(const DeltaArgs a)
                     h8 Bv[2];
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
-                        Bv[kb] = *reinterpret_cast<const h8 *>(&sm.VT[cc][swz(cc, 32 * kb + 8 * g)]);
+                        Bv[kb] = cat8(ld_tr4(&sm.Vs[0][0], C::LDW, 32 * kb + 8 * g, 16 * tc, lane),
+                                      ld_tr4(&sm.Vs[0][0], C::LDW, 32 * kb + 8 * g + 4, 16 * tc, lane));
                     f4 U[4];
 #pragma unroll
                     for (int ti = 0; ti < 4; ++ti) {
                         U[ti] = zero4();
                         const int kbmax = (16 * ti + 15) / 32;
                         for (int kb = 0; kb <= kbmax; ++kb) {
-                            const h8 A = *reinterpret_cast<const h8 *>(&sm.M2[16 * ti + r16][32 * kb + 8 * g]);
+                            const int k0 = 32 * kb + 8 * g;
+                            const h8 A = cat8(ld_tr4(&sm.M2T[0][0], C::LDT, k0, 16 * ti, lane),
+                                              ld_tr4(&sm.M2T[0][0], C::LDT, k0 + 4, 16 * ti, lane));
                             U[ti] = mma(A, Bv[kb], U[ti]);
                         }
                     }
@@ -350,7 +375,7 @@ build_delta_f16_kernel(const DeltaArgs a)
         // ----------------------------------------------------------- state state
         f4 X[MT][C::TPW];
         float sig[C::TPW] = {0.f, 0.f, 0.f, 0.f};
-        h8 Eb[2][2];   // E of two column tiles as fp16 B operands (token blocks 0-31, 32-63)
+        h8 Eb[C::TPW][2];  // E of the four column tiles as fp16 B operands (token blocks 0-31, 32-63)
         {
 #pragma unroll
             for (int jn = 0; jn < C::TPW; ++jn) {
@@ -385,74 +410,79 @@ build_delta_f16_kernel(const DeltaArgs a)
                 for (int mt = 0; mt < MT; ++mt) X[mt][jn] *= f;
                 sig[jn] = target;
             };
-            auto state_e = [&](int jn, int sl) {
-                const int n = C::TPW * w + jn;
-                const bool isS = n >= MT;
-                if (isS) {
-                    const float gbv = sm.gb[bs_];
+            // E = U 2^(sv - sig) - W Xhat for all four tiles, token tiles {2 hb, 2 hb + 1}
+            // per phase: every W fragment read from LDS feeds the four tiles' products
+            auto state_prescale = [&]() {   // chunk gate on S, value-scale catch-up
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) X[mt][jn] *= gbv;
+                for (int jn = 0; jn < C::TPW; ++jn) {
+                    const int n = C::TPW * w + jn;
+                    if (n >= MT) {
+                        const float gbv = sm.gb[bs_];
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) X[mt][jn] *= gbv;
+                        if (cs == 0) sig[jn] = (float)sm.sv[bs_];   // S starts at 0: take the value scale
+                        if ((float)sm.sv[bs_] > sig[jn] + 4.f) renorm(jn, true, (float)sm.sv[bs_]);
+                    }
                 }
-                f4 E[4];
+            };
+            auto state_e_half = [&](int hb) {
+                f4 E[C::TPW][2];
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti) E[ti] = zero4();
-                if (isS && cs == 0) sig[jn] = (float)sm.sv[bs_];   // S starts at 0: take the value scale
-                if (isS && (float)sm.sv[bs_] > sig[jn] + 4.f) renorm(jn, true, (float)sm.sv[bs_]);
-                if (isS) {
-                    const float usc = exp2f((float)sm.sv[bs_] - sig[jn]);
-                    const int cc = 16 * (n - MT) + r16;
+                for (int jn = 0; jn < C::TPW; ++jn) {
+                    const int n = C::TPW * w + jn;
 #pragma unroll
-                    for (int ti = 0; ti < 4; ++ti) {
-                        const float4 u = *reinterpret_cast<const float4 *>(&sm.UT[cc][16 * ti + 4 * g]);
-                        E[ti] = f4{u.x, u.y, u.z, u.w} * usc;
+                    for (int tj = 0; tj < 2; ++tj) E[jn][tj] = zero4();
+                    if (n >= MT) {
+                        const float usc = exp2f((float)sm.sv[bs_] - sig[jn]);
+                        const int cc = 16 * (n - MT) + r16;
+#pragma unroll
+                        for (int tj = 0; tj < 2; ++tj) {
+                            const float4 u = *reinterpret_cast<const float4 *>(&sm.UT[cc][16 * (2 * hb + tj) + 4 * g]);
+                            E[jn][tj] = f4{u.x, u.y, u.z, u.w} * usc;
+                        }
                     }
                 }
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
-                    h8 B;
+                    h8 B[C::TPW];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        B[i] = (_Float16)X[2 * kb][jn][i];
-                        B[4 + i] = (_Float16)X[2 * kb + 1][jn][i];
-                    }
+                    for (int jn = 0; jn < C::TPW; ++jn)
 #pragma unroll
-                    for (int ti = 0; ti < 4; ++ti) {
-                        const h4 lo = *reinterpret_cast<const h4 *>(&sm.nW[16 * ti + r16][32 * kb + 4 * g]);
-                        const h4 hi = *reinterpret_cast<const h4 *>(&sm.nW[16 * ti + r16][32 * kb + 16 + 4 * g]);
-                        h8 A;
+                        for (int i = 0; i < 4; ++i) {
+                            B[jn][i] = (_Float16)X[2 * kb][jn][i];
+                            B[jn][4 + i] = (_Float16)X[2 * kb + 1][jn][i];
+                        }
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) { A[e] = lo[e]; A[4 + e] = hi[e]; }
-                        E[ti] = mma(A, B, E[ti]);
+                    for (int tj = 0; tj < 2; ++tj) {
+                        const int ti = 2 * hb + tj;
+                        // -W[16 ti + m][k], k = 32 kb + 4g + (e & 3) + 16 (e >> 2)
+                        const h8 A = cat8(ld_tr4(&sm.nWT[0][0], C::LDT, 32 * kb + 4 * g, 16 * ti, lane),
+                                          ld_tr4(&sm.nWT[0][0], C::LDT, 32 * kb + 16 + 4 * g, 16 * ti, lane));
+#pragma unroll
+                        for (int jn = 0; jn < C::TPW; ++jn) E[jn][tj] = mma(A, B[jn], E[jn][tj]);
                     }
                 }
+                // token block hb (tokens 32 hb .. 32 hb + 31) as fp16 B operands
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int jn = 0; jn < C::TPW; ++jn)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        Eb[sl][kb][i] = (_Float16)E[2 * kb][i];
-                        Eb[sl][kb][4 + i] = (_Float16)E[2 * kb + 1][i];
+                        Eb[jn][hb][i] = (_Float16)E[jn][0][i];
+                        Eb[jn][hb][4 + i] = (_Float16)E[jn][1][i];
                     }
             };
-            // X += K^T E for two column tiles at once (they share the K^T fragments);
-            // rows in two halves so only half of the fragments are live at a time
-            auto state_u2 = [&](int j0, int s0, int j1, int s1) {
+            // Xhat += K^T E for all four tiles, row tiles [m0, m1): every K^T fragment
+            // read from LDS feeds the four tiles' products
+            auto state_u4 = [&](int m0, int m1) {
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    asm volatile("" ::: "memory");
+                for (int mt = m0; mt < m1; ++mt) {
 #pragma unroll
-                    for (int mh = 0; mh < MT / 2; ++mh) {
-                        const int mt = half * (MT / 2) + mh;
-                        const int d = 16 * mt + r16;
+                    for (int kb = 0; kb < 2; ++kb) {
+                        // K^T[16 mt + m][t], t = 32 kb + 4g + (e & 3) + 16 (e >> 2)
+                        const h8 A = cat8(ld_tr4(&sm.Ks[bs_][0][0], C::LDW, 32 * kb + 4 * g, 16 * mt, lane),
+                                          ld_tr4(&sm.Ks[bs_][0][0], C::LDW, 32 * kb + 16 + 4 * g, 16 * mt, lane));
 #pragma unroll
-                        for (int kb = 0; kb < 2; ++kb) {
-                            const h4 lo = *reinterpret_cast<const h4 *>(&sm.KT[bs_][d][swz(d, 32 * kb + 4 * g)]);
-                            const h4 hi = *reinterpret_cast<const h4 *>(&sm.KT[bs_][d][swz(d, 32 * kb + 16 + 4 * g)]);
-                            h8 A;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) { A[e] = lo[e]; A[4 + e] = hi[e]; }
-                            X[mt][j0] = mma(A, Eb[s0][kb], X[mt][j0]);
-                            X[mt][j1] = mma(A, Eb[s1][kb], X[mt][j1]);
-                        }
+                        for (int jn = 0; jn < C::TPW; ++jn) X[mt][jn] = mma(A, Eb[jn][kb], X[mt][jn]);
                     }
                 }
             };
@@ -460,13 +490,20 @@ build_delta_f16_kernel(const DeltaArgs a)
                 const int n = C::TPW * w + jn;
                 if ((cs & 3) == 3) renorm(jn, n >= MT, (float)sm.sv[bs_]);
             };
-            if (dos) { state_e(0, 0); state_e(1, 1); }
+            if (dos) {
+                state_prescale();
+                state_e_half(0);
+            }
             lds_barrier();
-            if (dos) { state_u2(0, 0, 1, 1); state_u(0); state_u(1); }
+            if (dos) state_e_half(1);
             lds_barrier();
-            if (dos) { state_e(2, 0); state_e(3, 1); }
+            if (dos) state_u4(0, MT / 2);
             lds_barrier();
-            if (dos) { state_u2(2, 0, 3, 1); state_u(2); state_u(3); }
+            if (dos) {
+                state_u4(MT / 2, MT);
+#pragma unroll
+                for (int jn = 0; jn < C::TPW; ++jn) state_u(jn);
+            }
             lds_barrier();
         }
 
