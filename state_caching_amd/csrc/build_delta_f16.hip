@@ -47,8 +47,7 @@ struct F16Smem {
     _Float16 Vs[64][C::LDW];     // V * 2^-sv, token-major
     float Gm[64][C::LDG];        // b_r k_r.k_s for s < r; the inverse of each diagonal
                                  // 16x16 block is kept transposed in its upper triangle
-    _Float16 M1T[64][C::LDT];    // (M diag(b))^T
-    _Float16 M2T[64][C::LDT];    // (M diag(b dec))^T
+    float Mi[4][16][20];         // inverses of the diagonal blocks, row-major
     float beta[64], bd[64];
     float gb[2];                 // chunk gate product, per pipeline slot
     int sv[2];                   // value scale exponent, per pipeline slot
@@ -93,11 +92,6 @@ build_delta_f16_kernel(const DeltaArgs a)
     const int nch = (len + 63) / 64;
     const bool is_prep = w >= NS;
 
-    // M1T/M2T blocks above the diagonal (of M) are never written
-    for (int idx = tid; idx < 64 * 64; idx += C::NT) {
-        const int r = idx >> 6, c = idx & 63;   // M[r][c] at [c][r]
-        if ((c >> 4) > (r >> 4)) { sm.M1T[c][r] = (_Float16)0; sm.M2T[c][r] = (_Float16)0; }
-    }
 
     // Warp-specialised roles.  Both loops run nch + 1 iterations of four
     // barriers each, so every barrier meets all waves; prep runs one chunk ahead.
@@ -136,6 +130,9 @@ build_delta_f16_kernel(const DeltaArgs a)
             }
         };
         if (nch > 0) { fetch_k(0); fetch_v(0); }
+        constexpr int NTW = MT / 4;   // W (and U) column tiles per prep wave
+        const h4 h4z = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+        h4 Xw[NTW][4], Xu[NTW][4];    // solved row blocks, fp16 B fragments
 
 
         for (int it = 0; it <= nch; ++it) {
@@ -192,26 +189,29 @@ build_delta_f16_kernel(const DeltaArgs a)
                     }
                     if (cp + 1 < nch) fetch_v(cp + 1);
                 }
-                // diagonal Gram tile b = pw, then the inverse of I + A'_bb by forward
-                // substitution.  A'_bb is written transposed into the block's upper
-                // triangle (column q of A' is then one contiguous row), and the
-                // inverse M_bb overwrites it, also transposed, when done.
-                {
-                    const int b = pw, o = 16 * b;
-                    f4 acc = zero4();
+                if (pw == 0) {
+                    // the four diagonal Gram tiles, then the inverses of I + A'_bb for all
+                    // four blocks at once (lanes 16b .. 16b + 15 solve block b).  A'_bb is
+                    // written transposed into the block's upper triangle (column q of A'
+                    // is then one contiguous row); the inverse M_bb goes to Mi[b] row-major.
 #pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) {
-                        const h8 A = *reinterpret_cast<const h8 *>(&sm.Ks[bp_][o + r16][32 * kb + 8 * g]);
-                        acc = mma(A, A, acc);
-                    }
+                    for (int b = 0; b < 4; ++b) {
+                        const int o = 16 * b;
+                        f4 acc = zero4();
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int rr = 4 * g + i;   // A'[rr][r16] for r16 < rr, stored at [r16][rr]
-                        if (r16 < rr) sm.Gm[o + r16][o + rr] = sm.beta[o + rr] * acc[i];
+                        for (int kb = 0; kb < KB; ++kb) {
+                            const h8 A = *reinterpret_cast<const h8 *>(&sm.Ks[bp_][o + r16][32 * kb + 8 * g]);
+                            acc = mma(A, A, acc);
+                        }
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int rr = 4 * g + i;   // A'[rr][r16] for r16 < rr, stored at [r16][rr]
+                            if (r16 < rr) sm.Gm[o + r16][o + rr] = sm.beta[o + rr] * acc[i];
+                        }
                     }
                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                    if (lane < 16) {
-                        const int c = lane;
+                    {
+                        const int o = 16 * g, c = r16;   // block g, column c
                         float x[16];
 #pragma unroll
                         for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
@@ -237,132 +237,84 @@ build_delta_f16_kernel(const DeltaArgs a)
                             for (int r = q + 1; r < 16; ++r) x[r] -= colv[r] * x[q];
                         }
                         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                        // M_bb[r][c] (r >= c) kept at Gm[o + c][o + r]
 #pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            if (r >= c) sm.Gm[o + c][o + r] = x[r];
+                        for (int r = 0; r < 16; ++r) sm.Mi[g][r][c] = x[r];   // zero above the diagonal
                     }
-                }
-                // off-diagonal Gram tiles
-                for (int q = pw; q < 6; q += 4) {
-                    const int ti = kOffTi[q], tj = kOffTj[q];
-                    f4 acc = zero4();
+                } else {
+                    // off-diagonal Gram tiles, two per wave
 #pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) {
-                        const h8 A = *reinterpret_cast<const h8 *>(&sm.Ks[bp_][16 * ti + r16][32 * kb + 8 * g]);
-                        const h8 B = *reinterpret_cast<const h8 *>(&sm.Ks[bp_][16 * tj + r16][32 * kb + 8 * g]);
-                        acc = mma(A, B, acc);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int rr = 16 * ti + 4 * g + i;
-                        sm.Gm[rr][16 * tj + r16] = sm.beta[rr] * acc[i];
-                    }
-                }
-            }
-            lds_barrier();
-            // ===================== phase 3: M column chains | E tile 1
-            if (dop) {
-                const int j = pw;   // column block of M this wave completes (indices unrolled)
-                f4 Mc[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    Mc[i] = zero4();
-                    if (i == j) {   // M_jj in accumulator layout: rows 4g + r, column r16
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int row = 4 * g + r;
-                            Mc[i][r] = (r16 <= row) ? sm.Gm[16 * i + r16][16 * i + row] : 0.f;
-                        }
-                    }
-                }
-#pragma unroll
-                for (int i = 1; i < 4; ++i) {
-                    if (i > j) {
+                    for (int u = 0; u < 2; ++u) {
+                        const int q = 2 * (pw - 1) + u;
+                        const int ti = kOffTi[q], tj = kOffTj[q];
                         f4 acc = zero4();
 #pragma unroll
-                        for (int t = 0; t < i; ++t) {
-                            if (t >= j) {
-#pragma unroll
-                                for (int r = 0; r < 4; ++r)
-                                    acc = mma(sm.Gm[16 * i + r16][16 * t + 4 * g + r], Mc[t][r], acc);
-                            }
-                        }
-                        f4 m = zero4();
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int k = 4 * g + r;   // M_ii[r16][k], zero above the diagonal
-                            const float mik = (k <= r16) ? sm.Gm[16 * i + k][16 * i + r16] : 0.f;
-                            m = mma(mik, acc[r], m);
-                        }
-                        Mc[i] = -m;
-                    }
-                }
-                const float bcol = sm.beta[16 * j + r16], bdcol = sm.bd[16 * j + r16];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (i >= j) {   // M[16i + 4g + r][16j + r16] at [16j + r16][16i + 4g + r]
-                        h4 m1, m2;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            m1[r] = (_Float16)(Mc[i][r] * bcol);
-                            m2[r] = (_Float16)(Mc[i][r] * bdcol);
-                        }
-                        *reinterpret_cast<h4 *>(&sm.M1T[16 * j + r16][16 * i + 4 * g]) = m1;
-                        *reinterpret_cast<h4 *>(&sm.M2T[16 * j + r16][16 * i + 4 * g]) = m2;
-                    }
-                }
-            }
-            lds_barrier();
-            // ===================== phase 4: W and U of chunk cp | update tile 1 =
-            if (dop) {
-                // W = M diag(b) K (stored negated), key-column tiles {pw, pw + 4, ...}
-                for (int td = pw; td < MT; td += 4) {
-                    const int d = 16 * td + r16;
-#pragma unroll
-                    for (int ti = 0; ti < 4; ++ti) {
-                        f4 acc = zero4();
-                        const int kbmax = (16 * ti + 15) / 32;
-                        for (int kb = 0; kb <= kbmax; ++kb) {
-                            const int k0 = 32 * kb + 8 * g;
-                            const h8 A = cat8(ld_tr4(&sm.M1T[0][0], C::LDT, k0, 16 * ti, lane),
-                                              ld_tr4(&sm.M1T[0][0], C::LDT, k0 + 4, 16 * ti, lane));
-                            const h8 B = cat8(ld_tr4(&sm.Ks[bp_][0][0], C::LDW, k0, 16 * td, lane),
-                                              ld_tr4(&sm.Ks[bp_][0][0], C::LDW, k0 + 4, 16 * td, lane));
+                        for (int kb = 0; kb < KB; ++kb) {
+                            const h8 A = *reinterpret_cast<const h8 *>(&sm.Ks[bp_][16 * ti + r16][32 * kb + 8 * g]);
+                            const h8 B = *reinterpret_cast<const h8 *>(&sm.Ks[bp_][16 * tj + r16][32 * kb + 8 * g]);
                             acc = mma(A, B, acc);
                         }
-                        h4 nw;   // -W[16 ti + 4g + i][d] at nWT[d][16 ti + 4g + i]
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) nw[i] = (_Float16)(-acc[i]);
-                        *reinterpret_cast<h4 *>(&sm.nWT[d][16 * ti + 4 * g]) = nw;
-                    }
-                }
-                // U = M diag(b dec) V^ for value-column tiles {pw, pw + 4, ...}
-                for (int tc = pw; tc < MT; tc += 4) {
-                    const int cc = 16 * tc + r16;
-                    h8 Bv[2];
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-                        Bv[kb] = cat8(ld_tr4(&sm.Vs[0][0], C::LDW, 32 * kb + 8 * g, 16 * tc, lane),
-                                      ld_tr4(&sm.Vs[0][0], C::LDW, 32 * kb + 8 * g + 4, 16 * tc, lane));
-                    f4 U[4];
-#pragma unroll
-                    for (int ti = 0; ti < 4; ++ti) {
-                        U[ti] = zero4();
-                        const int kbmax = (16 * ti + 15) / 32;
-                        for (int kb = 0; kb <= kbmax; ++kb) {
-                            const int k0 = 32 * kb + 8 * g;
-                            const h8 A = cat8(ld_tr4(&sm.M2T[0][0], C::LDT, k0, 16 * ti, lane),
-                                              ld_tr4(&sm.M2T[0][0], C::LDT, k0 + 4, 16 * ti, lane));
-                            U[ti] = mma(A, Bv[kb], U[ti]);
+                        for (int i = 0; i < 4; ++i) {
+                            const int rr = 16 * ti + 4 * g + i;
+                            sm.Gm[rr][16 * tj + r16] = sm.beta[rr] * acc[i];
                         }
                     }
-#pragma unroll
-                    for (int ti = 0; ti < 4; ++ti)
-                        *reinterpret_cast<float4 *>(&sm.UT[cc][16 * ti + 4 * g]) =
-                            make_float4(U[ti][0], U[ti][1], U[ti][2], U[ti][3]);
                 }
             }
+            lds_barrier();
+            // ===================== phases 3-4: W and U of chunk cp | E tile 1, update
+            // (I + L) [W | U] = [diag(b) K | diag(b dec) V^], L = diag(b) strictlower(K K^T),
+            // by block forward substitution over the four 16-row blocks:
+            //   X_i = M_ii (R_i - sum_{j<i} L_ij X_j),  M_ii = (I + L_ii)^-1
+            // Each wave owns the key-column tiles {pw, pw + 4, ...} of W and the same value-
+            // column tiles of U; rows 0-1 in phase 3, rows 2-3 in phase 4.  Products are
+            // 16 deep on the matrix cores: A fragments (rows of L_ij, M_ii) from LDS, B
+            // fragments from the accumulator tiles, k = 4g + e (upper half zero).
+            auto subst_row = [&](int i) {
+                const float4 bq = *reinterpret_cast<const float4 *>(&sm.beta[16 * i + 4 * g]);
+                const float4 dq = *reinterpret_cast<const float4 *>(&sm.bd[16 * i + 4 * g]);
+                f4 aw[NTW], au[NTW];
+#pragma unroll
+                for (int q = 0; q < NTW; ++q) {   // R_i in accumulator layout (rows 16i + 4g + e)
+                    const int x0 = 16 * (pw + 4 * q);
+                    const h4 kk = ld_tr4(&sm.Ks[bp_][0][0], C::LDW, 16 * i + 4 * g, x0, lane);
+                    const h4 vv = ld_tr4(&sm.Vs[0][0], C::LDW, 16 * i + 4 * g, x0, lane);
+                    aw[q] = f4{(float)kk[0] * bq.x, (float)kk[1] * bq.y, (float)kk[2] * bq.z, (float)kk[3] * bq.w};
+                    au[q] = f4{(float)vv[0] * dq.x, (float)vv[1] * dq.y, (float)vv[2] * dq.z, (float)vv[3] * dq.w};
+                }
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    if (j < i) {
+                        const float4 l = *reinterpret_cast<const float4 *>(&sm.Gm[16 * i + r16][16 * j + 4 * g]);
+                        const h8 A = {(_Float16)-l.x, (_Float16)-l.y, (_Float16)-l.z, (_Float16)-l.w,
+                                      (_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+#pragma unroll
+                        for (int q = 0; q < NTW; ++q) {
+                            aw[q] = mma(A, cat8(Xw[q][j], h4z), aw[q]);
+                            au[q] = mma(A, cat8(Xu[q][j], h4z), au[q]);
+                        }
+                    }
+                }
+                const float4 mi = *reinterpret_cast<const float4 *>(&sm.Mi[i][r16][4 * g]);
+                const h8 A = {(_Float16)mi.x, (_Float16)mi.y, (_Float16)mi.z, (_Float16)mi.w,
+                              (_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+#pragma unroll
+                for (int q = 0; q < NTW; ++q) {
+                    const h4 bw = {(_Float16)aw[q][0], (_Float16)aw[q][1], (_Float16)aw[q][2], (_Float16)aw[q][3]};
+                    const h4 bu = {(_Float16)au[q][0], (_Float16)au[q][1], (_Float16)au[q][2], (_Float16)au[q][3]};
+                    const f4 xw = mma(A, cat8(bw, h4z), zero4());
+                    const f4 xu = mma(A, cat8(bu, h4z), zero4());
+                    Xw[q][i] = h4{(_Float16)xw[0], (_Float16)xw[1], (_Float16)xw[2], (_Float16)xw[3]};
+                    Xu[q][i] = h4{(_Float16)xu[0], (_Float16)xu[1], (_Float16)xu[2], (_Float16)xu[3]};
+                    const int col = 16 * (pw + 4 * q) + r16;
+                    // -W[16i + 4g + e][col] at nWT[col][16i + 4g + e]; U likewise at UT
+                    *reinterpret_cast<h4 *>(&sm.nWT[col][16 * i + 4 * g]) = -Xw[q][i];
+                    *reinterpret_cast<float4 *>(&sm.UT[col][16 * i + 4 * g]) = make_float4(xu[0], xu[1], xu[2], xu[3]);
+                }
+            };
+            if (dop) { subst_row(0); subst_row(1); }
+            lds_barrier();
+            if (dop) { subst_row(2); subst_row(3); }
             lds_barrier();
         }
 
