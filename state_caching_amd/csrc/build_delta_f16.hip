@@ -71,8 +71,6 @@ __device__ __forceinline__ h4 ld_tr4(const _Float16 *S, int ld, int k0, int x0, 
 }
 __device__ __forceinline__ h8 cat8(h4 lo, h4 hi) { return h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}; }
 
-__constant__ int kOffTi[6] = {1, 2, 2, 3, 3, 3};
-__constant__ int kOffTj[6] = {0, 0, 1, 0, 1, 2};
 
 template <int D, typename TKV, typename TG>
 __global__ void __launch_bounds__((F16Cfg<D>::NT))
@@ -106,27 +104,26 @@ build_delta_f16_kernel(const DeltaArgs a)
         const TG *bp = reinterpret_cast<const TG *>(a.beta) + a.gtok0[s] * a.h_v + h;
         const TG *ap = reinterpret_cast<const TG *>(a.alpha) + a.gtok0[s] * a.h_v + h;
         typename Raw8<TKV>::type kraw[C::PASSES], vraw[C::PASSES];
-        float br = 0.f, ar = 1.f;
         double cl_lane = 0.0;
+        // Prefetches are straight-line loads of rows clamped into the segment (rows
+        // past its end are zeroed when staged), so the compiler's load waits stay
+        // exact and the next chunk's rows remain in flight across the phases.
+        TG braw, araw;   // gates of the next chunk (every prep wave loads them)
         auto fetch_k = [&](int c) {
 #pragma unroll
             for (int p = 0; p < C::PASSES; ++p) {
-                const int t = 64 * c + prow + RPP * p;
-                if (t < len) ld_raw8(kp + (int64_t)t * a.ldk + pcol, kraw[p]);
-                else zero_raw8(kraw[p]);
+                const int t = min(64 * c + prow + RPP * p, len - 1);
+                ld_raw8(kp + (int64_t)t * a.ldk + pcol, kraw[p]);
             }
-            if (pw == 0) {
-                const int t = 64 * c + lane;
-                if (t < len) { br = ld1(bp + (int64_t)t * a.h_v); ar = ld1(ap + (int64_t)t * a.h_v); }
-                else { br = 0.f; ar = 1.f; }
-            }
+            const int t = min(64 * c + lane, len - 1);
+            braw = bp[(int64_t)t * a.h_v];
+            araw = ap[(int64_t)t * a.h_v];
         };
         auto fetch_v = [&](int c) {
 #pragma unroll
             for (int p = 0; p < C::PASSES; ++p) {
-                const int t = 64 * c + prow + RPP * p;
-                if (t < len) ld_raw8(vp + (int64_t)t * a.ldv + pcol, vraw[p]);
-                else zero_raw8(vraw[p]);
+                const int t = min(64 * c + prow + RPP * p, len - 1);
+                ld_raw8(vp + (int64_t)t * a.ldv + pcol, vraw[p]);
             }
         };
         if (nch > 0) { fetch_k(0); fetch_v(0); }
@@ -135,9 +132,12 @@ build_delta_f16_kernel(const DeltaArgs a)
         h4 Xw[NTW][4], Xu[NTW][4];    // solved row blocks, fp16 B fragments
 
 
-        for (int it = 0; it <= nch; ++it) {
+        // chunks 0 .. nch-1, every iteration the same straight-line load stream (the
+        // last one refetches its own rows); then one idle round of barriers while the
+        // state waves finish the last chunk
+        for (int it = 0; it < nch; ++it) {
             const int cp = it;
-            const bool dop = cp < nch;
+            constexpr bool dop = true;
             const int bp_ = cp & 1;
             // ===================== phase 1: stage keys and gates of cp | E tile 0
             if (dop) {
@@ -148,6 +148,9 @@ build_delta_f16_kernel(const DeltaArgs a)
                     widen8(kraw[p], kx);
                     widen8(vraw[p], vx);
                     const int t = prow + RPP * p;
+                    const bool in = 64 * cp + t < len;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) { kx[e] = in ? kx[e] : 0.f; vx[e] = in ? vx[e] : 0.f; }
                     h8 kk;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
@@ -159,6 +162,8 @@ build_delta_f16_kernel(const DeltaArgs a)
                 vm = wave_max(vm);
                 if (lane == 0) sm.wmax[pw] = vm;
                 if (pw == 0) {
+                    const bool gin = 64 * cp + lane < len;
+                    const float br = gin ? to_f32(braw) : 0.f, ar = gin ? to_f32(araw) : 1.f;
                     const float l2 = log2f(ar);
                     const float sfx = wave_suffix_excl(l2);
                     cl_lane += (double)l2;
@@ -166,12 +171,12 @@ build_delta_f16_kernel(const DeltaArgs a)
                     sm.bd[lane] = br * exp2f(sfx);
                     if (lane == 0) sm.gb[bp_] = exp2f(sfx + l2);
                 }
-                if (cp + 1 < nch) fetch_k(cp + 1);
+                fetch_k(min(cp + 1, nch - 1));
             }
             lds_barrier();
             // ===================== phase 2: V^, Gram, diagonal inverses | update tile 0
             if (dop) {
-                // value scale of chunk cp; V^ = V * 2^-sv into VT
+                // value scale of chunk cp; V^ = V * 2^-sv into Vs
                 {
                     const float vm = fmaxf(fmaxf(sm.wmax[0], sm.wmax[1]), fmaxf(sm.wmax[2], sm.wmax[3]));
                     const int sv = pow2_exponent(vm);
@@ -182,12 +187,13 @@ build_delta_f16_kernel(const DeltaArgs a)
                         float vx[8];
                         widen8(vraw[p], vx);
                         const int t = prow + RPP * p;
+                        const bool in = 64 * cp + t < len;   // rows past the end were clamped
                         h8 vv;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) vv[e] = (_Float16)(vx[e] * vsc);
+                        for (int e = 0; e < 8; ++e) vv[e] = (_Float16)(in ? vx[e] * vsc : 0.f);
                         *reinterpret_cast<h8 *>(&sm.Vs[t][pcol]) = vv;
                     }
-                    if (cp + 1 < nch) fetch_v(cp + 1);
+                    fetch_v(min(cp + 1, nch - 1));
                 }
                 if (pw == 0) {
                     // the four diagonal Gram tiles, then the inverses of I + A'_bb for all
@@ -245,7 +251,8 @@ build_delta_f16_kernel(const DeltaArgs a)
 #pragma unroll
                     for (int u = 0; u < 2; ++u) {
                         const int q = 2 * (pw - 1) + u;
-                        const int ti = kOffTi[q], tj = kOffTj[q];
+                        // q = 0..5 -> (ti, tj) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+                        const int ti = q < 1 ? 1 : (q < 3 ? 2 : 3), tj = q - ti * (ti - 1) / 2;
                         f4 acc = zero4();
 #pragma unroll
                         for (int kb = 0; kb < KB; ++kb) {
@@ -317,6 +324,8 @@ build_delta_f16_kernel(const DeltaArgs a)
             if (dop) { subst_row(2); subst_row(3); }
             lds_barrier();
         }
+#pragma unroll
+        for (int ph = 0; ph < 4; ++ph) lds_barrier();
 
         if (pw == 0) {
             const double tot = wave_sum_f64(cl_lane);
