@@ -111,15 +111,27 @@ __device__ __forceinline__ void split_bf16(float x, __bf16 &hi, __bf16 &lo) {
 }
 
 // ---- wave64 reductions and scans -------------------------------------------
+// Within each 16-lane row by DPP lane moves (plain VALU operations), across the
+// four rows through lane reads into scalar registers.
+//   DPP controls: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E, row_half_mirror
+//   0x141, row_mirror 0x140, row_shl:n 0x100+n and row_shr:n 0x110+n (zero fill).
+#define HY_DPP(x, ctrl) __builtin_amdgcn_update_dpp(0.f, (x), (ctrl), 0xf, 0xf, true)
+__device__ __forceinline__ float lane_f(float x, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-    return x;
+    x = fmaxf(x, HY_DPP(x, 0xB1));
+    x = fmaxf(x, HY_DPP(x, 0x4E));
+    x = fmaxf(x, HY_DPP(x, 0x141));
+    x = fmaxf(x, HY_DPP(x, 0x140));
+    return fmaxf(fmaxf(lane_f(x, 0), lane_f(x, 16)), fmaxf(lane_f(x, 32), lane_f(x, 48)));
 }
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
+    x += HY_DPP(x, 0xB1);
+    x += HY_DPP(x, 0x4E);
+    x += HY_DPP(x, 0x141);
+    x += HY_DPP(x, 0x140);
+    return (lane_f(x, 0) + lane_f(x, 16)) + (lane_f(x, 32) + lane_f(x, 48));
 }
 __device__ __forceinline__ double wave_sum_f64(double x) {
 #pragma unroll
@@ -128,24 +140,27 @@ __device__ __forceinline__ double wave_sum_f64(double x) {
 }
 // exclusive suffix sum over the 64 lanes: returns sum_{j > lane} x_j
 __device__ __forceinline__ float wave_suffix_excl(float x) {
-    const int l = threadIdx.x & 63;
-    float s = x;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        float y = __shfl_down(s, o, 64);
-        if (l + o < 64) s += y;
-    }
-    return s - x;
+    float s = x;   // inclusive suffix within the row: lane i <- sum of lanes i..15
+    s += HY_DPP(s, 0x101);
+    s += HY_DPP(s, 0x102);
+    s += HY_DPP(s, 0x104);
+    s += HY_DPP(s, 0x108);
+    const float t1 = lane_f(s, 16), t2 = lane_f(s, 32), t3 = lane_f(s, 48);   // row totals
+    const int row = (threadIdx.x & 63) >> 4;
+    const float later = (row < 1 ? t1 : 0.f) + (row < 2 ? t2 : 0.f) + (row < 3 ? t3 : 0.f);
+    return (s + later) - x;
 }
 // inclusive prefix sum over the 64 lanes
 __device__ __forceinline__ float wave_prefix_incl(float x) {
-    const int l = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        float y = __shfl_up(x, o, 64);
-        if (l >= o) x += y;
-    }
-    return x;
+    float s = x;   // inclusive prefix within the row: lane i <- sum of lanes 0..i
+    s += HY_DPP(s, 0x111);
+    s += HY_DPP(s, 0x112);
+    s += HY_DPP(s, 0x114);
+    s += HY_DPP(s, 0x118);
+    const float t0 = lane_f(s, 15), t1 = lane_f(s, 31), t2 = lane_f(s, 47);   // row totals
+    const int row = (threadIdx.x & 63) >> 4;
+    const float earlier = (row > 0 ? t0 : 0.f) + (row > 1 ? t1 : 0.f) + (row > 2 ? t2 : 0.f);
+    return s + earlier;
 }
 
 // Power-of-two exponent that brings m (>= 0) into [0.5, 1); 0 for m == 0 or non-finite.
