@@ -209,10 +209,12 @@ build_delta_f16_kernel(const DeltaArgs a)
                             const h8 A = *reinterpret_cast<const h8 *>(&sm.Ks[bp_][o + r16][32 * kb + 8 * g]);
                             acc = mma(A, A, acc);
                         }
+                        const float4 bq = *reinterpret_cast<const float4 *>(&sm.beta[o + 4 * g]);
+                        const float bqv[4] = {bq.x, bq.y, bq.z, bq.w};
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const int rr = 4 * g + i;   // A'[rr][r16] for r16 < rr, stored at [r16][rr]
-                            if (r16 < rr) sm.Gm[o + r16][o + rr] = sm.beta[o + rr] * acc[i];
+                            if (r16 < rr) sm.Gm[o + r16][o + rr] = bqv[i] * acc[i];
                         }
                     }
                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -221,26 +223,28 @@ build_delta_f16_kernel(const DeltaArgs a)
                         float x[16];
 #pragma unroll
                         for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
-                        float4 nxt[4], cur[4];
+                        // column q of A' (its entries r > q) rides a ring of four rows, loaded
+                        // four steps ahead; only the float4 pieces holding some r > q
+                        float4 ring[4][4];
+                        auto load_col = [&](int q, float4 (&dst)[4]) {
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) nxt[v] = *reinterpret_cast<const float4 *>(&sm.Gm[o][o + 4 * v]);
+                            for (int v = 0; v < 4; ++v)
+                                if (4 * v + 3 > q) dst[v] = *reinterpret_cast<const float4 *>(&sm.Gm[o + q][o + 4 * v]);
+                        };
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) load_col(q, ring[q]);
 #pragma unroll
                         for (int q = 0; q < 15; ++q) {
+                            const float4 *cur = ring[q % 4];
+                            float colv[16];
 #pragma unroll
-                            for (int v = 0; v < 4; ++v) cur[v] = nxt[v];
-                            asm volatile("" ::: "memory");
-                            if (q + 1 < 15) {
-#pragma unroll
-                                for (int v = 0; v < 4; ++v)
-                                    nxt[v] = *reinterpret_cast<const float4 *>(&sm.Gm[o + q + 1][o + 4 * v]);
+                            for (int v = 0; v < 4; ++v) {
+                                colv[4 * v] = cur[v].x; colv[4 * v + 1] = cur[v].y;
+                                colv[4 * v + 2] = cur[v].z; colv[4 * v + 3] = cur[v].w;
                             }
-                            asm volatile("" ::: "memory");
-                            const float colv[16] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w,
-                                                    cur[1].x, cur[1].y, cur[1].z, cur[1].w,
-                                                    cur[2].x, cur[2].y, cur[2].z, cur[2].w,
-                                                    cur[3].x, cur[3].y, cur[3].z, cur[3].w};
 #pragma unroll
                             for (int r = q + 1; r < 16; ++r) x[r] -= colv[r] * x[q];
+                            if (q + 4 < 15) load_col(q + 4, ring[q % 4]);
                         }
                         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
