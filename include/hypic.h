@@ -185,7 +185,8 @@ hypic_status hypic_seam_advance(const hypic_seam_desc *d, float *S_inout, void *
  * Workspace: hypic_workspace_size(desc, HYPIC_WS_COMPOSE) bytes.  It is 0
  * except for a dense split-precision compose with d_k in {64, 128}, seams and
  * n >= 2: the operators of all n-1 windows are computed first and staged
- * there, (3 w d_k + 4) floats per (window, value head), 16-byte aligned.
+ * there, (3 wp d_k + 4) floats per (window, value head) with wp = w rounded
+ * up to a multiple of 4, 16-byte aligned.
  * Errors: HYPIC_E_INVALID, HYPIC_E_UNSUPPORTED, HYPIC_E_WORKSPACE, HYPIC_E_HIP.
  */
 typedef struct {

@@ -11,13 +11,13 @@
 // serial chain advances.
 //
 // Seam of an inner segment (window operators precomputed per (window, head)
-// by seam_ops_kernel: W = M diag(b) K, K^T, U^T, gw):
-//   S' = gw S + K^T (U - gw W S)
-// Each wave forms its part of P = W S from its own rows, W[:, rows] S[rows, :],
-// at the end of the previous step and leaves it in LDS; after a barrier every
-// lane sums the parts into its slice of E = U - gw P and updates its own rows
-// to S'.  After a second barrier (S' complete, split into bf16 hi/lo in LDS)
-// every wave forms its rows of T S' + S0.
+// by seam_ops_kernel: W = M diag(b) K, K, U^T, gw).  The window maps the state
+// to S' = gw S + K^T E with E = U - gw W S, so the step is
+//   S_new = T S' + S0 = gw (T S) + (T K^T) E + S0,
+// one barrier per step: T S and W S both read the state S of this step (W S
+// as per-wave parts formed from each wave's own rows at the end of the
+// previous step), and T K^T needs only the segment's T and the window's keys,
+// so it is formed beside T S from the same T fragments.
 #include "common.h"
 #include "launch.h"
 #include "seam.h"
@@ -29,9 +29,9 @@ struct CsCfg {
     static constexpr int NW = D / 16;    // waves, 16 state rows each
     static constexpr int NT = 64 * NW;
     static constexpr int KB = D / 32;    // 32-deep k blocks of the T S product
-    // register ring depth (segments in flight; window records use the same
-    // depth): three, or two for the seam variant at d = 128, whose window
-    // records and 16-row T slices would not fit three deep in 256 registers
+    // register ring depth: segments (and window records) in flight; two for
+    // the seam variant at d = 128, whose 16-row T slices and window pieces would
+    // not fit three deep in 256 registers
     static constexpr int NST = (SEAMS && D == 128) ? 2 : 3;
     static constexpr int LDB = D + 8;    // split-state row stride (bf16)
 };
@@ -39,35 +39,60 @@ struct CsCfg {
 template <int D, bool SEAMS>
 struct CsSmem {
     using C = CsCfg<D, SEAMS>;
-    // no seams: S double-buffered; seams: buffer 0 holds S' of the current step
-    uint16_t SH[SEAMS ? 1 : 2][16][C::LDB];   // state hi, [column][row]
-    uint16_t SL[SEAMS ? 1 : 2][16][C::LDB];   // state lo
-    f4 Ppart[SEAMS ? C::NW : 1][64];          // per-wave part of W S, accumulator layout
+    // double-buffered by step parity: step j reads buffer j & 1 and writes the other
+    uint16_t SH[2][16][C::LDB];                   // state hi, [column][row]
+    uint16_t SL[2][16][C::LDB];                   // state lo
+    f4 Ppart[SEAMS ? 2 : 1][SEAMS ? C::NW : 1][64];   // per-wave parts of W S, accumulator layout
+    uint16_t KH[SEAMS ? 2 : 1][16][C::LDB];       // window keys hi, [token][dim], rows >= w zero
+    uint16_t KL[SEAMS ? 2 : 1][16][C::LDB];       // window keys lo
 };
+
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef float f2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 __device__ __forceinline__ float bf16_val(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// fp32 pair -> bf16 hi pair (rounded to nearest) and lo pair bf16(x - hi)
+// (x - hi is exact), one conversion per pair
+__device__ __forceinline__ void split2(float x0, float x1, bf2 &h, bf2 &l) {
+    h = __builtin_convertvector(f2v{x0, x1}, bf2);
+    const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+    l = __builtin_convertvector(f2v{x0 - __uint_as_float(hb << 16), x1 - __uint_as_float(hb & 0xffff0000u)}, bf2);
+}
 // fp32 x8 -> bf16 hi/lo fragments
 __device__ __forceinline__ void split8(const float (&x)[8], b8 &hi, b8 &lo) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const __bf16 hb = (__bf16)x[e];
-        hi[e] = hb;
-        lo[e] = (__bf16)(x[e] - (float)hb);
+    for (int e = 0; e < 8; e += 2) {
+        bf2 h, l;
+        split2(x[e], x[e + 1], h, l);
+        hi[e] = h[0]; hi[e + 1] = h[1];
+        lo[e] = l[0]; lo[e + 1] = l[1];
     }
 }
 // fp32 x4 into elements 0..3 of hi/lo fragments, elements 4..7 zero: the
 // k-permuted operand k = 4g + e (e < 4) of a 16-deep product on 16x16x32
 __device__ __forceinline__ void split4z(const float (&x)[4], b8 &hi, b8 &lo) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const __bf16 hb = (__bf16)x[e];
-        hi[e] = hb;
-        lo[e] = (__bf16)(x[e] - (float)hb);
-        hi[4 + e] = (__bf16)0.f;
-        lo[4 + e] = (__bf16)0.f;
+    for (int e = 0; e < 4; e += 2) {
+        bf2 h, l;
+        split2(x[e], x[e + 1], h, l);
+        hi[e] = h[0]; hi[e + 1] = h[1];
+        lo[e] = l[0]; lo[e + 1] = l[1];
     }
+#pragma unroll
+    for (int e = 4; e < 8; ++e) {
+        hi[e] = (__bf16)0.f;
+        lo[e] = (__bf16)0.f;
+    }
+}
+// fp32 x4 -> packed bf16 hi and lo (two 32-bit words each)
+__device__ __forceinline__ void split4p(float x0, float x1, float x2, float x3, uint2 &hi, uint2 &lo) {
+    bf2 h0, l0, h1, l1;
+    split2(x0, x1, h0, l0);
+    split2(x2, x3, h1, l1);
+    hi = make_uint2(__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1));
+    lo = make_uint2(__builtin_bit_cast(uint32_t, l0), __builtin_bit_cast(uint32_t, l1));
 }
 __device__ __forceinline__ f4 mma3(const b8 &ah, const b8 &al, const b8 &bh, const b8 &bl, f4 c) {
     c = mma(al, bh, c);
@@ -98,31 +123,35 @@ __global__ void __launch_bounds__((CsCfg<D, SEAMS>::NT)) compose_split_kernel(co
     for (int i = 0; i < 4; ++i)
         Sown[i] = a.S_in ? a.S_in[hoff + (int64_t)(row0 + 4 * g + i) * D + c0 + r16] : 0.f;
     auto put_state = [&](int buf, const f4 &x) {   // own rows, split, into the LDS block
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint16_t hb = bf16_bits(x[i]);
-            sm.SH[buf][r16][row0 + 4 * g + i] = hb;
-            sm.SL[buf][r16][row0 + 4 * g + i] = bf16_bits(x[i] - bf16_val(hb));
-        }
+        uint2 hi, lo;
+        split4p(x[0], x[1], x[2], x[3], hi, lo);
+        *reinterpret_cast<uint2 *>(&sm.SH[buf][r16][row0 + 4 * g]) = hi;
+        *reinterpret_cast<uint2 *>(&sm.SL[buf][r16][row0 + 4 * g]) = lo;
     };
 
     // ---- register ring of T rows and S0 rows ---------------------------------
     // lane (g, r16): T[row0 + r16][32 kb + 8 g .. + 7] for every kb, S0 as Sown
     float Tb[NST][D / 4];
     f4 S0b[NST];
-    auto fetch = [&](int j, float (&T)[D / 4], f4 &S0) {
-        const int slot = a.order[j];
-        const float *Tp = a.T_pool + (int64_t)slot * a.h_v * D * D + hoff;
-        const float *Sp = a.S0_pool + (int64_t)slot * a.h_v * D * D + hoff;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const float4 *p = reinterpret_cast<const float4 *>(Tp + (int64_t)(row0 + r16) * D + 32 * kb + 8 * g);
-            const float4 x0 = p[0], x1 = p[1];
-            T[8 * kb + 0] = x0.x; T[8 * kb + 1] = x0.y; T[8 * kb + 2] = x0.z; T[8 * kb + 3] = x0.w;
-            T[8 * kb + 4] = x1.x; T[8 * kb + 5] = x1.y; T[8 * kb + 6] = x1.z; T[8 * kb + 7] = x1.w;
-        }
+    auto t_rows = [&](int j) {   // this lane's row of T for segment position j
+        return a.T_pool + (int64_t)a.order[j] * a.h_v * D * D + hoff + (int64_t)(row0 + r16) * D + 8 * g;
+    };
+    auto fetch_t = [&](const float *Tp, int kb, float (&T)[D / 4]) {
+        const float4 *p = reinterpret_cast<const float4 *>(Tp + 32 * kb);
+        const float4 x0 = p[0], x1 = p[1];
+        T[8 * kb + 0] = x0.x; T[8 * kb + 1] = x0.y; T[8 * kb + 2] = x0.z; T[8 * kb + 3] = x0.w;
+        T[8 * kb + 4] = x1.x; T[8 * kb + 5] = x1.y; T[8 * kb + 6] = x1.z; T[8 * kb + 7] = x1.w;
+    };
+    auto fetch_s0 = [&](int j, f4 &S0) {
+        const float *Sp = a.S0_pool + (int64_t)a.order[j] * a.h_v * D * D + hoff;
 #pragma unroll
         for (int i = 0; i < 4; ++i) S0[i] = Sp[(int64_t)(row0 + 4 * g + i) * D + c0 + r16];
+    };
+    auto fetch = [&](int j, float (&T)[D / 4], f4 &S0) {
+        const float *Tp = t_rows(j);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) fetch_t(Tp, kb, T);
+        fetch_s0(j, S0);
     };
     // S_new = S0 + T S for this wave's rows, S split in LDS buffer `buf`
     auto product = [&](const float (&T)[D / 4], const f4 &S0, int buf) {
@@ -168,48 +197,47 @@ __global__ void __launch_bounds__((CsCfg<D, SEAMS>::NT)) compose_split_kernel(co
         for (int s = 0; s < NST - 1; ++s)
             if (j0 + s < n) step(j0 + s, s);
     } else {
-        // window operators of the step with prompt position pos, this lane's slices:
-        //   Wv: W[t = r16][row0 + 4g .. +3]      (A operand of the part of W S)
-        //   Kv: K^T[row0 + r16][4g .. +3]        (A operand of K^T E)
-        //   Uv: U^T[c0 + r16][4g .. +3]          (E layout: U[4g + i][c0 + r16])
+        // window operators of the step with prompt position pos (pos >= 1; step
+        // position 0 has no window and runs with W = K = U = 0, gw = 1), this
+        // lane's slices, one ring slot per step in flight:
+        //   Wv: W[t = r16][row0 + 4g .. +3]   (A operand of this wave's part of W S)
+        //   Uv: U^T[c0 + r16][4g .. +3]       (E layout: U[4g + i][c0 + r16])
+        //   Kg: K[kt][kd .. kd + 3]           (this thread's piece of the keys, staged in LDS)
         const int w = a.seam.w, wp = winop_wp(w);
         const int win_hi = a.first_pos + n - 2;   // last window record of this launch
-        float4 Wv[NST], Kv[NST], Uv[NST];
+        constexpr int KPR = D / 4;                // key float4 pieces per token row
+        const int kt = tid / KPR, kd = 4 * (tid % KPR);
+        float4 Wv[NST], Uv[NST], Kg[NST];
         float gw[NST];
-        const bool wrow = r16 < w, wtok = 4 * g < wp;
+        bool hw[NST];
+        const bool wrow = r16 < w, wtok = 4 * g < wp, ktok = kt < w;
         auto fetch_win = [&](int pos, int st) {
             const int wi = min(max(pos - 1, 0), win_hi);   // clamped: always in range
             const float *o = ops + ((int64_t)wi * a.h_v + h) * winop_floats<D>(w);
             Wv[st] = *reinterpret_cast<const float4 *>(o + (int64_t)(wrow ? r16 : 0) * D + row0 + 4 * g);
-            Kv[st] = *reinterpret_cast<const float4 *>(o + (int64_t)wp * D + (int64_t)(row0 + r16) * wp + (wtok ? 4 * g : 0));
+            Kg[st] = *reinterpret_cast<const float4 *>(o + (int64_t)wp * D + (int64_t)(ktok ? kt : 0) * D + kd);
             Uv[st] = *reinterpret_cast<const float4 *>(o + (int64_t)2 * wp * D + (int64_t)(c0 + r16) * wp + (wtok ? 4 * g : 0));
             gw[st] = o[(int64_t)3 * wp * D];
+            hw[st] = pos >= 1;
         };
-        // this wave's part of P = W S from its own rows (masked beyond the window)
-        auto part_p = [&](int st) {
-            const float wx[4] = {wrow ? Wv[st].x : 0.f, wrow ? Wv[st].y : 0.f,
-                                 wrow ? Wv[st].z : 0.f, wrow ? Wv[st].w : 0.f};
+        // this wave's part of W S from its own rows (masked beyond the window)
+        auto part_p = [&](int st, int buf) {
+            const bool m = wrow && hw[st];
+            const float wx[4] = {m ? Wv[st].x : 0.f, m ? Wv[st].y : 0.f, m ? Wv[st].z : 0.f, m ? Wv[st].w : 0.f};
             const float sx[4] = {Sown[0], Sown[1], Sown[2], Sown[3]};
             b8 ah, al, bh, bl;
             split4z(wx, ah, al);
             split4z(sx, bh, bl);
-            sm.Ppart[wv][lane] = mma3(ah, al, bh, bl, zero4());
+            sm.Ppart[buf][wv][lane] = mma3(ah, al, bh, bl, zero4());
         };
-        // S' = gw S + K^T (U - gw sum of parts) for this wave's rows; split into LDS
-        auto seam_update = [&](int st) {
-            f4 p = zero4();
-#pragma unroll
-            for (int q = 0; q < C::NW; ++q) p += sm.Ppart[q][lane];
-            const float gwv = gw[st];
-            const float ex[4] = {wtok ? Uv[st].x - gwv * p[0] : 0.f, wtok ? Uv[st].y - gwv * p[1] : 0.f,
-                                 wtok ? Uv[st].z - gwv * p[2] : 0.f, wtok ? Uv[st].w - gwv * p[3] : 0.f};
-            const float kx[4] = {wtok ? Kv[st].x : 0.f, wtok ? Kv[st].y : 0.f,
-                                 wtok ? Kv[st].z : 0.f, wtok ? Kv[st].w : 0.f};
-            b8 ah, al, bh, bl;
-            split4z(kx, ah, al);
-            split4z(ex, bh, bl);
-            Sown = mma3(ah, al, bh, bl, Sown * gwv);
-            put_state(0, Sown);
+        // the window's keys, split, into LDS buffer buf (rows >= w zero)
+        auto stage_k = [&](int st, int buf) {
+            const bool m = ktok && hw[st];
+            const float kx[4] = {m ? Kg[st].x : 0.f, m ? Kg[st].y : 0.f, m ? Kg[st].z : 0.f, m ? Kg[st].w : 0.f};
+            uint2 hi, lo;
+            split4p(kx[0], kx[1], kx[2], kx[3], hi, lo);
+            *reinterpret_cast<uint2 *>(&sm.KH[buf][kt][kd]) = hi;
+            *reinterpret_cast<uint2 *>(&sm.KL[buf][kt][kd]) = lo;
         };
 
         // Load order: loads retire in issue order, so a wait for one load also waits
@@ -220,22 +248,56 @@ __global__ void __launch_bounds__((CsCfg<D, SEAMS>::NT)) compose_split_kernel(co
 #pragma unroll
         for (int s = 0; s < NST; ++s) fetch_win(a.first_pos + s, s);
 #pragma unroll
-        for (int s = 0; s < NST; ++s)
-            if (s < n) fetch(s, Tb[s], S0b[s]);
-        if (a.first_pos == 0) put_state(0, Sown);   // step 0 has no window
-        else part_p(0);
+        for (int s = 0; s < NST; ++s) fetch(min(s, n - 1), Tb[s], S0b[s]);
+        put_state(0, Sown);
+        part_p(0, 0);
+        stage_k(0, 0);
+        int cur = 0;
 
+        // step j: S, parts of W S and the keys of this step complete in buffer cur
         auto step = [&](const int j, const int s) __attribute__((always_inline)) {
             const int pos = a.first_pos + j;
-            lds_barrier();   // parts of W S (or the initial state) complete
-            if (pos >= 1) {
-                seam_update(s);
-                lds_barrier();   // S' complete
+            lds_barrier();
+            // T S and P^T = K T^T (rows of T K^T as the lanes' columns) from the
+            // same T fragments
+            f4 ts = zero4(), ts1 = zero4(), pt = zero4(), pt1 = zero4();
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int k0 = 32 * kb + 8 * g;
+                float tx[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) tx[e] = Tb[s][8 * kb + e];
+                b8 ah, al;
+                split8(tx, ah, al);
+                const b8 bh = ld_b8(&sm.SH[cur][r16][k0]), bl = ld_b8(&sm.SL[cur][r16][k0]);
+                const b8 kh = ld_b8(&sm.KH[cur][r16][k0]), kl = ld_b8(&sm.KL[cur][r16][k0]);
+                ts = mma(ah, bh, ts);
+                ts1 = mma(al, bh, ts1);
+                ts1 = mma(ah, bl, ts1);
+                pt = mma(kh, ah, pt);
+                pt1 = mma(kl, ah, pt1);
+                pt1 = mma(kh, al, pt1);
             }
-            const f4 acc = product(Tb[s], S0b[s], 0);
+            // E = U - gw W S (token 4g + i, column r16)
+            f4 ps = zero4();
+#pragma unroll
+            for (int q = 0; q < C::NW; ++q) ps += sm.Ppart[cur][q][lane];
+            const bool mu = wtok && hw[s];
+            const float gwv = hw[s] ? gw[s] : 1.f;
+            const float ex[4] = {mu ? Uv[s].x - gwv * ps[0] : 0.f, mu ? Uv[s].y - gwv * ps[1] : 0.f,
+                                 mu ? Uv[s].z - gwv * ps[2] : 0.f, mu ? Uv[s].w - gwv * ps[3] : 0.f};
+            const f4 p = pt + pt1;
+            const float px[4] = {p[0], p[1], p[2], p[3]};
+            b8 ah, al, bh, bl;
+            split4z(px, ah, al);   // (T K^T)[row0 + r16][t = 4g + e]
+            split4z(ex, bh, bl);   // E[t = 4g + e][c0 + r16]
+            const f4 acc = mma3(ah, al, bh, bl, S0b[s]) + gwv * (ts + ts1);
             Sown = acc;
-            // window of step j + 1: this wave's part of W S
-            part_p((s + 1) % NST);
+            put_state(cur ^ 1, acc);
+            // the next step's parts of W S and its keys
+            part_p((s + 1) % NST, cur ^ 1);
+            stage_k((s + 1) % NST, cur ^ 1);
+            cur ^= 1;
             // refills, straight-line and in range (clamped): window of step j + NST
             // into the slot step j used, then segment j + NST into this ring stage
             fetch_win(pos + NST, s);

@@ -209,7 +209,7 @@ __device__ void seam_apply(WinSmem<D, WMAX, 16> &ws, float *ST, int ldst, const 
 // Workspace record of one (window, head): the window's operators, fp32, with
 // the token count padded to wp = w rounded up to 4 (padding rows are zero):
 //   W  [wp][D]  M diag(b) K                       (token-major)
-//   KT [D][wp]  keys after conv and normalisation (dimension-major)
+//   K  [wp][D]  keys after conv and normalisation (token-major)
 //   UT [D][wp]  (M diag(b dec) V)^T               (value column-major)
 //   gw          gate product over the window
 __host__ __device__ __forceinline__ int winop_wp(int w) { return (w + 3) & ~3; }
@@ -355,7 +355,7 @@ __global__ void __launch_bounds__(64) seam_ops_kernel(const SeamArgs a, float *o
         }
     }
     __syncthreads();
-    float *oW = o, *oKT = o + (int64_t)wp * D, *oUT = o + (int64_t)2 * wp * D;
+    float *oW = o, *oK = o + (int64_t)wp * D, *oUT = o + (int64_t)2 * wp * D;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         const int d = lane + 64 * c;
@@ -374,13 +374,14 @@ __global__ void __launch_bounds__(64) seam_ops_kernel(const SeamArgs a, float *o
         }
 #pragma unroll
         for (int t = 0; t < WM; ++t)
-            if (t < wp) oW[(int64_t)t * D + d] = Wd[t];
+            if (t < wp) {
+                oW[(int64_t)t * D + d] = Wd[t];
+                oK[(int64_t)t * D + d] = K[t][c];
+            }
 #pragma unroll
         for (int t4 = 0; t4 < WM; t4 += 4)
-            if (t4 < wp) {
-                *reinterpret_cast<float4 *>(oKT + (int64_t)d * wp + t4) = make_float4(K[t4][c], K[t4 + 1][c], K[t4 + 2][c], K[t4 + 3][c]);
+            if (t4 < wp)
                 *reinterpret_cast<float4 *>(oUT + (int64_t)d * wp + t4) = make_float4(Ud[t4], Ud[t4 + 1], Ud[t4 + 2], Ud[t4 + 3]);
-            }
     }
 }
 

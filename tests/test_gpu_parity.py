@@ -262,6 +262,45 @@ def test_cfg4_like_small_pipeline(dtype):
     assert e1 <= TOL[dtype] and e2 <= TOL[dtype]
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_split_compose_with_seams(d):
+    """The split-precision compose with fused seam windows (d in {64, 128}) on
+    non-degenerate gates: against the oracle's composition of the same GPU-built
+    pairs (isolates the compose and window arithmetic), and against full
+    recompute of the prompt."""
+    need_gpu()
+    wl = synth.gdn(95 + d, [70, 64, 100, 65, 90, 33, 80], 1, 2, d, torch.bfloat16,
+                   alpha_div=64.0, conv_w=4, seam_w=8)
+    dw, T, S0 = _check_build(wl)
+    S_init = synth.random_state(96 + d, 2, d, d)
+    case(f"split compose with seams d={d}")
+    S = dw.compose(T, S0, S_init=S_init.cuda())
+    torch.cuda.synchronize()
+    S_or = oracle.compose(np64(T), np64(S0), S_init=np64(S_init), wl=wl, seams=True)
+    full = oracle.full_recompute(wl, S_init=np64(S_init))
+    e1, e2 = oracle.relF(np64(S), S_or), oracle.relF(np64(S), full)
+    print(f"  relF vs oracle compose of the same pairs {e1:.3e}, vs full recompute {e2:.3e}")
+    assert e1 <= 2e-5 and e2 <= TOL[torch.bfloat16]
+
+
+def test_split_compose_seams_across_launches():
+    """More segments than one compose launch holds, with seams: windows are
+    indexed by prompt position across launches."""
+    need_gpu()
+    wl = synth.gdn(97, [12] * 150, 1, 1, 64, torch.bfloat16, alpha_div=16.0, conv_w=4,
+                   seam_w=8)
+    sca, DW = _lib()
+    dw = DW(wl)
+    T, S0 = dw.build()
+    case("split compose with seams, 150 segments")
+    S = dw.compose(T, S0)
+    torch.cuda.synchronize()
+    S_or = oracle.compose(np64(T), np64(S0), wl=wl, seams=True)
+    e = oracle.relF(np64(S), S_or)
+    print(f"  relF vs oracle compose of the same pairs {e:.3e}")
+    assert e <= 2e-5
+
+
 def test_cfg4_sampled():
     need_gpu()
     wl = synth.config(4)
