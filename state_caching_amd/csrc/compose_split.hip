@@ -29,10 +29,13 @@ struct CsCfg {
     static constexpr int NW = D / 16;    // waves, 16 state rows each
     static constexpr int NT = 64 * NW;
     static constexpr int KB = D / 32;    // 32-deep k blocks of the T S product
-    // register ring depth: segments (and window records) in flight; two for
-    // the seam variant at d = 128, whose 16-row T slices and window pieces would
-    // not fit three deep in 256 registers
+    // register ring depths: S0 rows and window records NST steps ahead (the
+    // unroll factor of the step loop); raw T rows NTQ steps ahead of their
+    // staging, which is itself one step ahead of their use.  The seam variant at
+    // d = 128 keeps NST = 2, NTQ = 1 to stay within 256 registers (deeper T
+    // rings measured no faster there)
     static constexpr int NST = (SEAMS && D == 128) ? 2 : 3;
+    static constexpr int NTQ = (SEAMS && D == 128) ? 1 : NST;
     static constexpr int LDB = D + 8;    // split-state row stride (bf16)
 };
 
@@ -45,6 +48,8 @@ struct CsSmem {
     f4 Ppart[SEAMS ? 2 : 1][SEAMS ? C::NW : 1][64];   // per-wave parts of W S, accumulator layout
     uint16_t KH[SEAMS ? 2 : 1][16][C::LDB];       // window keys hi, [token][dim], rows >= w zero
     uint16_t KL[SEAMS ? 2 : 1][16][C::LDB];       // window keys lo
+    uint16_t TH[C::NW][16][C::LDB];               // each wave's 16 rows of T, split (wave-private)
+    uint16_t TL[C::NW][16][C::LDB];
 };
 
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
@@ -105,7 +110,7 @@ template <int D, bool SEAMS>
 __global__ void __launch_bounds__((CsCfg<D, SEAMS>::NT)) compose_split_kernel(const ComposeArgs a, const float *ops)
 {
     using C = CsCfg<D, SEAMS>;
-    constexpr int KB = C::KB, NST = C::NST;
+    constexpr int KB = C::KB, NST = C::NST, NTQ = C::NTQ;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     CsSmem<D, SEAMS> &sm = *reinterpret_cast<CsSmem<D, SEAMS> *>(smem_raw);
 
@@ -130,40 +135,60 @@ __global__ void __launch_bounds__((CsCfg<D, SEAMS>::NT)) compose_split_kernel(co
     };
 
     // ---- register ring of T rows and S0 rows ---------------------------------
-    // lane (g, r16): T[row0 + r16][32 kb + 8 g .. + 7] for every kb, S0 as Sown
-    float Tb[NST][D / 4];
+    // T rows load coalesced (whole rows per instruction: lane l takes row
+    // RPI q + l / QPR, columns 4 (l % QPR) .. + 3 of load q), are split into bf16
+    // hi/lo one step ahead of their use, off the serial chain, and parked in the
+    // wave's own LDS rows TH/TL, from which the products read matrix-core
+    // fragments T[row0 + r16][32 kb + 8 g .. + 7].  S0 rows: as Sown.
+    constexpr int QPR = D / 4, RPI = 64 / QPR, NQ = 16 / RPI;
+    float4 Tq[NTQ][NQ];
     f4 S0b[NST];
-    auto t_rows = [&](int j) {   // this lane's row of T for segment position j
-        return a.T_pool + (int64_t)a.order[j] * a.h_v * D * D + hoff + (int64_t)(row0 + r16) * D + 8 * g;
+    auto fetch_t = [&](int j, float4 (&T)[NQ]) {
+        const float *Tp = a.T_pool + (int64_t)a.order[j] * a.h_v * D * D + hoff +
+                          (int64_t)(row0 + lane / QPR) * D + 4 * (lane % QPR);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) T[q] = *reinterpret_cast<const float4 *>(Tp + (int64_t)q * RPI * D);
     };
-    auto fetch_t = [&](const float *Tp, int kb, float (&T)[D / 4]) {
-        const float4 *p = reinterpret_cast<const float4 *>(Tp + 32 * kb);
-        const float4 x0 = p[0], x1 = p[1];
-        T[8 * kb + 0] = x0.x; T[8 * kb + 1] = x0.y; T[8 * kb + 2] = x0.z; T[8 * kb + 3] = x0.w;
-        T[8 * kb + 4] = x1.x; T[8 * kb + 5] = x1.y; T[8 * kb + 6] = x1.z; T[8 * kb + 7] = x1.w;
+    auto stage_t = [&](const float4 (&T)[NQ]) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            uint2 hi, lo;
+            split4p(T[q].x, T[q].y, T[q].z, T[q].w, hi, lo);
+            const int r = RPI * q + lane / QPR, c = 4 * (lane % QPR);
+            *reinterpret_cast<uint2 *>(&sm.TH[wv][r][c]) = hi;
+            *reinterpret_cast<uint2 *>(&sm.TL[wv][r][c]) = lo;
+        }
     };
     auto fetch_s0 = [&](int j, f4 &S0) {
         const float *Sp = a.S0_pool + (int64_t)a.order[j] * a.h_v * D * D + hoff;
 #pragma unroll
         for (int i = 0; i < 4; ++i) S0[i] = Sp[(int64_t)(row0 + 4 * g + i) * D + c0 + r16];
     };
-    auto fetch = [&](int j, float (&T)[D / 4], f4 &S0) {
-        const float *Tp = t_rows(j);
+    // ring start: T of positions 0 .. NTQ-1 in slots 0 .. NTQ-1, position 0
+    // staged and its slot refilled with position NTQ; S0 of positions 0 .. NST-1.
+    // Afterwards the end of step j stages T of position j + 1 (slot (j + 1) % NTQ),
+    // refills that slot with position j + 1 + NTQ, and refills the S0 slot of
+    // step j with position j + NST.
+    auto ring_start = [&]() {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) fetch_t(Tp, kb, T);
-        fetch_s0(j, S0);
+        for (int s = 0; s < NTQ; ++s) fetch_t(min(s, n - 1), Tq[s]);
+#pragma unroll
+        for (int s = 0; s < NST; ++s) fetch_s0(min(s, n - 1), S0b[s]);
+        stage_t(Tq[0]);
+        fetch_t(min(NTQ, n - 1), Tq[0]);
+    };
+    auto ring_advance = [&](int j, int s) {   // end of step j, unroll slot s = j % NST
+        const int s1 = (s + 1) % NTQ;
+        stage_t(Tq[s1]);
+        fetch_t(min(j + 1 + NTQ, n - 1), Tq[s1]);
     };
     // S_new = S0 + T S for this wave's rows, S split in LDS buffer `buf`
-    auto product = [&](const float (&T)[D / 4], const f4 &S0, int buf) {
+    auto product = [&](const f4 &S0, int buf) {
         f4 acc = S0, c1 = zero4();
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const int k0 = 32 * kb + 8 * g;
-            float tx[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tx[e] = T[8 * kb + e];
-            b8 ah, al;
-            split8(tx, ah, al);
+            const b8 ah = ld_b8(&sm.TH[wv][r16][k0]), al = ld_b8(&sm.TL[wv][r16][k0]);
             const b8 bh = ld_b8(&sm.SH[buf][r16][k0]), bl = ld_b8(&sm.SL[buf][r16][k0]);
             acc = mma(ah, bh, acc);
             c1 = mma(al, bh, c1);
@@ -174,19 +199,19 @@ __global__ void __launch_bounds__((CsCfg<D, SEAMS>::NT)) compose_split_kernel(co
 
     if constexpr (!SEAMS) {
         // S_{j+1} = T_j S_j + S0_j; S_j split in buffer cur, one barrier per step
-#pragma unroll
-        for (int s = 0; s < NST; ++s)
-            if (s < n) fetch(s, Tb[s], S0b[s]);
+        ring_start();
         put_state(0, Sown);
         int cur = 0;
         auto step = [&](const int j, const int s) __attribute__((always_inline)) {
             lds_barrier();   // S_j complete in buffer cur
-            const f4 acc = product(Tb[s], S0b[s], cur);
-            // straight-line refill (clamped): no branch between the products and their reads
-            fetch(min(j + NST, n - 1), Tb[s], S0b[s]);
+            const f4 acc = product(S0b[s], cur);
             Sown = acc;
             put_state(cur ^ 1, acc);
             cur ^= 1;
+            // off the chain, straight-line and clamped in range: next T staged,
+            // ring refills
+            ring_advance(j, s);
+            fetch_s0(min(j + NST, n - 1), S0b[s]);
         };
         int j0 = 0;
         for (; j0 + NST <= n; j0 += NST) {
@@ -247,8 +272,18 @@ __global__ void __launch_bounds__((CsCfg<D, SEAMS>::NT)) compose_split_kernel(co
         // what step j itself and the end of step j need.
 #pragma unroll
         for (int s = 0; s < NST; ++s) fetch_win(a.first_pos + s, s);
-#pragma unroll
-        for (int s = 0; s < NST; ++s) fetch(min(s, n - 1), Tb[s], S0b[s]);
+        ring_start();
+        // L2 warm-up: every workgroup of a head touches its own 1/8 of T (16 rows,
+        // one float4 per thread) three positions ahead, so the HBM misses of a
+        // position are spread over the head's workgroups before its rows are
+        // streamed by all of them; the value is retired one step later
+        float4 warm = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int cb = lb % (D / 16);
+        auto touch_t = [&](int j) {
+            warm = *reinterpret_cast<const float4 *>(a.T_pool + (int64_t)a.order[min(j, n - 1)] * a.h_v * D * D +
+                                                     hoff + (int64_t)cb * 16 * D + 4 * tid);
+        };
+        touch_t(3);
         put_state(0, Sown);
         part_p(0, 0);
         stage_k(0, 0);
@@ -264,11 +299,7 @@ __global__ void __launch_bounds__((CsCfg<D, SEAMS>::NT)) compose_split_kernel(co
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 const int k0 = 32 * kb + 8 * g;
-                float tx[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) tx[e] = Tb[s][8 * kb + e];
-                b8 ah, al;
-                split8(tx, ah, al);
+                const b8 ah = ld_b8(&sm.TH[wv][r16][k0]), al = ld_b8(&sm.TL[wv][r16][k0]);
                 const b8 bh = ld_b8(&sm.SH[cur][r16][k0]), bl = ld_b8(&sm.SL[cur][r16][k0]);
                 const b8 kh = ld_b8(&sm.KH[cur][r16][k0]), kl = ld_b8(&sm.KL[cur][r16][k0]);
                 ts = mma(ah, bh, ts);
@@ -298,11 +329,15 @@ __global__ void __launch_bounds__((CsCfg<D, SEAMS>::NT)) compose_split_kernel(co
             part_p((s + 1) % NST, cur ^ 1);
             stage_k((s + 1) % NST, cur ^ 1);
             cur ^= 1;
-            // refills, straight-line and in range (clamped): window of step j + NST
-            // into the slot step j used, then segment j + NST into this ring stage
+            // off the chain, straight-line and clamped in range: next T staged and
+            // its ring slot refilled; the window of step j + NST into the slot step j
+            // used, and its S0
+            ring_advance(j, s);
             fetch_win(pos + NST, s);
             asm volatile("" ::: "memory");
-            fetch(min(j + NST, n - 1), Tb[s], S0b[s]);
+            fetch_s0(min(j + NST, n - 1), S0b[s]);
+            asm volatile("" :: "v"(warm.x), "v"(warm.y), "v"(warm.z), "v"(warm.w));
+            touch_t(j + 4);
         };
         int j0 = 0;
         for (; j0 + NST <= n; j0 += NST) {
