@@ -195,81 +195,75 @@ build_delta_f16_kernel(const DeltaArgs a)
                     }
                     fetch_v(min(cp + 1, nch - 1));
                 }
-                if (pw == 0) {
-                    // the four diagonal Gram tiles, then the inverses of I + A'_bb for all
-                    // four blocks at once (lanes 16b .. 16b + 15 solve block b).  A'_bb is
-                    // written transposed into the block's upper triangle (column q of A'
-                    // is then one contiguous row); the inverse M_bb goes to Mi[b] row-major.
+                // off-diagonal Gram tile q -> (ti, tj): q = 0..5 -> (1,0) (2,0) (2,1) (3,0) (3,1) (3,2);
+                // waves 0-3 take tile pw, waves 2-3 also tile pw + 2
+                auto offdiag = [&](int q) {
+                    const int ti = q < 1 ? 1 : (q < 3 ? 2 : 3), tj = q - ti * (ti - 1) / 2;
+                    f4 acc = zero4();
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        const int o = 16 * b;
-                        f4 acc = zero4();
+                    for (int kb = 0; kb < KB; ++kb) {
+                        const h8 A = *reinterpret_cast<const h8 *>(&sm.Ks[bp_][16 * ti + r16][32 * kb + 8 * g]);
+                        const h8 B = *reinterpret_cast<const h8 *>(&sm.Ks[bp_][16 * tj + r16][32 * kb + 8 * g]);
+                        acc = mma(A, B, acc);
+                    }
+                    const float4 bq = *reinterpret_cast<const float4 *>(&sm.beta[16 * ti + 4 * g]);
+                    const float bqv[4] = {bq.x, bq.y, bq.z, bq.w};
 #pragma unroll
-                        for (int kb = 0; kb < KB; ++kb) {
-                            const h8 A = *reinterpret_cast<const h8 *>(&sm.Ks[bp_][o + r16][32 * kb + 8 * g]);
-                            acc = mma(A, A, acc);
-                        }
-                        const float4 bq = *reinterpret_cast<const float4 *>(&sm.beta[o + 4 * g]);
-                        const float bqv[4] = {bq.x, bq.y, bq.z, bq.w};
+                    for (int i = 0; i < 4; ++i) sm.Gm[16 * ti + 4 * g + i][16 * tj + r16] = bqv[i] * acc[i];
+                };
+                offdiag(pw);
+                if (pw >= 2) offdiag(pw + 2);
+                {
+                    // diagonal block pw: Gram tile, A' = b_r k_r.k_s (s < r) written
+                    // transposed into the block's upper triangle (column q of A' is then
+                    // one contiguous row), then the inverse of I + A' by forward
+                    // substitution, lane column c = r16 (the four lane groups repeat it)
+                    const int o = 16 * pw;
+                    f4 acc = zero4();
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int rr = 4 * g + i;   // A'[rr][r16] for r16 < rr, stored at [r16][rr]
-                            if (r16 < rr) sm.Gm[o + r16][o + rr] = bqv[i] * acc[i];
-                        }
+                    for (int kb = 0; kb < KB; ++kb) {
+                        const h8 A = *reinterpret_cast<const h8 *>(&sm.Ks[bp_][o + r16][32 * kb + 8 * g]);
+                        acc = mma(A, A, acc);
+                    }
+                    const float4 bq = *reinterpret_cast<const float4 *>(&sm.beta[o + 4 * g]);
+                    const float bqv[4] = {bq.x, bq.y, bq.z, bq.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int rr = 4 * g + i;   // A'[rr][r16] for r16 < rr, stored at [r16][rr]
+                        if (r16 < rr) sm.Gm[o + r16][o + rr] = bqv[i] * acc[i];
                     }
                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                    {
-                        const int o = 16 * g, c = r16;   // block g, column c
-                        float x[16];
+                    const int c = r16;
+                    float x[16];
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
-                        // column q of A' (its entries r > q) rides a ring of four rows, loaded
-                        // four steps ahead; only the float4 pieces holding some r > q
-                        float4 ring[4][4];
-                        auto load_col = [&](int q, float4 (&dst)[4]) {
+                    for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
+                    // column q of A' (its entries r > q) rides a ring of four rows, loaded
+                    // four steps ahead; only the float4 pieces holding some r > q
+                    float4 ring[4][4];
+                    auto load_col = [&](int q, float4 (&dst)[4]) {
 #pragma unroll
-                            for (int v = 0; v < 4; ++v)
-                                if (4 * v + 3 > q) dst[v] = *reinterpret_cast<const float4 *>(&sm.Gm[o + q][o + 4 * v]);
-                        };
+                        for (int v = 0; v < 4; ++v)
+                            if (4 * v + 3 > q) dst[v] = *reinterpret_cast<const float4 *>(&sm.Gm[o + q][o + 4 * v]);
+                    };
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) load_col(q, ring[q]);
+                    for (int q = 0; q < 4; ++q) load_col(q, ring[q]);
 #pragma unroll
-                        for (int q = 0; q < 15; ++q) {
-                            const float4 *cur = ring[q % 4];
-                            float colv[16];
+                    for (int q = 0; q < 15; ++q) {
+                        const float4 *cur = ring[q % 4];
+                        float colv[16];
 #pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                colv[4 * v] = cur[v].x; colv[4 * v + 1] = cur[v].y;
-                                colv[4 * v + 2] = cur[v].z; colv[4 * v + 3] = cur[v].w;
-                            }
-#pragma unroll
-                            for (int r = q + 1; r < 16; ++r) x[r] -= colv[r] * x[q];
-                            if (q + 4 < 15) load_col(q + 4, ring[q % 4]);
+                        for (int v = 0; v < 4; ++v) {
+                            colv[4 * v] = cur[v].x; colv[4 * v + 1] = cur[v].y;
+                            colv[4 * v + 2] = cur[v].z; colv[4 * v + 3] = cur[v].w;
                         }
-                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) sm.Mi[g][r][c] = x[r];   // zero above the diagonal
+                        for (int r = q + 1; r < 16; ++r) x[r] -= colv[r] * x[q];
+                        if (q + 4 < 15) load_col(q + 4, ring[q % 4]);
                     }
-                } else {
-                    // off-diagonal Gram tiles, two per wave
+                    // column c of the inverse (zero above the diagonal); the four lane
+                    // groups hold the same column and write the same values
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int q = 2 * (pw - 1) + u;
-                        // q = 0..5 -> (ti, tj) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
-                        const int ti = q < 1 ? 1 : (q < 3 ? 2 : 3), tj = q - ti * (ti - 1) / 2;
-                        f4 acc = zero4();
-#pragma unroll
-                        for (int kb = 0; kb < KB; ++kb) {
-                            const h8 A = *reinterpret_cast<const h8 *>(&sm.Ks[bp_][16 * ti + r16][32 * kb + 8 * g]);
-                            const h8 B = *reinterpret_cast<const h8 *>(&sm.Ks[bp_][16 * tj + r16][32 * kb + 8 * g]);
-                            acc = mma(A, B, acc);
-                        }
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int rr = 16 * ti + 4 * g + i;
-                            sm.Gm[rr][16 * tj + r16] = sm.beta[rr] * acc[i];
-                        }
-                    }
+                    for (int r = 0; r < 16; ++r) sm.Mi[pw][r][c] = x[r];
                 }
             }
             lds_barrier();
@@ -375,8 +369,6 @@ build_delta_f16_kernel(const DeltaArgs a)
                 for (int mt = 0; mt < MT; ++mt) X[mt][jn] *= f;
                 sig[jn] = target;
             };
-            // E = U 2^(sv - sig) - W Xhat for all four tiles, token tiles {2 hb, 2 hb + 1}
-            // per phase: every W fragment read from LDS feeds the four tiles' products
             auto state_prescale = [&]() {   // chunk gate on S, value-scale catch-up
 #pragma unroll
                 for (int jn = 0; jn < C::TPW; ++jn) {
@@ -390,51 +382,54 @@ build_delta_f16_kernel(const DeltaArgs a)
                     }
                 }
             };
-            auto state_e_half = [&](int hb) {
-                f4 E[C::TPW][2];
+            // E = U 2^(sv - sig) - W Xhat for the column tiles {2 pp, 2 pp + 1}, all 64
+            // tokens: each tile's Xhat is converted to fp16 fragments once per chunk
+            auto state_e_pair = [&](int pp) {
+                f4 E[2][4];
 #pragma unroll
-                for (int jn = 0; jn < C::TPW; ++jn) {
-                    const int n = C::TPW * w + jn;
+                for (int q = 0; q < 2; ++q) {
+                    const int jn = 2 * pp + q, n = C::TPW * w + jn;
 #pragma unroll
-                    for (int tj = 0; tj < 2; ++tj) E[jn][tj] = zero4();
+                    for (int tj = 0; tj < 4; ++tj) E[q][tj] = zero4();
                     if (n >= MT) {
                         const float usc = exp2f((float)sm.sv[bs_] - sig[jn]);
                         const int cc = 16 * (n - MT) + r16;
 #pragma unroll
-                        for (int tj = 0; tj < 2; ++tj) {
-                            const float4 u = *reinterpret_cast<const float4 *>(&sm.UT[cc][16 * (2 * hb + tj) + 4 * g]);
-                            E[jn][tj] = f4{u.x, u.y, u.z, u.w} * usc;
+                        for (int tj = 0; tj < 4; ++tj) {
+                            const float4 u = *reinterpret_cast<const float4 *>(&sm.UT[cc][16 * tj + 4 * g]);
+                            E[q][tj] = f4{u.x, u.y, u.z, u.w} * usc;
                         }
                     }
                 }
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
-                    h8 B[C::TPW];
+                    h8 B[2];
 #pragma unroll
-                    for (int jn = 0; jn < C::TPW; ++jn)
+                    for (int q = 0; q < 2; ++q)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            B[jn][i] = (_Float16)X[2 * kb][jn][i];
-                            B[jn][4 + i] = (_Float16)X[2 * kb + 1][jn][i];
+                            B[q][i] = (_Float16)X[2 * kb][2 * pp + q][i];
+                            B[q][4 + i] = (_Float16)X[2 * kb + 1][2 * pp + q][i];
                         }
 #pragma unroll
-                    for (int tj = 0; tj < 2; ++tj) {
-                        const int ti = 2 * hb + tj;
-                        // -W[16 ti + m][k], k = 32 kb + 4g + (e & 3) + 16 (e >> 2)
-                        const h8 A = cat8(ld_tr4(&sm.nWT[0][0], C::LDT, 32 * kb + 4 * g, 16 * ti, lane),
-                                          ld_tr4(&sm.nWT[0][0], C::LDT, 32 * kb + 16 + 4 * g, 16 * ti, lane));
+                    for (int tj = 0; tj < 4; ++tj) {
+                        // -W[16 tj + m][k], k = 32 kb + 4g + (e & 3) + 16 (e >> 2)
+                        const h8 A = cat8(ld_tr4(&sm.nWT[0][0], C::LDT, 32 * kb + 4 * g, 16 * tj, lane),
+                                          ld_tr4(&sm.nWT[0][0], C::LDT, 32 * kb + 16 + 4 * g, 16 * tj, lane));
 #pragma unroll
-                        for (int jn = 0; jn < C::TPW; ++jn) E[jn][tj] = mma(A, B[jn], E[jn][tj]);
+                        for (int q = 0; q < 2; ++q) E[q][tj] = mma(A, B[q], E[q][tj]);
                     }
                 }
-                // token block hb (tokens 32 hb .. 32 hb + 31) as fp16 B operands
+                // token blocks of 32 as fp16 B operands of the update
 #pragma unroll
-                for (int jn = 0; jn < C::TPW; ++jn)
+                for (int q = 0; q < 2; ++q)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        Eb[jn][hb][i] = (_Float16)E[jn][0][i];
-                        Eb[jn][hb][4 + i] = (_Float16)E[jn][1][i];
-                    }
+                    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            Eb[2 * pp + q][hb][i] = (_Float16)E[q][2 * hb][i];
+                            Eb[2 * pp + q][hb][4 + i] = (_Float16)E[q][2 * hb + 1][i];
+                        }
             };
             // Xhat += K^T E for all four tiles, row tiles [m0, m1): every K^T fragment
             // read from LDS feeds the four tiles' products
@@ -457,10 +452,10 @@ build_delta_f16_kernel(const DeltaArgs a)
             };
             if (dos) {
                 state_prescale();
-                state_e_half(0);
+                state_e_pair(0);
             }
             lds_barrier();
-            if (dos) state_e_half(1);
+            if (dos) state_e_pair(1);
             lds_barrier();
             if (dos) state_u4(0, MT / 2);
             lds_barrier();
