@@ -144,13 +144,13 @@ build_delta_f16_kernel(const DeltaArgs a)
                 float vm = 0.f;
 #pragma unroll
                 for (int p = 0; p < C::PASSES; ++p) {
+                    const int t = prow + RPP * p;
+                    const bool in = 64 * cp + t < len;   // rows past the end were clamped: zero them
+                    mask_raw8(kraw[p], in);
+                    mask_raw8(vraw[p], in);
                     float kx[8], vx[8];
                     widen8(kraw[p], kx);
                     widen8(vraw[p], vx);
-                    const int t = prow + RPP * p;
-                    const bool in = 64 * cp + t < len;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) { kx[e] = in ? kx[e] : 0.f; vx[e] = in ? vx[e] : 0.f; }
                     h8 kk;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
@@ -185,12 +185,11 @@ build_delta_f16_kernel(const DeltaArgs a)
 #pragma unroll
                     for (int p = 0; p < C::PASSES; ++p) {
                         float vx[8];
-                        widen8(vraw[p], vx);
+                        widen8(vraw[p], vx);   // zeroed past the end in phase 1
                         const int t = prow + RPP * p;
-                        const bool in = 64 * cp + t < len;   // rows past the end were clamped
                         h8 vv;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) vv[e] = (_Float16)(in ? vx[e] * vsc : 0.f);
+                        for (int e = 0; e < 8; ++e) vv[e] = (_Float16)(vx[e] * vsc);
                         *reinterpret_cast<h8 *>(&sm.Vs[t][pcol]) = vv;
                     }
                     fetch_v(min(cp + 1, nch - 1));

@@ -73,6 +73,15 @@ __device__ __forceinline__ void ld_raw8(const float *p, raw8_f32 &r) {
 }
 __device__ __forceinline__ void zero_raw8(raw8_bf16 &r) { r.u = make_uint4(0u, 0u, 0u, 0u); }
 __device__ __forceinline__ void zero_raw8(raw8_f32 &r) { r.a = make_float4(0.f, 0.f, 0.f, 0.f); r.b = r.a; }
+// zero a raw row piece (rows past a segment end are loaded clamped, then zeroed)
+__device__ __forceinline__ void mask_raw8(raw8_bf16 &r, bool keep) {
+    r.u = make_uint4(keep ? r.u.x : 0u, keep ? r.u.y : 0u, keep ? r.u.z : 0u, keep ? r.u.w : 0u);
+}
+__device__ __forceinline__ void mask_raw8(raw8_f32 &r, bool keep) {
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    r.a = keep ? r.a : z;
+    r.b = keep ? r.b : z;
+}
 __device__ __forceinline__ void widen8(const raw8_bf16 &r, float (&x)[8]) {
     const uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};
 #pragma unroll
