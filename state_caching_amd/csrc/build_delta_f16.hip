@@ -95,6 +95,9 @@ build_delta_f16_kernel(const DeltaArgs a)
     // barriers each, so every barrier meets all waves; prep runs one chunk ahead.
     if (is_prep) {
         // ------------------------------------------------------------ prep state
+        // the prep chain sets the pace: its waves issue ahead of the state waves
+        // sharing their SIMDs, which fill the gaps
+        __builtin_amdgcn_s_setprio(3);
         const int ptid = tid - 64 * NS, pw = w - NS;
         constexpr int CPR = D / 8;
         const int prow = (ptid >= 0 ? ptid : 0) / CPR, pcol = 8 * ((ptid >= 0 ? ptid : 0) % CPR);
@@ -161,15 +164,20 @@ build_delta_f16_kernel(const DeltaArgs a)
                 }
                 vm = wave_max(vm);
                 if (lane == 0) sm.wmax[pw] = vm;
-                if (pw == 0) {
+                {
+                    // gates: every prep wave computes them (straight-line with the
+                    // staging), wave 0 writes them
                     const bool gin = 64 * cp + lane < len;
                     const float br = gin ? to_f32(braw) : 0.f, ar = gin ? to_f32(araw) : 1.f;
                     const float l2 = log2f(ar);
                     const float sfx = wave_suffix_excl(l2);
                     cl_lane += (double)l2;
-                    sm.beta[lane] = br;
-                    sm.bd[lane] = br * exp2f(sfx);
-                    if (lane == 0) sm.gb[bp_] = exp2f(sfx + l2);
+                    const float bdv = br * exp2f(sfx), gbv = exp2f(sfx + l2);
+                    if (pw == 0) {
+                        sm.beta[lane] = br;
+                        sm.bd[lane] = bdv;
+                        if (lane == 0) sm.gb[bp_] = gbv;
+                    }
                 }
                 fetch_k(min(cp + 1, nch - 1));
             }
@@ -211,7 +219,6 @@ build_delta_f16_kernel(const DeltaArgs a)
                     for (int i = 0; i < 4; ++i) sm.Gm[16 * ti + 4 * g + i][16 * tj + r16] = bqv[i] * acc[i];
                 };
                 offdiag(pw);
-                if (pw >= 2) offdiag(pw + 2);
                 {
                     // diagonal block pw: Gram tile, A' = b_r k_r.k_s (s < r) written
                     // transposed into the block's upper triangle (column q of A' is then
@@ -231,8 +238,7 @@ build_delta_f16_kernel(const DeltaArgs a)
                         const int rr = 4 * g + i;   // A'[rr][r16] for r16 < rr, stored at [r16][rr]
                         if (r16 < rr) sm.Gm[o + r16][o + rr] = bqv[i] * acc[i];
                     }
-                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                    const int c = r16;
+                    const int c = r16;   // (LDS operations of a wave complete in order)
                     float x[16];
 #pragma unroll
                     for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
@@ -264,6 +270,7 @@ build_delta_f16_kernel(const DeltaArgs a)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) sm.Mi[pw][r][c] = x[r];
                 }
+                if (pw >= 2) offdiag(pw + 2);
             }
             lds_barrier();
             // ===================== phases 3-4: W and U of chunk cp | E tile 1, update
