@@ -12,9 +12,9 @@
 //   state waves (d/32) : chunk c   -- E = U - W Xhat, Xhat += K^T E on the
 //                        wave's four 16-column tiles of X
 //
-// Four LDS barriers per chunk; the state waves put a quarter of their matrix
-// work into every phase so the matrix cores stay busy while the prep waves
-// run their latency-bound steps.  Xhat is kept in power-of-two units per
+// Three LDS barriers per chunk; the state waves spread their matrix work over
+// the phases so the matrix cores stay busy while the prep waves run their
+// latency-bound steps.  Xhat is kept in power-of-two units per
 // column tile (renormalised every 4 chunks, or when the value scale runs
 // ahead of the state), so every computed fp16 operand stays in range.
 #include "common.h"
@@ -91,7 +91,7 @@ build_delta_f16_kernel(const DeltaArgs a)
     const bool is_prep = w >= NS;
 
 
-    // Warp-specialised roles.  Both loops run nch + 1 iterations of four
+    // Warp-specialised roles.  Both loops run nch + 1 iterations of three
     // barriers each, so every barrier meets all waves; prep runs one chunk ahead.
     if (is_prep) {
         // ------------------------------------------------------------ prep state
@@ -142,7 +142,7 @@ build_delta_f16_kernel(const DeltaArgs a)
             const int cp = it;
             constexpr bool dop = true;
             const int bp_ = cp & 1;
-            // ===================== phase 1: stage keys and gates of cp | E tile 0
+            // ===================== phase 1: stage keys and gates of cp | E of column tiles 0-1
             if (dop) {
                 float vm = 0.f;
 #pragma unroll
@@ -182,7 +182,7 @@ build_delta_f16_kernel(const DeltaArgs a)
                 fetch_k(min(cp + 1, nch - 1));
             }
             lds_barrier();
-            // ===================== phase 2: V^, Gram, diagonal inverses | update tile 0
+            // ===================== phase 2: V^, Gram, diagonal inverses | E of column tiles 2-3
             if (dop) {
                 // value scale of chunk cp; V^ = V * 2^-sv into Vs
                 {
@@ -273,12 +273,12 @@ build_delta_f16_kernel(const DeltaArgs a)
                 if (pw >= 2) offdiag(pw + 2);
             }
             lds_barrier();
-            // ===================== phases 3-4: W and U of chunk cp | E tile 1, update
+            // ===================== phase 3: W and U of chunk cp | update
             // (I + L) [W | U] = [diag(b) K | diag(b dec) V^], L = diag(b) strictlower(K K^T),
             // by block forward substitution over the four 16-row blocks:
             //   X_i = M_ii (R_i - sum_{j<i} L_ij X_j),  M_ii = (I + L_ii)^-1
             // Each wave owns the key-column tiles {pw, pw + 4, ...} of W and the same value-
-            // column tiles of U; rows 0-1 in phase 3, rows 2-3 in phase 4.  Products are
+            // column tiles of U (the rows chain only through its own registers).  Products are
             // 16 deep on the matrix cores: A fragments (rows of L_ij, M_ii) from LDS, B
             // fragments from the accumulator tiles, k = 4g + e (upper half zero).
             auto subst_row = [&](int i) {
@@ -323,13 +323,11 @@ build_delta_f16_kernel(const DeltaArgs a)
                     *reinterpret_cast<float4 *>(&sm.UT[col][16 * i + 4 * g]) = make_float4(xu[0], xu[1], xu[2], xu[3]);
                 }
             };
-            if (dop) { subst_row(0); subst_row(1); }
-            lds_barrier();
-            if (dop) { subst_row(2); subst_row(3); }
+            if (dop) { subst_row(0); subst_row(1); subst_row(2); subst_row(3); }
             lds_barrier();
         }
 #pragma unroll
-        for (int ph = 0; ph < 4; ++ph) lds_barrier();
+        for (int ph = 0; ph < 3; ++ph) lds_barrier();
 
         if (pw == 0) {
             const double tot = wave_sum_f64(cl_lane);
@@ -463,10 +461,8 @@ build_delta_f16_kernel(const DeltaArgs a)
             lds_barrier();
             if (dos) state_e_pair(1);
             lds_barrier();
-            if (dos) state_u4(0, MT / 2);
-            lds_barrier();
             if (dos) {
-                state_u4(MT / 2, MT);
+                state_u4(0, MT);
 #pragma unroll
                 for (int jn = 0; jn < C::TPW; ++jn) state_u(jn);
             }
