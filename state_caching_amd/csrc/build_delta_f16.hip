@@ -44,11 +44,12 @@ struct F16Smem {
                                  // come from transposed loads of these rows)
     _Float16 nWT[D][C::LDT];     // -W^T = -(M diag(b) K)^T, token-contiguous rows
     float UT[D][C::LDU];         // U^T (value column-major), in units of 2^sv
-    _Float16 Vs[64][C::LDW];     // V * 2^-sv, token-major
-    float Gm[64][C::LDG];        // b_r k_r.k_s for s < r; the inverse of each diagonal
-                                 // 16x16 block is kept transposed in its upper triangle
-    float Mi[4][16][20];         // inverses of the diagonal blocks, row-major
-    float beta[64], bd[64];
+    _Float16 Vs[64][C::LDW];     // diag(dec) V * 2^-sv, token-major
+    float Gm[64][C::LDG];        // k_r.k_s for s < r in the off-diagonal blocks; each
+                                 // diagonal block holds A' = b_r k_r.k_s transposed in
+                                 // its upper triangle
+    float Mi[4][16][20];         // M' = (I + A'_bb)^-1 diag(b_b) per diagonal block, row-major
+    float beta[64], dec[64];     // b_t and dec_t = prod_{s > t} a_s of the chunk in prep
     float gb[2];                 // chunk gate product, per pipeline slot
     int sv[2];                   // value scale exponent, per pipeline slot
     float wmax[4];
@@ -172,10 +173,10 @@ build_delta_f16_kernel(const DeltaArgs a)
                     const float l2 = log2f(ar);
                     const float sfx = wave_suffix_excl(l2);
                     cl_lane += (double)l2;
-                    const float bdv = br * exp2f(sfx), gbv = exp2f(sfx + l2);
+                    const float dcv = exp2f(sfx), gbv = exp2f(sfx + l2);
                     if (pw == 0) {
                         sm.beta[lane] = br;
-                        sm.bd[lane] = bdv;
+                        sm.dec[lane] = dcv;
                         if (lane == 0) sm.gb[bp_] = gbv;
                     }
                 }
@@ -184,7 +185,7 @@ build_delta_f16_kernel(const DeltaArgs a)
             lds_barrier();
             // ===================== phase 2: V^, Gram, diagonal inverses | E of column tiles 2-3
             if (dop) {
-                // value scale of chunk cp; V^ = V * 2^-sv into Vs
+                // value scale of chunk cp; V^ = diag(dec) V * 2^-sv into Vs
                 {
                     const float vm = fmaxf(fmaxf(sm.wmax[0], sm.wmax[1]), fmaxf(sm.wmax[2], sm.wmax[3]));
                     const int sv = pow2_exponent(vm);
@@ -195,9 +196,10 @@ build_delta_f16_kernel(const DeltaArgs a)
                         float vx[8];
                         widen8(vraw[p], vx);   // zeroed past the end in phase 1
                         const int t = prow + RPP * p;
+                        const float rsc = vsc * sm.dec[t];
                         h8 vv;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) vv[e] = (_Float16)(vx[e] * vsc);
+                        for (int e = 0; e < 8; ++e) vv[e] = (_Float16)(vx[e] * rsc);
                         *reinterpret_cast<h8 *>(&sm.Vs[t][pcol]) = vv;
                     }
                     fetch_v(min(cp + 1, nch - 1));
@@ -213,10 +215,8 @@ build_delta_f16_kernel(const DeltaArgs a)
                         const h8 B = *reinterpret_cast<const h8 *>(&sm.Ks[bp_][16 * tj + r16][32 * kb + 8 * g]);
                         acc = mma(A, B, acc);
                     }
-                    const float4 bq = *reinterpret_cast<const float4 *>(&sm.beta[16 * ti + 4 * g]);
-                    const float bqv[4] = {bq.x, bq.y, bq.z, bq.w};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sm.Gm[16 * ti + 4 * g + i][16 * tj + r16] = bqv[i] * acc[i];
+                    for (int i = 0; i < 4; ++i) sm.Gm[16 * ti + 4 * g + i][16 * tj + r16] = acc[i];
                 };
                 offdiag(pw);
                 {
@@ -265,45 +265,64 @@ build_delta_f16_kernel(const DeltaArgs a)
                         for (int r = q + 1; r < 16; ++r) x[r] -= colv[r] * x[q];
                         if (q + 4 < 15) load_col(q + 4, ring[q % 4]);
                     }
-                    // column c of the inverse (zero above the diagonal); the four lane
-                    // groups hold the same column and write the same values
+                    // column c of M' = (I + A')^-1 diag(b) (zero above the diagonal); the
+                    // four lane groups hold the same column and write the same values
+                    const float bc = sm.beta[o + c];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) sm.Mi[pw][r][c] = x[r];
+                    for (int r = 0; r < 16; ++r) sm.Mi[pw][r][c] = x[r] * bc;
                 }
                 if (pw >= 2) offdiag(pw + 2);
             }
             lds_barrier();
             // ===================== phase 3: W and U of chunk cp | update
-            // (I + L) [W | U] = [diag(b) K | diag(b dec) V^], L = diag(b) strictlower(K K^T),
-            // by block forward substitution over the four 16-row blocks:
-            //   X_i = M_ii (R_i - sum_{j<i} L_ij X_j),  M_ii = (I + L_ii)^-1
-            // Each wave owns the key-column tiles {pw, pw + 4, ...} of W and the same value-
-            // column tiles of U (the rows chain only through its own registers).  Products are
-            // 16 deep on the matrix cores: A fragments (rows of L_ij, M_ii) from LDS, B
-            // fragments from the accumulator tiles, k = 4g + e (upper half zero).
+            // (I + L) [W | U] = [diag(b) K | diag(b dec) V^], L = diag(b) strictlower(G),
+            // G = K K^T, by block forward substitution over the four 16-row blocks.  With
+            // M'_ii = (I + L_ii)^-1 diag(b_i) the row blocks are
+            //   X_i = M'_ii (R_i - sum_{j<i} G_ij X_j),  R = [K | diag(dec) V^]
+            // (diag(dec) is folded into V^ when it is staged).  Each wave owns the
+            // key-column tiles {pw, pw + 4, ...} of W and the same value-column tiles
+            // of U; the rows chain only through its own registers.  Products are 16 deep
+            // on the matrix cores, B fragments from the accumulator tiles, k = 4g + e;
+            // R_i rides the upper half of the first product (identity times the fp16 rows).
+            h4 idq;   // identity fragment: I[r16][4g + e]
+#pragma unroll
+            for (int e = 0; e < 4; ++e) idq[e] = (_Float16)(r16 == 4 * g + e ? 1.f : 0.f);
             auto subst_row = [&](int i) {
-                const float4 bq = *reinterpret_cast<const float4 *>(&sm.beta[16 * i + 4 * g]);
-                const float4 dq = *reinterpret_cast<const float4 *>(&sm.bd[16 * i + 4 * g]);
-                f4 aw[NTW], au[NTW];
+                h4 kk[NTW], vv[NTW];   // R_i rows 16i + 4g + e, fp16 B fragments
 #pragma unroll
-                for (int q = 0; q < NTW; ++q) {   // R_i in accumulator layout (rows 16i + 4g + e)
+                for (int q = 0; q < NTW; ++q) {
                     const int x0 = 16 * (pw + 4 * q);
-                    const h4 kk = ld_tr4(&sm.Ks[bp_][0][0], C::LDW, 16 * i + 4 * g, x0, lane);
-                    const h4 vv = ld_tr4(&sm.Vs[0][0], C::LDW, 16 * i + 4 * g, x0, lane);
-                    aw[q] = f4{(float)kk[0] * bq.x, (float)kk[1] * bq.y, (float)kk[2] * bq.z, (float)kk[3] * bq.w};
-                    au[q] = f4{(float)vv[0] * dq.x, (float)vv[1] * dq.y, (float)vv[2] * dq.z, (float)vv[3] * dq.w};
+                    kk[q] = ld_tr4(&sm.Ks[bp_][0][0], C::LDW, 16 * i + 4 * g, x0, lane);
+                    vv[q] = ld_tr4(&sm.Vs[0][0], C::LDW, 16 * i + 4 * g, x0, lane);
                 }
+                h4 bw[NTW], bu[NTW];
+                if (i == 0) {
 #pragma unroll
-                for (int j = 0; j < 3; ++j) {
-                    if (j < i) {
-                        const float4 l = *reinterpret_cast<const float4 *>(&sm.Gm[16 * i + r16][16 * j + 4 * g]);
-                        const h8 A = {(_Float16)-l.x, (_Float16)-l.y, (_Float16)-l.z, (_Float16)-l.w,
-                                      (_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+                    for (int q = 0; q < NTW; ++q) { bw[q] = kk[q]; bu[q] = vv[q]; }
+                } else {
+                    f4 aw[NTW], au[NTW];
 #pragma unroll
-                        for (int q = 0; q < NTW; ++q) {
-                            aw[q] = mma(A, cat8(Xw[q][j], h4z), aw[q]);
-                            au[q] = mma(A, cat8(Xu[q][j], h4z), au[q]);
+                    for (int j = 0; j < 3; ++j) {
+                        if (j < i) {
+                            const float4 l = *reinterpret_cast<const float4 *>(&sm.Gm[16 * i + r16][16 * j + 4 * g]);
+                            const h4 nl = {(_Float16)-l.x, (_Float16)-l.y, (_Float16)-l.z, (_Float16)-l.w};
+                            const h8 A = cat8(nl, j == 0 ? idq : h4z);
+#pragma unroll
+                            for (int q = 0; q < NTW; ++q) {
+                                if (j == 0) {
+                                    aw[q] = mma(A, cat8(Xw[q][0], kk[q]), zero4());
+                                    au[q] = mma(A, cat8(Xu[q][0], vv[q]), zero4());
+                                } else {
+                                    aw[q] = mma(A, cat8(Xw[q][j], h4z), aw[q]);
+                                    au[q] = mma(A, cat8(Xu[q][j], h4z), au[q]);
+                                }
+                            }
                         }
+                    }
+#pragma unroll
+                    for (int q = 0; q < NTW; ++q) {
+                        bw[q] = h4{(_Float16)aw[q][0], (_Float16)aw[q][1], (_Float16)aw[q][2], (_Float16)aw[q][3]};
+                        bu[q] = h4{(_Float16)au[q][0], (_Float16)au[q][1], (_Float16)au[q][2], (_Float16)au[q][3]};
                     }
                 }
                 const float4 mi = *reinterpret_cast<const float4 *>(&sm.Mi[i][r16][4 * g]);
@@ -311,10 +330,8 @@ build_delta_f16_kernel(const DeltaArgs a)
                               (_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
 #pragma unroll
                 for (int q = 0; q < NTW; ++q) {
-                    const h4 bw = {(_Float16)aw[q][0], (_Float16)aw[q][1], (_Float16)aw[q][2], (_Float16)aw[q][3]};
-                    const h4 bu = {(_Float16)au[q][0], (_Float16)au[q][1], (_Float16)au[q][2], (_Float16)au[q][3]};
-                    const f4 xw = mma(A, cat8(bw, h4z), zero4());
-                    const f4 xu = mma(A, cat8(bu, h4z), zero4());
+                    const f4 xw = mma(A, cat8(bw[q], h4z), zero4());
+                    const f4 xu = mma(A, cat8(bu[q], h4z), zero4());
                     Xw[q][i] = h4{(_Float16)xw[0], (_Float16)xw[1], (_Float16)xw[2], (_Float16)xw[3]};
                     Xu[q][i] = h4{(_Float16)xu[0], (_Float16)xu[1], (_Float16)xu[2], (_Float16)xu[3]};
                     const int col = 16 * (pw + 4 * q) + r16;
