@@ -109,8 +109,8 @@ typedef enum {
  * Workspace: hypic_workspace_size(desc, HYPIC_WS_BUILD) bytes (0 without conv
  * or key normalisation; ws may then be NULL).  Empty ranges give T = I, S0 = 0.
  * Errors: HYPIC_E_INVALID (null pointers, negative lengths, h_v % h_k != 0),
- * HYPIC_E_UNSUPPORTED (dimensions, DECAY+DIAG with conv, DELTA+DIAG),
- * HYPIC_E_WORKSPACE, HYPIC_E_HIP.
+ * HYPIC_E_UNSUPPORTED (dimensions, h_v * d_k >= 2^24, DECAY+DIAG with conv,
+ * DELTA+DIAG), HYPIC_E_WORKSPACE, HYPIC_E_HIP.
  */
 typedef struct {
     int32_t rule, gate_kind, in_dtype;

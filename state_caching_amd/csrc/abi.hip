@@ -64,6 +64,8 @@ hypic_status validate_build(const hypic_build_desc *d)
     if (d->gate_kind < HYPIC_GATE_HEAD_CONST || d->gate_kind > HYPIC_GATE_DIAG) return HYPIC_E_INVALID;
     if (d->conv_w < 0 || d->conv_w > 4) return HYPIC_E_INVALID;
     if (d->d_k != d->d_v || !dim_ok(d->d_k)) return HYPIC_E_UNSUPPORTED;
+    // row pitches h * d enter 24-bit multiplies in the build kernels
+    if ((int64_t)d->h_v * d->d_k >= (1 << 24)) return HYPIC_E_UNSUPPORTED;
     if (d->rule == HYPIC_RULE_DELTA && d->gate_kind != HYPIC_GATE_SCALAR) return HYPIC_E_UNSUPPORTED;
     if (d->rule == HYPIC_RULE_DECAY && build_needs_prep(d)) return HYPIC_E_UNSUPPORTED;
     if (!d->k || !d->v || !d->gate || !d->T_out || !d->S0_out) return HYPIC_E_INVALID;

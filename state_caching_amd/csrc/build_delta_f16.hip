@@ -113,22 +113,25 @@ build_delta_f16_kernel(const DeltaArgs a)
         // past its end are zeroed when staged), so the compiler's load waits stay
         // exact and the next chunk's rows remain in flight across the phases.
         TG braw, araw;   // gates of the next chunk (every prep wave loads them)
+        // row addresses: a per-chunk base (uniform, 64-bit) plus the row within the
+        // chunk (< 64, clamped to the segment's last row) times the pitch on 24-bit
+        // multiplies
         auto fetch_k = [&](int c) {
+            const int last = len - 1 - 64 * c;   // >= 0 for every chunk of the segment
+            const TKV *kc = kp + (int64_t)(64 * c) * a.ldk + pcol;
 #pragma unroll
-            for (int p = 0; p < C::PASSES; ++p) {
-                const int t = min(64 * c + prow + RPP * p, len - 1);
-                ld_raw8(kp + (int64_t)t * a.ldk + pcol, kraw[p]);
-            }
-            const int t = min(64 * c + lane, len - 1);
-            braw = bp[(int64_t)t * a.h_v];
-            araw = ap[(int64_t)t * a.h_v];
+            for (int p = 0; p < C::PASSES; ++p)
+                ld_raw8(kc + __umul24(min(prow + RPP * p, last), (unsigned)a.ldk), kraw[p]);
+            const int tg = min(lane, last);
+            braw = bp[(int64_t)(64 * c) * a.h_v + __umul24(tg, (unsigned)a.h_v)];
+            araw = ap[(int64_t)(64 * c) * a.h_v + __umul24(tg, (unsigned)a.h_v)];
         };
         auto fetch_v = [&](int c) {
+            const int last = len - 1 - 64 * c;
+            const TKV *vc = vp + (int64_t)(64 * c) * a.ldv + pcol;
 #pragma unroll
-            for (int p = 0; p < C::PASSES; ++p) {
-                const int t = min(64 * c + prow + RPP * p, len - 1);
-                ld_raw8(vp + (int64_t)t * a.ldv + pcol, vraw[p]);
-            }
+            for (int p = 0; p < C::PASSES; ++p)
+                ld_raw8(vc + __umul24(min(prow + RPP * p, last), (unsigned)a.ldv), vraw[p]);
         };
         if (nch > 0) { fetch_k(0); fetch_v(0); }
         constexpr int NTW = MT / 4;   // W (and U) column tiles per prep wave
