@@ -393,16 +393,20 @@ build_delta_f16_kernel(const DeltaArgs a)
                 for (int mt = 0; mt < MT; ++mt) X[mt][jn] *= f;
                 sig[jn] = target;
             };
-            auto state_prescale = [&]() {   // chunk gate on S, value-scale catch-up
+            // chunk gate of the next chunk (index it) on S, value-scale catch-up: its
+            // gate and value scale are in LDS from phases 1 and 2 of this iteration,
+            // so this runs at the end of phase 3, after this chunk's update
+            auto state_prescale_next = [&]() {
+                const int bn = it & 1;
 #pragma unroll
                 for (int jn = 0; jn < C::TPW; ++jn) {
                     const int n = C::TPW * w + jn;
                     if (n >= MT) {
-                        const float gbv = sm.gb[bs_];
+                        const float gbv = sm.gb[bn];
 #pragma unroll
                         for (int mt = 0; mt < MT; ++mt) X[mt][jn] *= gbv;
-                        if (cs == 0) sig[jn] = (float)sm.sv[bs_];   // S starts at 0: take the value scale
-                        if ((float)sm.sv[bs_] > sig[jn] + 4.f) renorm(jn, true, (float)sm.sv[bs_]);
+                        if (it == 0) sig[jn] = (float)sm.sv[bn];   // S starts at 0: take the value scale
+                        if ((float)sm.sv[bn] > sig[jn] + 4.f) renorm(jn, true, (float)sm.sv[bn]);
                     }
                 }
             };
@@ -474,10 +478,7 @@ build_delta_f16_kernel(const DeltaArgs a)
                 const int n = C::TPW * w + jn;
                 if ((cs & 3) == 3) renorm(jn, n >= MT, (float)sm.sv[bs_]);
             };
-            if (dos) {
-                state_prescale();
-                state_e_pair(0);
-            }
+            if (dos) state_e_pair(0);
             lds_barrier();
             if (dos) state_e_pair(1);
             lds_barrier();
@@ -486,6 +487,7 @@ build_delta_f16_kernel(const DeltaArgs a)
 #pragma unroll
                 for (int jn = 0; jn < C::TPW; ++jn) state_u(jn);
             }
+            if (it < nch) state_prescale_next();
             lds_barrier();
         }
 
