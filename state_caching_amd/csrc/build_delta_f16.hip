@@ -10,7 +10,7 @@
 //                        lower-triangular inverse M; W = M diag(b) K and
 //                        U = M diag(b dec) V into LDS
 //   state waves (d/32) : chunk c   -- E = U - W Xhat, Xhat += K^T E on the
-//                        wave's four 16-column tiles of X
+//                        wave's four 16-column tiles of X (two of Tbar, two of S)
 //
 // Three LDS barriers per chunk; the state waves spread their matrix work over
 // the phases so the matrix cores stay busy while the prep waves run their
@@ -356,18 +356,22 @@ build_delta_f16_kernel(const DeltaArgs a)
         lds_barrier();
     } else {
         // ----------------------------------------------------------- state state
+        // column tiles of X = [Tbar | S] held by this wave: Tbar tiles 2w, 2w + 1 and S
+        // tiles MT + 2w, MT + 2w + 1 (every state wave carries the same share of the
+        // S-only work: chunk-gate prescale and value terms)
+        auto tile_n = [&](int jn) { return jn < 2 ? 2 * w + jn : MT + 2 * w + jn - 2; };
         f4 X[MT][C::TPW];
         float sig[C::TPW] = {0.f, 0.f, 0.f, 0.f};
         h8 Eb[C::TPW][2];  // E of the four column tiles as fp16 B operands (token blocks 0-31, 32-63)
         {
 #pragma unroll
             for (int jn = 0; jn < C::TPW; ++jn) {
-                const int n = C::TPW * w + jn;
+                const int n = tile_n(jn);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        X[mt][jn][i] = (n < MT && 16 * mt + 4 * g + i == 16 * n + r16) ? 1.f : 0.f;
+                        X[mt][jn][i] = (jn < 2 && 16 * mt + 4 * g + i == 16 * n + r16) ? 1.f : 0.f;
             }
         }
 
@@ -399,9 +403,8 @@ build_delta_f16_kernel(const DeltaArgs a)
             auto state_prescale_next = [&]() {
                 const int bn = it & 1;
 #pragma unroll
-                for (int jn = 0; jn < C::TPW; ++jn) {
-                    const int n = C::TPW * w + jn;
-                    if (n >= MT) {
+                for (int jn = 2; jn < C::TPW; ++jn) {
+                    {
                         const float gbv = sm.gb[bn];
 #pragma unroll
                         for (int mt = 0; mt < MT; ++mt) X[mt][jn] *= gbv;
@@ -416,10 +419,10 @@ build_delta_f16_kernel(const DeltaArgs a)
                 f4 E[2][4];
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    const int jn = 2 * pp + q, n = C::TPW * w + jn;
+                    const int jn = 2 * pp + q, n = tile_n(jn);
 #pragma unroll
                     for (int tj = 0; tj < 4; ++tj) E[q][tj] = zero4();
-                    if (n >= MT) {
+                    if (jn >= 2) {
                         const float usc = exp2f((float)sm.sv[bs_] - sig[jn]);
                         const int cc = 16 * (n - MT) + r16;
 #pragma unroll
@@ -475,8 +478,7 @@ build_delta_f16_kernel(const DeltaArgs a)
                 }
             };
             auto state_u = [&](int jn) {   // periodic renormalisation
-                const int n = C::TPW * w + jn;
-                if ((cs & 3) == 3) renorm(jn, n >= MT, (float)sm.sv[bs_]);
+                if ((cs & 3) == 3) renorm(jn, jn >= 2, (float)sm.sv[bs_]);
             };
             if (dos) state_e_pair(0);
             lds_barrier();
@@ -498,8 +500,8 @@ build_delta_f16_kernel(const DeltaArgs a)
             float *Su = a.S0_out + (int64_t)unit * D * D;
 #pragma unroll
             for (int jn = 0; jn < C::TPW; ++jn) {
-                const int n = C::TPW * w + jn;
-                const bool isS = n >= MT;
+                const int n = tile_n(jn);
+                const bool isS = jn >= 2;
                 const double e = (double)sig[jn] + (isS ? 0.0 : cl_tot);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
