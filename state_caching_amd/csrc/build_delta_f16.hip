@@ -49,7 +49,7 @@ struct F16Smem {
                                  // diagonal block holds A' = b_r k_r.k_s transposed in
                                  // its upper triangle
     float Mi[4][16][20];         // M' = (I + A'_bb)^-1 diag(b_b) per diagonal block, row-major
-    float beta[64], dec[64];     // b_t and dec_t = prod_{s > t} a_s of the chunk in prep
+    float beta[2][64], dec[2][64];   // b_t and dec_t = prod_{s > t} a_s, per pipeline slot
     float gb[2];                 // chunk gate product, per pipeline slot
     int sv[2];                   // value scale exponent, per pipeline slot
     float wmax[4];
@@ -133,7 +133,24 @@ build_delta_f16_kernel(const DeltaArgs a)
             for (int p = 0; p < C::PASSES; ++p)
                 ld_raw8(vc + __umul24(min(prow + RPP * p, last), (unsigned)a.ldv), vraw[p]);
         };
-        if (nch > 0) { fetch_k(0); fetch_v(0); }
+        // gates of chunk c from braw/araw (every prep wave computes them, wave 0
+        // writes them): b, dec, the chunk product; the log-gate total accumulates
+        // when count is set
+        auto gates = [&](int c, bool count) {
+            const int bc = c & 1;
+            const bool gin = 64 * c + lane < len;
+            const float br = gin ? to_f32(braw) : 0.f, ar = gin ? to_f32(araw) : 1.f;
+            const float l2 = log2f(ar);
+            const float sfx = wave_suffix_excl(l2);
+            cl_lane += count ? (double)l2 : 0.0;
+            const float dcv = exp2f(sfx), gbv = exp2f(sfx + l2);
+            if (pw == 0) {
+                sm.beta[bc][lane] = br;
+                sm.dec[bc][lane] = dcv;
+                if (lane == 0) sm.gb[bc] = gbv;
+            }
+        };
+        if (nch > 0) { fetch_k(0); fetch_v(0); gates(0, true); }
         constexpr int NTW = MT / 4;   // W (and U) column tiles per prep wave
         const h4 h4z = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
         h4 Xw[NTW][4], Xu[NTW][4];    // solved row blocks, fp16 B fragments
@@ -146,7 +163,7 @@ build_delta_f16_kernel(const DeltaArgs a)
             const int cp = it;
             constexpr bool dop = true;
             const int bp_ = cp & 1;
-            // ===================== phase 1: stage keys and gates of cp | E of column tiles 0-1
+            // ===================== phase 1: stage keys of cp | E of column tiles 0-1
             if (dop) {
                 float vm = 0.f;
 #pragma unroll
@@ -168,21 +185,6 @@ build_delta_f16_kernel(const DeltaArgs a)
                 }
                 vm = wave_max(vm);
                 if (lane == 0) sm.wmax[pw] = vm;
-                {
-                    // gates: every prep wave computes them (straight-line with the
-                    // staging), wave 0 writes them
-                    const bool gin = 64 * cp + lane < len;
-                    const float br = gin ? to_f32(braw) : 0.f, ar = gin ? to_f32(araw) : 1.f;
-                    const float l2 = log2f(ar);
-                    const float sfx = wave_suffix_excl(l2);
-                    cl_lane += (double)l2;
-                    const float dcv = exp2f(sfx), gbv = exp2f(sfx + l2);
-                    if (pw == 0) {
-                        sm.beta[lane] = br;
-                        sm.dec[lane] = dcv;
-                        if (lane == 0) sm.gb[bp_] = gbv;
-                    }
-                }
                 fetch_k(min(cp + 1, nch - 1));
             }
             lds_barrier();
@@ -199,7 +201,7 @@ build_delta_f16_kernel(const DeltaArgs a)
                         float vx[8];
                         widen8(vraw[p], vx);   // zeroed past the end in phase 1
                         const int t = prow + RPP * p;
-                        const float rsc = vsc * sm.dec[t];
+                        const float rsc = vsc * sm.dec[bp_][t];
                         h8 vv;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) vv[e] = (_Float16)(vx[e] * rsc);
@@ -208,7 +210,8 @@ build_delta_f16_kernel(const DeltaArgs a)
                     fetch_v(min(cp + 1, nch - 1));
                 }
                 // off-diagonal Gram tile q -> (ti, tj): q = 0..5 -> (1,0) (2,0) (2,1) (3,0) (3,1) (3,2);
-                // waves 0-3 take tile pw, waves 2-3 also tile pw + 2
+                // every wave takes tiles pw and pw + 2 (waves 0-1 repeat tiles 2-3 of waves
+                // 2-3 and write the same values), straight-line with the diagonal block
                 auto offdiag = [&](int q) {
                     const int ti = q < 1 ? 1 : (q < 3 ? 2 : 3), tj = q - ti * (ti - 1) / 2;
                     f4 acc = zero4();
@@ -222,6 +225,7 @@ build_delta_f16_kernel(const DeltaArgs a)
                     for (int i = 0; i < 4; ++i) sm.Gm[16 * ti + 4 * g + i][16 * tj + r16] = acc[i];
                 };
                 offdiag(pw);
+                offdiag(pw + 2);
                 {
                     // diagonal block pw: Gram tile, A' = b_r k_r.k_s (s < r) written
                     // transposed into the block's upper triangle (column q of A' is then
@@ -234,7 +238,7 @@ build_delta_f16_kernel(const DeltaArgs a)
                         const h8 A = *reinterpret_cast<const h8 *>(&sm.Ks[bp_][o + r16][32 * kb + 8 * g]);
                         acc = mma(A, A, acc);
                     }
-                    const float4 bq = *reinterpret_cast<const float4 *>(&sm.beta[o + 4 * g]);
+                    const float4 bq = *reinterpret_cast<const float4 *>(&sm.beta[bp_][o + 4 * g]);
                     const float bqv[4] = {bq.x, bq.y, bq.z, bq.w};
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -270,11 +274,10 @@ build_delta_f16_kernel(const DeltaArgs a)
                     }
                     // column c of M' = (I + A')^-1 diag(b) (zero above the diagonal); the
                     // four lane groups hold the same column and write the same values
-                    const float bc = sm.beta[o + c];
+                    const float bc = sm.beta[bp_][o + c];
 #pragma unroll
                     for (int r = 0; r < 16; ++r) sm.Mi[pw][r][c] = x[r] * bc;
                 }
-                if (pw >= 2) offdiag(pw + 2);
             }
             lds_barrier();
             // ===================== phase 3: W and U of chunk cp | update
@@ -344,6 +347,9 @@ build_delta_f16_kernel(const DeltaArgs a)
                 }
             };
             if (dop) { subst_row(0); subst_row(1); subst_row(2); subst_row(3); }
+            // gates of the next chunk (its gate loads went out in phase 1); the last
+            // iteration recomputes its own rows into the idle slot
+            gates(cp + 1, cp + 1 < nch);
             lds_barrier();
         }
 #pragma unroll
@@ -397,20 +403,15 @@ build_delta_f16_kernel(const DeltaArgs a)
                 for (int mt = 0; mt < MT; ++mt) X[mt][jn] *= f;
                 sig[jn] = target;
             };
-            // chunk gate of the next chunk (index it) on S, value-scale catch-up: its
-            // gate and value scale are in LDS from phases 1 and 2 of this iteration,
-            // so this runs at the end of phase 3, after this chunk's update
-            auto state_prescale_next = [&]() {
-                const int bn = it & 1;
+            // chunk gate on the S tiles, value-scale catch-up (before their E in phase 2)
+            auto state_prescale = [&]() {
 #pragma unroll
                 for (int jn = 2; jn < C::TPW; ++jn) {
-                    {
-                        const float gbv = sm.gb[bn];
+                    const float gbv = sm.gb[bs_];
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) X[mt][jn] *= gbv;
-                        if (it == 0) sig[jn] = (float)sm.sv[bn];   // S starts at 0: take the value scale
-                        if ((float)sm.sv[bn] > sig[jn] + 4.f) renorm(jn, true, (float)sm.sv[bn]);
-                    }
+                    for (int mt = 0; mt < MT; ++mt) X[mt][jn] *= gbv;
+                    if (cs == 0) sig[jn] = (float)sm.sv[bs_];   // S starts at 0: take the value scale
+                    if ((float)sm.sv[bs_] > sig[jn] + 4.f) renorm(jn, true, (float)sm.sv[bs_]);
                 }
             };
             // E = U 2^(sv - sig) - W Xhat for the column tiles {2 pp, 2 pp + 1}, all 64
@@ -482,14 +483,16 @@ build_delta_f16_kernel(const DeltaArgs a)
             };
             if (dos) state_e_pair(0);
             lds_barrier();
-            if (dos) state_e_pair(1);
+            if (dos) {
+                state_prescale();
+                state_e_pair(1);
+            }
             lds_barrier();
             if (dos) {
                 state_u4(0, MT);
 #pragma unroll
                 for (int jn = 0; jn < C::TPW; ++jn) state_u(jn);
             }
-            if (it < nch) state_prescale_next();
             lds_barrier();
         }
 
