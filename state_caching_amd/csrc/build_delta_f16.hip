@@ -49,6 +49,9 @@ struct F16Smem {
                                  // diagonal block holds A' = b_r k_r.k_s transposed in
                                  // its upper triangle
     float Mi[4][16][20];         // M' = (I + A'_bb)^-1 diag(b_b) per diagonal block, row-major
+    // 2x2 blocked inverse of each diagonal block (per prep wave): A21 row-major,
+    // M11 transposed, M22 row-major, Y = A21 M11 transposed
+    float A21s[4][8][12], M11t[4][8][12], M22s[4][8][12], Yt[4][8][12];
     float beta[2][64], dec[2][64];   // b_t and dec_t = prod_{s > t} a_s, per pipeline slot
     float gb[2];                 // chunk gate product, per pipeline slot
     int sv[2];                   // value scale exponent, per pipeline slot
@@ -243,40 +246,64 @@ build_delta_f16_kernel(const DeltaArgs a)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int rr = 4 * g + i;   // A'[rr][r16] for r16 < rr, stored at [r16][rr]
-                        if (r16 < rr) sm.Gm[o + r16][o + rr] = bqv[i] * acc[i];
+                        const float av = bqv[i] * acc[i];
+                        if (r16 < rr) sm.Gm[o + r16][o + rr] = av;
+                        if (rr >= 8 && r16 < 8) sm.A21s[pw][rr - 8][r16] = av;   // A21 row-major
                     }
-                    const int c = r16;   // (LDS operations of a wave complete in order)
-                    float x[16];
+                    // (I + A')^-1 = [[M11, 0], [M21, M22]]: M11, M22 by forward substitution
+                    // on the 8x8 diagonal halves, side by side (lane column c = r16: c < 8 a
+                    // column of M11, c >= 8 one of M22; the four lane groups repeat it),
+                    // then M21 = -M22 A21 M11 with one entry per lane.  LDS operations of a
+                    // wave complete in order.
+                    const int c = r16, bb = c & 8, cl = c & 7;
+                    float x[8];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
-                    // column q of A' (its entries r > q) rides a ring of four rows, loaded
-                    // four steps ahead; only the float4 pieces holding some r > q
-                    float4 ring[4][4];
-                    auto load_col = [&](int q, float4 (&dst)[4]) {
+                    for (int r = 0; r < 8; ++r) x[r] = (r == cl) ? 1.f : 0.f;
+                    float4 col[7][2];   // columns q of the half (rows q+1 .. 7 used)
 #pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            if (4 * v + 3 > q) dst[v] = *reinterpret_cast<const float4 *>(&sm.Gm[o + q][o + 4 * v]);
-                    };
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) load_col(q, ring[q]);
-#pragma unroll
-                    for (int q = 0; q < 15; ++q) {
-                        const float4 *cur = ring[q % 4];
-                        float colv[16];
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            colv[4 * v] = cur[v].x; colv[4 * v + 1] = cur[v].y;
-                            colv[4 * v + 2] = cur[v].z; colv[4 * v + 3] = cur[v].w;
-                        }
-#pragma unroll
-                        for (int r = q + 1; r < 16; ++r) x[r] -= colv[r] * x[q];
-                        if (q + 4 < 15) load_col(q + 4, ring[q % 4]);
+                    for (int q = 0; q < 7; ++q) {
+                        col[q][0] = *reinterpret_cast<const float4 *>(&sm.Gm[o + bb + q][o + bb]);
+                        col[q][1] = *reinterpret_cast<const float4 *>(&sm.Gm[o + bb + q][o + bb + 4]);
                     }
-                    // column c of M' = (I + A')^-1 diag(b) (zero above the diagonal); the
-                    // four lane groups hold the same column and write the same values
+#pragma unroll
+                    for (int q = 0; q < 7; ++q) {
+                        const float cv[8] = {col[q][0].x, col[q][0].y, col[q][0].z, col[q][0].w,
+                                             col[q][1].x, col[q][1].y, col[q][1].z, col[q][1].w};
+#pragma unroll
+                        for (int r = q + 1; r < 8; ++r) x[r] -= cv[r] * x[q];
+                    }
+                    if (c < 8) {
+                        *reinterpret_cast<float4 *>(&sm.M11t[pw][c][0]) = make_float4(x[0], x[1], x[2], x[3]);
+                        *reinterpret_cast<float4 *>(&sm.M11t[pw][c][4]) = make_float4(x[4], x[5], x[6], x[7]);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 8; ++r) sm.M22s[pw][r][cl] = x[r];
+                    }
+                    // Y = A21 M11, entry (yr, yc) per lane
+                    const int yr = lane >> 3, yc = lane & 7;
+                    const float4 a0 = *reinterpret_cast<const float4 *>(&sm.A21s[pw][yr][0]);
+                    const float4 a1 = *reinterpret_cast<const float4 *>(&sm.A21s[pw][yr][4]);
+                    const float4 m0 = *reinterpret_cast<const float4 *>(&sm.M11t[pw][yc][0]);
+                    const float4 m1 = *reinterpret_cast<const float4 *>(&sm.M11t[pw][yc][4]);
+                    const float yv = a0.x * m0.x + a0.y * m0.y + a0.z * m0.z + a0.w * m0.w +
+                                     a1.x * m1.x + a1.y * m1.y + a1.z * m1.z + a1.w * m1.w;
+                    sm.Yt[pw][yc][yr] = yv;
+                    // M21 = -M22 Y
+                    const float4 p0 = *reinterpret_cast<const float4 *>(&sm.M22s[pw][yr][0]);
+                    const float4 p1 = *reinterpret_cast<const float4 *>(&sm.M22s[pw][yr][4]);
+                    const float4 y0 = *reinterpret_cast<const float4 *>(&sm.Yt[pw][yc][0]);
+                    const float4 y1 = *reinterpret_cast<const float4 *>(&sm.Yt[pw][yc][4]);
+                    const float m21 = -(p0.x * y0.x + p0.y * y0.y + p0.z * y0.z + p0.w * y0.w +
+                                        p1.x * y1.x + p1.y * y1.y + p1.z * y1.z + p1.w * y1.w);
+                    // M' = (I + A')^-1 diag(b): column c (rows 0-7 M11 or zero, rows 8-15
+                    // zero or M22), and M21 entry (8 + yr, yc)
                     const float bc = sm.beta[bp_][o + c];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) sm.Mi[pw][r][c] = x[r] * bc;
+                    for (int r = 0; r < 8; ++r) {
+                        sm.Mi[pw][r][c] = c < 8 ? x[r] * bc : 0.f;
+                        if (c >= 8) sm.Mi[pw][8 + r][c] = x[r] * bc;
+                    }
+                    sm.Mi[pw][8 + yr][yc] = m21 * sm.beta[bp_][o + yc];
                 }
             }
             lds_barrier();
