@@ -6,11 +6,13 @@
 // X = [Tbar | S] through chunks of 64 tokens), organised as a two-stage
 // software pipeline inside one workgroup per (segment, value head):
 //
-//   prep waves  (4)    : chunk c+1 -- stage K, V, gates; Gram K K^T; the unit
-//                        lower-triangular inverse M; W = M diag(b) K and
-//                        U = M diag(b dec) V into LDS
+//   prep waves  (4)    : chunk c+1 -- stage K, V, gates; diagonal Gram blocks and
+//                        their inverses; W = M diag(b) K and U = M diag(b dec) V
+//                        into LDS
 //   state waves (d/32) : chunk c   -- E = U - W Xhat, Xhat += K^T E on the
-//                        wave's four 16-column tiles of X (two of Tbar, two of S)
+//                        wave's four 16-column tiles of X (two of Tbar, two of S);
+//                        the off-diagonal Gram tiles of chunk c+1 (matrix work the
+//                        prep waves hand over)
 //
 // Three LDS barriers per chunk; the state waves spread their matrix work over
 // the phases so the matrix cores stay busy while the prep waves run their
@@ -191,7 +193,7 @@ build_delta_f16_kernel(const DeltaArgs a)
                 fetch_k(min(cp + 1, nch - 1));
             }
             lds_barrier();
-            // ===================== phase 2: V^, Gram, diagonal inverses | E of column tiles 2-3
+            // ===================== phase 2: V^, diagonal Gram blocks and inverses | off-diagonal Gram, E of column tiles 2-3
             if (dop) {
                 // value scale of chunk cp; V^ = diag(dec) V * 2^-sv into Vs
                 {
@@ -212,23 +214,6 @@ build_delta_f16_kernel(const DeltaArgs a)
                     }
                     fetch_v(min(cp + 1, nch - 1));
                 }
-                // off-diagonal Gram tile q -> (ti, tj): q = 0..5 -> (1,0) (2,0) (2,1) (3,0) (3,1) (3,2);
-                // every wave takes tiles pw and pw + 2 (waves 0-1 repeat tiles 2-3 of waves
-                // 2-3 and write the same values), straight-line with the diagonal block
-                auto offdiag = [&](int q) {
-                    const int ti = q < 1 ? 1 : (q < 3 ? 2 : 3), tj = q - ti * (ti - 1) / 2;
-                    f4 acc = zero4();
-#pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) {
-                        const h8 A = *reinterpret_cast<const h8 *>(&sm.Ks[bp_][16 * ti + r16][32 * kb + 8 * g]);
-                        const h8 B = *reinterpret_cast<const h8 *>(&sm.Ks[bp_][16 * tj + r16][32 * kb + 8 * g]);
-                        acc = mma(A, B, acc);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sm.Gm[16 * ti + 4 * g + i][16 * tj + r16] = acc[i];
-                };
-                offdiag(pw);
-                offdiag(pw + 2);
                 {
                     // diagonal block pw: Gram tile, A' = b_r k_r.k_s (s < r) written
                     // transposed into the block's upper triangle (column q of A' is then
@@ -508,8 +493,27 @@ build_delta_f16_kernel(const DeltaArgs a)
             auto state_u = [&](int jn) {   // periodic renormalisation
                 if ((cs & 3) == 3) renorm(jn, jn >= 2, (float)sm.sv[bs_]);
             };
+            // the off-diagonal Gram tiles G_ij = K_i K_j^T of the prep waves' chunk it
+            // (staged in its phase 1, used by its phase 3): tile q -> (ti, tj), q = 0..5 ->
+            // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2); state wave w takes q = w, w + NS, ...
+            auto offdiag = [&](int q) {
+                const int bp = it & 1;
+                const int ti = q < 1 ? 1 : (q < 3 ? 2 : 3), tj = q - ti * (ti - 1) / 2;
+                f4 acc = zero4();
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const h8 A = *reinterpret_cast<const h8 *>(&sm.Ks[bp][16 * ti + r16][32 * kb + 8 * g]);
+                    const h8 B = *reinterpret_cast<const h8 *>(&sm.Ks[bp][16 * tj + r16][32 * kb + 8 * g]);
+                    acc = mma(A, B, acc);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.Gm[16 * ti + 4 * g + i][16 * tj + r16] = acc[i];
+            };
             if (dos) state_e_pair(0);
             lds_barrier();
+            if (it < nch) {
+                for (int q = w; q < 6; q += NS) offdiag(q);
+            }
             if (dos) {
                 state_prescale();
                 state_e_pair(1);
