@@ -127,11 +127,11 @@ __global__ void __launch_bounds__((CsCfg<D, SEAMS>::NT)) compose_split_kernel(co
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         Sown[i] = a.S_in ? a.S_in[hoff + (int64_t)(row0 + 4 * g + i) * D + c0 + r16] : 0.f;
+    uint2 own_hi, own_lo;   // the split of the own rows last put into LDS
     auto put_state = [&](int buf, const f4 &x) {   // own rows, split, into the LDS block
-        uint2 hi, lo;
-        split4p(x[0], x[1], x[2], x[3], hi, lo);
-        *reinterpret_cast<uint2 *>(&sm.SH[buf][r16][row0 + 4 * g]) = hi;
-        *reinterpret_cast<uint2 *>(&sm.SL[buf][r16][row0 + 4 * g]) = lo;
+        split4p(x[0], x[1], x[2], x[3], own_hi, own_lo);
+        *reinterpret_cast<uint2 *>(&sm.SH[buf][r16][row0 + 4 * g]) = own_hi;
+        *reinterpret_cast<uint2 *>(&sm.SL[buf][r16][row0 + 4 * g]) = own_lo;
     };
 
     // ---- register ring of T rows and S0 rows ---------------------------------
@@ -246,21 +246,22 @@ __global__ void __launch_bounds__((CsCfg<D, SEAMS>::NT)) compose_split_kernel(co
             hw[st] = pos >= 1;
         };
         // this wave's part of W S from its own rows (masked beyond the window)
+        // this wave's part of W S from its own rows (masked beyond the window), with
+        // the split of the own rows made when they were put into LDS
         auto part_p = [&](int st, int buf) {
             const bool m = wrow && hw[st];
             const float wx[4] = {m ? Wv[st].x : 0.f, m ? Wv[st].y : 0.f, m ? Wv[st].z : 0.f, m ? Wv[st].w : 0.f};
-            const float sx[4] = {Sown[0], Sown[1], Sown[2], Sown[3]};
-            b8 ah, al, bh, bl;
+            b8 ah, al;
             split4z(wx, ah, al);
-            split4z(sx, bh, bl);
+            const b8 bh = __builtin_bit_cast(b8, make_uint4(own_hi.x, own_hi.y, 0u, 0u));
+            const b8 bl = __builtin_bit_cast(b8, make_uint4(own_lo.x, own_lo.y, 0u, 0u));
             sm.Ppart[buf][wv][lane] = mma3(ah, al, bh, bl, zero4());
         };
         // the window's keys, split, into LDS buffer buf (rows >= w zero)
         auto stage_k = [&](int st, int buf) {
             const bool m = ktok && hw[st];
-            const float kx[4] = {m ? Kg[st].x : 0.f, m ? Kg[st].y : 0.f, m ? Kg[st].z : 0.f, m ? Kg[st].w : 0.f};
             uint2 hi, lo;
-            split4p(kx[0], kx[1], kx[2], kx[3], hi, lo);
+            split4p(m ? Kg[st].x : 0.f, m ? Kg[st].y : 0.f, m ? Kg[st].z : 0.f, m ? Kg[st].w : 0.f, hi, lo);
             *reinterpret_cast<uint2 *>(&sm.KH[buf][kt][kd]) = hi;
             *reinterpret_cast<uint2 *>(&sm.KL[buf][kt][kd]) = lo;
         };
