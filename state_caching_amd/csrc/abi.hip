@@ -73,6 +73,7 @@ hypic_status validate_build(const hypic_build_desc *d)
     if (!aligned16(d->k) || !aligned16(d->v) || !aligned16(d->T_out) || !aligned16(d->S0_out))
         return HYPIC_E_INVALID;
     if (d->conv_w > 0 && (!d->conv_from || !d->conv_wk || !d->conv_wv)) return HYPIC_E_INVALID;
+    if (d->conv_w > 0 && (!aligned16(d->conv_wk) || !aligned16(d->conv_wv))) return HYPIC_E_INVALID;
     for (int s = 0; s < d->n_seg; ++s) {
         if (d->seg_start[s] < 0 || d->seg_len[s] < 0 || d->seg_len[s] > INT32_MAX) return HYPIC_E_INVALID;
         if (d->conv_w > 0 && (d->conv_from[s] < 0 || d->conv_from[s] > d->seg_start[s])) return HYPIC_E_INVALID;
@@ -170,12 +171,17 @@ hypic_status hypic_segment_build(const hypic_build_desc *d, void *ws, size_t ws_
     const int D = d->d_k;
     const int in_kind = d->in_dtype == HYPIC_BF16 ? IN_BF16 : IN_F32;
     const bool prep = build_needs_prep(d);
-    float *wk = nullptr, *wvv = nullptr;
+    // the fp16-operand build (bf16 inputs, d >= 64) takes fp16 keys from the conv
+    const bool khalf = prep && d->in_dtype == HYPIC_BF16 && D >= 64 && d->rule == HYPIC_RULE_DELTA;
+    float *wk = nullptr, *wvv = nullptr, *wvs = nullptr;
     if (prep) {
         const int64_t rows = build_rows(d);
         wk = static_cast<float *>(ws);
         const size_t kb = (size_t)rows * d->h_k * D * sizeof(float);
         wvv = reinterpret_cast<float *>(static_cast<char *>(ws) + ((kb + 255) & ~(size_t)255));
+        // fp16 value rows take the first half of the value region, their factors the
+        // second half
+        wvs = wvv + ((size_t)rows * d->h_v * D / 2);
     }
     int64_t packed = 0;
     for (int s0 = 0; s0 < d->n_seg; s0 += kMaxSeg) {
@@ -209,20 +215,30 @@ hypic_status hypic_segment_build(const hypic_build_desc *d, void *ws, size_t ws_
                     c.out0[i] = a.tok0[i] - packed;
                     c.len[i] = a.len[i];
                 }
-                c.x = d->k; c.w = d->conv_wk; c.out = wk + packed * d->h_k * D; c.H = d->h_k;
+                // for the fp16-operand build the rows go out in fp16 (normalised keys;
+                // value rows divided by a power of two each, kept beside them), which
+                // that build rounds its operands to anyway; fp32 otherwise
+                c.x = d->k; c.w = d->conv_wk; c.H = d->h_k; c.scale = nullptr;
+                c.out = khalf ? static_cast<void *>(reinterpret_cast<_Float16 *>(wk) + packed * d->h_k * D)
+                              : static_cast<void *>(wk + packed * d->h_k * D);
                 c.l2norm = d->k_l2norm;
-                if ((st = from_hip(launch_conv(c, D, in_kind, rows_b, hs))) != HYPIC_OK) return st;
-                c.x = d->v; c.w = d->conv_wv; c.out = wvv + packed * d->h_v * D; c.H = d->h_v;
+                if ((st = from_hip(launch_conv(c, D, in_kind, khalf, rows_b, hs))) != HYPIC_OK) return st;
+                c.x = d->v; c.w = d->conv_wv; c.H = d->h_v;
+                c.out = khalf ? static_cast<void *>(reinterpret_cast<_Float16 *>(wvv) + packed * d->h_v * D)
+                              : static_cast<void *>(wvv + packed * d->h_v * D);
+                c.scale = khalf ? wvs + packed * d->h_v : nullptr;
                 c.l2norm = 0;
-                if ((st = from_hip(launch_conv(c, D, in_kind, rows_b, hs))) != HYPIC_OK) return st;
-                a.k = wk; a.v = wvv;
+                if ((st = from_hip(launch_conv(c, D, in_kind, khalf, rows_b, hs))) != HYPIC_OK) return st;
+                a.k = khalf ? static_cast<const void *>(reinterpret_cast<_Float16 *>(wk)) : wk;
+                a.v = khalf ? static_cast<const void *>(reinterpret_cast<_Float16 *>(wvv)) : wvv;
+                a.vscale = khalf ? wvs : nullptr;
                 a.ldk = (int64_t)d->h_k * D; a.ldv = (int64_t)d->h_v * D;
                 packed += rows_b;
             } else {
                 a.k = d->k; a.v = d->v;
                 a.ldk = (int64_t)d->h_k * D; a.ldv = (int64_t)d->h_v * D;
             }
-            const int kv_kind = prep ? IN_F32 : in_kind;
+            const int kv_kind = khalf ? IN_F16K : (prep ? IN_F32 : in_kind);
             st = from_hip(launch_build_delta(a, D, kv_kind, in_kind, d->in_dtype == HYPIC_BF16,
                                              nb * d->h_v, hs));
         } else {

@@ -19,6 +19,8 @@
 // latency-bound steps.  Xhat is kept in power-of-two units per
 // column tile (renormalised every 4 chunks, or when the value scale runs
 // ahead of the state), so every computed fp16 operand stays in range.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -78,7 +80,7 @@ __device__ __forceinline__ h4 ld_tr4(const _Float16 *S, int ld, int k0, int x0, 
 __device__ __forceinline__ h8 cat8(h4 lo, h4 hi) { return h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}; }
 
 
-template <int D, typename TKV, typename TG>
+template <int D, typename TK, typename TV, typename TG>
 __global__ void __launch_bounds__((F16Cfg<D>::NT))
 build_delta_f16_kernel(const DeltaArgs a)
 {
@@ -108,11 +110,16 @@ build_delta_f16_kernel(const DeltaArgs a)
         constexpr int CPR = D / 8;
         const int prow = (ptid >= 0 ? ptid : 0) / CPR, pcol = 8 * ((ptid >= 0 ? ptid : 0) % CPR);
         constexpr int RPP = 256 / CPR;             // rows per pass
-        const TKV *kp = reinterpret_cast<const TKV *>(a.k) + a.tok0[s] * a.ldk + (int64_t)kh * D;
-        const TKV *vp = reinterpret_cast<const TKV *>(a.v) + a.tok0[s] * a.ldv + (int64_t)h * D;
+        const TK *kp = reinterpret_cast<const TK *>(a.k) + a.tok0[s] * a.ldk + (int64_t)kh * D;
+        const TV *vp = reinterpret_cast<const TV *>(a.v) + a.tok0[s] * a.ldv + (int64_t)h * D;
         const TG *bp = reinterpret_cast<const TG *>(a.beta) + a.gtok0[s] * a.h_v + h;
         const TG *ap = reinterpret_cast<const TG *>(a.alpha) + a.gtok0[s] * a.h_v + h;
-        typename Raw8<TKV>::type kraw[C::PASSES], vraw[C::PASSES];
+        typename Raw8<TK>::type kraw[C::PASSES];
+        typename Raw8<TV>::type vraw[C::PASSES];
+        // fp16 value rows from the conv carry a power-of-two factor per (row, head)
+        constexpr bool VSC = std::is_same<TV, _Float16>::value;
+        float vrs[C::PASSES];
+        const float *vsp = VSC ? a.vscale + a.tok0[s] * a.h_v + h : nullptr;
         double cl_lane = 0.0;
         // Prefetches are straight-line loads of rows clamped into the segment (rows
         // past its end are zeroed when staged), so the compiler's load waits stay
@@ -123,7 +130,7 @@ build_delta_f16_kernel(const DeltaArgs a)
         // multiplies
         auto fetch_k = [&](int c) {
             const int last = len - 1 - 64 * c;   // >= 0 for every chunk of the segment
-            const TKV *kc = kp + (int64_t)(64 * c) * a.ldk + pcol;
+            const TK *kc = kp + (int64_t)(64 * c) * a.ldk + pcol;
 #pragma unroll
             for (int p = 0; p < C::PASSES; ++p)
                 ld_raw8(kc + __umul24(min(prow + RPP * p, last), (unsigned)a.ldk), kraw[p]);
@@ -133,10 +140,14 @@ build_delta_f16_kernel(const DeltaArgs a)
         };
         auto fetch_v = [&](int c) {
             const int last = len - 1 - 64 * c;
-            const TKV *vc = vp + (int64_t)(64 * c) * a.ldv + pcol;
+            const TV *vc = vp + (int64_t)(64 * c) * a.ldv + pcol;
 #pragma unroll
-            for (int p = 0; p < C::PASSES; ++p)
-                ld_raw8(vc + __umul24(min(prow + RPP * p, last), (unsigned)a.ldv), vraw[p]);
+            for (int p = 0; p < C::PASSES; ++p) {
+                const int r = min(prow + RPP * p, last);
+                ld_raw8(vc + __umul24(r, (unsigned)a.ldv), vraw[p]);
+                if constexpr (VSC) vrs[p] = vsp[(int64_t)(64 * c) * a.h_v + __umul24(r, (unsigned)a.h_v)];
+                else vrs[p] = 1.f;
+            }
         };
         // gates of chunk c from braw/araw (every prep wave computes them, wave 0
         // writes them): b, dec, the chunk product; the log-gate total accumulates
@@ -181,11 +192,13 @@ build_delta_f16_kernel(const DeltaArgs a)
                     widen8(kraw[p], kx);
                     widen8(vraw[p], vx);
                     h8 kk;
+                    float pm = 0.f;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         kk[e] = (_Float16)kx[e];
-                        vm = fmaxf(vm, fabsf(vx[e]));
+                        pm = fmaxf(pm, fabsf(vx[e]));
                     }
+                    vm = fmaxf(vm, VSC ? pm * vrs[p] : pm);
                     *reinterpret_cast<h8 *>(&sm.Ks[bp_][t][pcol]) = kk;
                 }
                 vm = wave_max(vm);
@@ -206,7 +219,7 @@ build_delta_f16_kernel(const DeltaArgs a)
                         float vx[8];
                         widen8(vraw[p], vx);   // zeroed past the end in phase 1
                         const int t = prow + RPP * p;
-                        const float rsc = vsc * sm.dec[bp_][t];
+                        const float rsc = vsc * sm.dec[bp_][t] * (VSC ? vrs[p] : 1.f);
                         h8 vv;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) vv[e] = (_Float16)(vx[e] * rsc);
@@ -551,33 +564,33 @@ build_delta_f16_kernel(const DeltaArgs a)
     }
 }
 
-template <int D, typename TKV, typename TG>
+template <int D, typename TK, typename TV, typename TG>
 hipError_t launch_f16_one(const DeltaArgs &a, int n_units, hipStream_t st)
 {
     const size_t smem = sizeof(F16Smem<D>);
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&build_delta_f16_kernel<D, TKV, TG>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&build_delta_f16_kernel<D, TK, TV, TG>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;
         attr = true;
     }
-    hipLaunchKernelGGL((build_delta_f16_kernel<D, TKV, TG>), dim3(n_units), dim3(F16Cfg<D>::NT), smem, st, a);
+    hipLaunchKernelGGL((build_delta_f16_kernel<D, TK, TV, TG>), dim3(n_units), dim3(F16Cfg<D>::NT), smem, st, a);
     return hipGetLastError();
 }
 
+// bf16 inputs (keys, values and gates), or the conv workspace of a bf16-input
+// build (fp16 keys, fp16 values with a power of two per row) with bf16 gates
 hipError_t launch_build_delta_f16(const DeltaArgs &a, int D, int kv_kind, int g_kind, int n_units,
                                   hipStream_t st)
 {
-    const bool kvb = kv_kind == IN_BF16, gbf = g_kind == IN_BF16;
+    if (g_kind != IN_BF16) return hipErrorInvalidValue;
     if (D == 128) {
-        if (kvb && gbf) return launch_f16_one<128, bf16_t, bf16_t>(a, n_units, st);
-        if (!kvb && gbf) return launch_f16_one<128, float, bf16_t>(a, n_units, st);
-        if (!kvb && !gbf) return launch_f16_one<128, float, float>(a, n_units, st);
+        if (kv_kind == IN_BF16) return launch_f16_one<128, bf16_t, bf16_t, bf16_t>(a, n_units, st);
+        if (kv_kind == IN_F16K) return launch_f16_one<128, _Float16, _Float16, bf16_t>(a, n_units, st);
     } else if (D == 64) {
-        if (kvb && gbf) return launch_f16_one<64, bf16_t, bf16_t>(a, n_units, st);
-        if (!kvb && gbf) return launch_f16_one<64, float, bf16_t>(a, n_units, st);
-        if (!kvb && !gbf) return launch_f16_one<64, float, float>(a, n_units, st);
+        if (kv_kind == IN_BF16) return launch_f16_one<64, bf16_t, bf16_t, bf16_t>(a, n_units, st);
+        if (kv_kind == IN_F16K) return launch_f16_one<64, _Float16, _Float16, bf16_t>(a, n_units, st);
     }
     return hipErrorInvalidValue;
 }

@@ -61,10 +61,21 @@ __device__ __forceinline__ void ld8(const float *p, float (&x)[8]) {
 // Raw 8-element vectors as loaded from global memory; widened when staged,
 // so a register prefetch does not wait for its data at the load.
 struct raw8_bf16 { uint4 u; };
+struct raw8_f16 { uint4 u; };
 struct raw8_f32 { float4 a, b; };
 template <typename T> struct Raw8;
 template <> struct Raw8<bf16_t> { typedef raw8_bf16 type; };
+template <> struct Raw8<_Float16> { typedef raw8_f16 type; };
 template <> struct Raw8<float> { typedef raw8_f32 type; };
+__device__ __forceinline__ void ld_raw8(const _Float16 *p, raw8_f16 &r) { r.u = *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void mask_raw8(raw8_f16 &r, bool keep) {
+    r.u = make_uint4(keep ? r.u.x : 0u, keep ? r.u.y : 0u, keep ? r.u.z : 0u, keep ? r.u.w : 0u);
+}
+__device__ __forceinline__ void widen8(const raw8_f16 &r, float (&x)[8]) {
+    const h8 v = __builtin_bit_cast(h8, r.u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+}
 
 __device__ __forceinline__ void ld_raw8(const bf16_t *p, raw8_bf16 &r) { r.u = *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ void ld_raw8(const float *p, raw8_f32 &r) {

@@ -11,7 +11,12 @@ namespace hy {
 constexpr int kMaxSeg = HYPIC_MAX_SEG_PER_LAUNCH;
 
 // Input element kinds of a launch.
-enum InKind : int { IN_F32 = 0, IN_BF16 = 1 };
+enum InKind : int {
+    IN_F32 = 0,
+    IN_BF16 = 1,
+    IN_F16K = 2,   // keys fp16, values fp16 times a power of two per (row, head)
+                   // (conv workspace of the fp16-operand build)
+};
 
 // Chunkwise gated-delta build, one workgroup per (segment, value head).
 struct DeltaArgs {
@@ -20,6 +25,7 @@ struct DeltaArgs {
     float *T_out, *S0_out;      // at the launch's first segment
     int h_k, h_v;
     int64_t ldk, ldv;           // row strides of k and v in elements
+    const float *vscale;        // IN_F16K: [rows, h_v] power-of-two factor of each value row
     int n_seg;
     int64_t tok0[kMaxSeg];      // first row of each range in k / v
     int64_t gtok0[kMaxSeg];     // first row of each range in beta / alpha
@@ -43,7 +49,9 @@ struct DecayArgs {
 struct ConvArgs {
     const void *x;              // [N, H, D] raw rows
     const float *w;             // [H*D, W]
-    float *out;                 // packed [sum len, H, D]
+    void *out;                  // packed [sum len, H, D], fp32 or fp16 (out_kind)
+    float *scale;               // null, or [sum len, H]: fp16 rows are stored divided by this
+                                // power of two (their max |y| then lies in [0.5, 1))
     int H, W, l2norm;
     int n_seg;
     int64_t tok0[kMaxSeg];      // first row of each range
@@ -80,7 +88,7 @@ hipError_t launch_build_delta_f16(const DeltaArgs &a, int D, int kv_kind, int g_
                                   hipStream_t st);
 hipError_t launch_build_decay(const DecayArgs &a, int D, int in_kind, int n_units,
                               hipStream_t st);
-hipError_t launch_conv(const ConvArgs &a, int D, int in_kind, int64_t total_rows,
+hipError_t launch_conv(const ConvArgs &a, int D, int in_kind, bool out_f16, int64_t total_rows,
                        hipStream_t st);
 hipError_t launch_compose(const ComposeArgs &a, int D, int tform, int prec, int in_kind,
                           hipStream_t st);
