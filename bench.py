@@ -205,7 +205,7 @@ def main():
 
     if args.leg in ("build", "all"):
         log("generating the 32k-token cold prompt (8 x 4096, 32/16 heads, d=128, bf16)")
-        wl3 = synth.config(3)
+        wl3 = synth.workload("gdn_gqa_d128_8x4096_bf16")
         dw3 = DeviceWorkload(wl3, dev)
         T = torch.empty((wl3.n_seg, wl3.h_v, 128, 128), dtype=torch.float32, device=dev)
         S0 = torch.empty_like(T)
@@ -234,10 +234,10 @@ def main():
                                    "inputs, fp32 pairs: build all (segment, head) pairs then compose",
                        "segments": wl3.n_seg, "seg_len": 4096, "h_v": wl3.h_v, "h_k": wl3.h_k,
                        "d": 128, "in_dtype": "bf16"},
-            "roofline": {"bound": "mfma", "kernel": "build_delta_f16_kernel<128,bf16,bf16>",
+            "roofline": {"bound": "mfma", "kernel": "build_delta_f16_kernel<128,bf16,bf16,bf16>",
                          "achieved": ach, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
                          "frac": ach / PEAK_MFMA_F16,
-                         "traffic": counter_traffic(["build_delta_f16_kernel"], "cfg3"),
+                         "traffic": counter_traffic(["build_delta_f16_kernel"], "gdn_32k_prompt"),
                          "kernel_ms": kb, "algorithmic_flop": fl,
                          "algorithmic_bytes": build_bytes(wl3)},
             "build_tokens_per_s": wl3.n_tokens / (kb * 1e-3),
@@ -249,7 +249,7 @@ def main():
 
     if args.leg in ("compose", "all"):
         log("generating the 100 x 1024-token prompt with conv and seams (32 heads, d=128, bf16)")
-        wl4 = synth.config(4)
+        wl4 = synth.workload("gdn_d128_32h_100x1024_seams_bf16")
         dw4 = DeviceWorkload(wl4, dev)
         T4, S04 = dw4.build()          # pre-built pairs (not timed)
         S4 = torch.empty((wl4.h_v, 128, 128), dtype=torch.float32, device=dev)
@@ -276,7 +276,7 @@ def main():
                              "kernel": "hypic_compose = seam_ops_kernel<128> + compose_split_kernel<128,seams>",
                              "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
                              "frac": gbs / PEAK_HBM,
-                             "traffic": counter_traffic(["seam_ops_kernel", "compose_split_kernel"], "cfg4"),
+                             "traffic": counter_traffic(["seam_ops_kernel", "compose_split_kernel"], "gdn_100_segments_seams"),
                              "algorithmic_bytes": by,
                              "mfma_tflops": compose_flops(wl4) / (k4 * 1e-3) / 1e12}}
         out["compose"] = comp
@@ -287,7 +287,7 @@ def main():
 
     if not args.no_cpu:
         log("timing the fp64 oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(synth.config(3))
+        out["cpu_baseline"] = cpu_baseline(synth.workload("gdn_gqa_d128_8x4096_bf16"))
     print(json.dumps(out), flush=True)
 
 

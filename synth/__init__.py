@@ -181,36 +181,30 @@ def gla(seed, seg_len, h, d, dtype=torch.bfloat16, literal=True, name="gla"):
                     gate=_round(g, dtype), seed=seed)
 
 
-def config(i: int) -> Workload:
-    """The five reference workloads (seed = index)."""
-    if i == 0:
-        w = gdn(0, [64, 64], 1, 1, 16, torch.float32, name="cfg0-gdn-d16-2x64-fp32")
-    elif i == 1:
-        w = retnet(1, [256] * 4, 8, 64, name="cfg1-retnet-d64-8h-4x256-fp32")
-    elif i == 2:
-        w = gla(2, [512] * 8, 16, 128, literal=True, name="cfg2-gla-d128-16h-8x512-bf16")
-    elif i == 3:
-        w = gdn(3, [4096] * 8, 16, 32, 128, torch.bfloat16,
-                name="cfg3-gdn-gqa32v16k-d128-8x4096-bf16")
-    elif i == 4:
-        w = gdn(4, [1024] * 100, 32, 32, 128, torch.bfloat16, conv_w=4, seam_w=8,
-                name="cfg4-gdn-d128-32h-100x1024-conv4-seam8-bf16")
-    else:
-        raise ValueError(i)
-    return w
+# Named synthetic workloads (the seed is fixed per workload).
+WORKLOADS = ("gdn_d16_2x64_fp32", "retnet_d64_8h_4x256_fp32", "gla_d128_16h_8x512_bf16",
+             "gdn_gqa_d128_8x4096_bf16", "gdn_d128_32h_100x1024_seams_bf16",
+             "gla_d128_16h_8x512_bf16_slow", "gdn_gqa_d128_8x4096_bf16_slow")
 
 
-def companion(tag: str) -> Workload:
-    """Non-degenerate companions whose transition operators stay far from 0."""
-    if tag == "2b":
-        return gla(2, [512] * 8, 16, 128, literal=False, name="cfg2b-gla-slow")
-    if tag == "3b":
-        return gdn(3, [4096] * 8, 16, 32, 128, torch.bfloat16, alpha_div=4096.0,
-                   name="cfg3b-gdn-gqa-slow")
-    if tag == "4b":
-        return gdn(4, [1024] * 100, 32, 32, 128, torch.bfloat16, alpha_div=1024.0,
-                   conv_w=4, seam_w=8, name="cfg4b-gdn-slow")
-    raise ValueError(tag)
+def workload(name: str) -> Workload:
+    """A named workload.  The *_slow companions keep the transition operators
+    far from 0 (slow decay), so that products of many of them stay measurable."""
+    if name == "gdn_d16_2x64_fp32":
+        return gdn(0, [64, 64], 1, 1, 16, torch.float32, name=name)
+    if name == "retnet_d64_8h_4x256_fp32":
+        return retnet(1, [256] * 4, 8, 64, name=name)
+    if name == "gla_d128_16h_8x512_bf16":
+        return gla(2, [512] * 8, 16, 128, literal=True, name=name)
+    if name == "gdn_gqa_d128_8x4096_bf16":
+        return gdn(3, [4096] * 8, 16, 32, 128, torch.bfloat16, name=name)
+    if name == "gdn_d128_32h_100x1024_seams_bf16":
+        return gdn(4, [1024] * 100, 32, 32, 128, torch.bfloat16, conv_w=4, seam_w=8, name=name)
+    if name == "gla_d128_16h_8x512_bf16_slow":
+        return gla(2, [512] * 8, 16, 128, literal=False, name=name)
+    if name == "gdn_gqa_d128_8x4096_bf16_slow":
+        return gdn(3, [4096] * 8, 16, 32, 128, torch.bfloat16, alpha_div=4096.0, name=name)
+    raise ValueError(name)
 
 
 def random_pairs(seed, n_slots, h, d_k, d_v, tform="dense", rho=0.9):

@@ -44,11 +44,11 @@ def _check_build(wl, segs=None, heads=None, tol=None, T=None, S0=None, label="")
 
 # ----------------------------------------------------------- reference configs
 
-def test_cfg0_gdn_fp32_build_compose():
+def test_gdn_d16_fp32_build_compose():
     need_gpu()
-    wl = synth.config(0)
+    wl = synth.workload("gdn_d16_2x64_fp32")
     dw, T, S0 = _check_build(wl)
-    case("compose cfg0")
+    case("compose gdn d16 fp32")
     S = dw.compose(T, S0)
     torch.cuda.synchronize()
     Tr, Sr = oracle.build_pairs(wl)
@@ -60,11 +60,11 @@ def test_cfg0_gdn_fp32_build_compose():
     assert oracle.relF(np64(S), full) <= 1e-5
 
 
-def test_cfg1_retnet_fp32_build_compose_naive():
+def test_retnet_fp32_build_compose_naive():
     need_gpu()
-    wl = synth.config(1)
+    wl = synth.workload("retnet_d64_8h_4x256_fp32")
     dw, T, S0 = _check_build(wl)
-    case("compose cfg1 (scalar T)")
+    case("compose retnet (scalar T)")
     S = dw.compose(T, S0)
     torch.cuda.synchronize()
     Tr, Sr = oracle.build_pairs(wl)
@@ -80,27 +80,27 @@ def test_cfg1_retnet_fp32_build_compose_naive():
     assert round(r, 3) == 0.221
 
 
-def test_cfg2_gla_bf16_build():
+def test_gla_bf16_build():
     need_gpu()
-    wl = synth.config(2)
+    wl = synth.workload("gla_d128_16h_8x512_bf16")
     dw, T, S0 = _check_build(wl)
-    case("compose cfg2 (diag T)")
+    case("compose gla (diag T)")
     S = dw.compose(T, S0)
     torch.cuda.synchronize()
     Tr, Sr = oracle.build_pairs(wl)
     assert oracle.relF(np64(S), oracle.compose(Tr, Sr)) <= 2e-3
 
 
-def test_cfg2b_gla_slow_build():
+def test_gla_slow_build():
     need_gpu()
-    _check_build(synth.companion("2b"), segs=[0, 5], heads=[0, 7, 15])
+    _check_build(synth.workload("gla_d128_16h_8x512_bf16_slow"), segs=[0, 5], heads=[0, 7, 15])
 
 
-def test_cfg3_gdn_gqa_sampled():
+def test_gdn_gqa_32k_prompt_sampled():
     need_gpu()
-    wl = synth.config(3)
+    wl = synth.workload("gdn_gqa_d128_8x4096_bf16")
     dw, T, S0 = _check_build(wl, segs=[0, 7], heads=[0, 1, 31], label="(sampled units)")
-    case("compose cfg3")
+    case("compose gdn gqa 32k prompt")
     S = dw.compose(T, S0)
     torch.cuda.synchronize()
     heads = [3]
@@ -111,9 +111,9 @@ def test_cfg3_gdn_gqa_sampled():
     assert e <= 2e-3
 
 
-def test_cfg3b_gdn_slow_sampled():
+def test_gdn_gqa_slow_sampled():
     need_gpu()
-    _check_build(synth.companion("3b"), segs=[2], heads=[4, 5], label="(sampled units)")
+    _check_build(synth.workload("gdn_gqa_d128_8x4096_bf16_slow"), segs=[2], heads=[4, 5], label="(sampled units)")
 
 
 # ------------------------------------------------------------- shape coverage
@@ -244,7 +244,7 @@ def test_seam_standalone_outputs(dtype):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
-def test_cfg4_like_small_pipeline(dtype):
+def test_seam_pipeline_small(dtype):
     """Conv + seams, small: pairs built from raw rows, composed with seams, against
     the oracle's composition and against full recompute."""
     need_gpu()
@@ -301,11 +301,11 @@ def test_split_compose_seams_across_launches():
     assert e <= 2e-5
 
 
-def test_cfg4_sampled():
+def test_gdn_100_segments_seams_sampled():
     need_gpu()
-    wl = synth.config(4)
+    wl = synth.workload("gdn_d128_32h_100x1024_seams_bf16")
     dw, T, S0 = _check_build(wl, segs=[0, 1, 99], heads=[0, 17], label="(sampled units)")
-    case("compose cfg4 with 99 seams")
+    case("compose 100 segments with 99 seams")
     S = dw.compose(T, S0)
     torch.cuda.synchronize()
     heads = [9]

@@ -10,11 +10,11 @@ def test_pin(orc, pin):
     pin(orc.build())
 
 
-def test_config1_head5_naive_ratio(orc):
+def test_retnet_head5_naive_ratio(orc):
     """The reference RetNet workload: head 5 has gamma = 1 - 2^-10, so the
     two-segment naive-addition ratio at 256 tokens is 1 - gamma^256 = 0.2213."""
     import synth
-    wl = synth.config(1)
+    wl = synth.workload("retnet_d64_8h_4x256_fp32")
     T, S0 = orc.build_pairs(wl, segs=[0, 1], heads=[5])
     true = orc.compose(T, S0)[0]
     delta = true - orc.naive_sum(S0)[0]
