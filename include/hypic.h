@@ -181,12 +181,21 @@ hypic_status hypic_seam_advance(const hypic_seam_desc *d, float *S_inout, void *
  *            seams->w <= 16), dense tform only; seams->q/o/T_w/S_w0 must be
  *            NULL here
  *   prec     HYPIC_PREC_FP32 or HYPIC_PREC_SPLIT for the dense product
+ *   group_len  dense split compose with d_k in {64, 128} only (ignored
+ *            otherwise): 1 folds the positions one after another; G >= 2
+ *            folds every G consecutive positions (windows included) into one
+ *            pair in parallel, then folds those pairs in order (composition is
+ *            associative, ch.2 sec.2); 0 picks G from n and h_v.  The result
+ *            is the same fold up to rounding.  Negative: HYPIC_E_INVALID.
  *
- * Workspace: hypic_workspace_size(desc, HYPIC_WS_COMPOSE) bytes.  It is 0
- * except for a dense split-precision compose with d_k in {64, 128}, seams and
- * n >= 2: the operators of all n-1 windows are computed first and staged
- * there, (3 wp d_k + 4) floats per (window, value head) with wp = w rounded
- * up to a multiple of 4, 16-byte aligned.
+ * Workspace: hypic_workspace_size(desc, HYPIC_WS_COMPOSE) bytes, 16-byte
+ * aligned.  It is 0 except for a dense split-precision compose with d_k in
+ * {64, 128}:
+ *   - with seams and n >= 2, the operators of all n-1 windows are computed
+ *     first and staged there, (3 wp d_k + 4) floats per (window, value head)
+ *     with wp = w rounded up to a multiple of 4 (rounded up to 256 bytes);
+ *   - with groups, two pools of group pairs follow, [ng, h_v, d_k, d_v] fp32
+ *     each, ng = ceil(min(n, HYPIC_MAX_SEG_PER_LAUNCH) / G).
  * Errors: HYPIC_E_INVALID, HYPIC_E_UNSUPPORTED, HYPIC_E_WORKSPACE, HYPIC_E_HIP.
  */
 typedef struct {
@@ -199,6 +208,7 @@ typedef struct {
     const float *S_init;
     float *S_out;
     const hypic_seam_desc *seams;
+    int32_t group_len;         /* 0 automatic, 1 serial, G >= 2 groups of G positions */
 } hypic_compose_desc;
 
 hypic_status hypic_compose(const hypic_compose_desc *d, void *ws, size_t ws_bytes,

@@ -60,7 +60,7 @@ class ComposeDesc(ctypes.Structure):
     _fields_ = [("tform", _i32), ("prec", _i32), ("h_v", _i32), ("d_k", _i32), ("d_v", _i32),
                 ("n", _i32), ("n_slots", _i32), ("order", _pi32),
                 ("T_pool", _vp), ("S0_pool", _vp), ("S_init", _vp), ("S_out", _vp),
-                ("seams", ctypes.POINTER(SeamDesc))]
+                ("seams", ctypes.POINTER(SeamDesc)), ("group_len", _i32)]
 
 
 class HypicError(RuntimeError):
@@ -257,8 +257,11 @@ class Seams:
 def compose(T_pool: torch.Tensor, S0_pool: torch.Tensor, order: Sequence[int],
             S_init: Optional[torch.Tensor] = None, tform: int = T_DENSE, prec: int = PREC_SPLIT,
             seams: Optional[Seams] = None, S_out: Optional[torch.Tensor] = None,
-            workspace: Optional[torch.Tensor] = None, stream=None):
-    """S = fold_i (S <- T[order[i]] S + S0[order[i]]), seams before positions 1.."""
+            workspace: Optional[torch.Tensor] = None, stream=None, group_len: int = 0):
+    """S = fold_i (S <- T[order[i]] S + S0[order[i]]), seams before positions 1..
+
+    group_len: 0 automatic, 1 serial fold, G >= 2 fold groups of G positions
+    in parallel, then the group pairs in order (dense split compose only)."""
     n_slots, h_v, d_k, d_v = S0_pool.shape
     if tuple(T_pool.shape) != t_shape(tform, n_slots, h_v, d_k):
         raise ValueError("T_pool shape does not match the transition form")
@@ -277,7 +280,7 @@ def compose(T_pool: torch.Tensor, S0_pool: torch.Tensor, order: Sequence[int],
     d = ComposeDesc(tform=tform, prec=prec, h_v=h_v, d_k=d_k, d_v=d_v, n=n, n_slots=n_slots,
                     order=ctypes.cast(ordr, _pi32), T_pool=_ptr(T_pool), S0_pool=_ptr(S0_pool),
                     S_init=_ptr(S_init), S_out=_ptr(S_out),
-                    seams=ctypes.pointer(sd) if sd is not None else None)
+                    seams=ctypes.pointer(sd) if sd is not None else None, group_len=int(group_len))
     L = _lib()
     need = L.hypic_workspace_size(ctypes.byref(d), WS_COMPOSE)
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):

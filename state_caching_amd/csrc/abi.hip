@@ -105,10 +105,51 @@ bool compose_uses_split(const hypic_compose_desc *d)
            (d->d_k == 64 || d->d_k == 128);
 }
 
-size_t compose_ws_bytes(const hypic_compose_desc *d)
+// Group length of the two-level compose for a launch of nb positions (1: the
+// serial fold).  Automatic (group_len 0): enough (group, head) workgroups to
+// fill the chip once, when the serial fold is long enough to gain from it.
+int compose_group_len(const hypic_compose_desc *d, int nb)
+{
+    if (!compose_uses_split(d) || nb < 2 || d->group_len == 1) return 1;
+    if (d->seams && d->seams->w > 8) return 1;   // the group kernel holds windows of up to 8 rows
+    if (d->group_len > 1) return std::min(d->group_len, nb);
+    if (nb < 16) return 1;
+    const int per_cu = d->d_k == 128 ? 1 : 2;
+    const int ng = std::max(1, 256 * per_cu / d->h_v);
+    const int G = (nb + ng - 1) / ng;
+    return G >= 2 ? G : 1;
+}
+
+// group pairs of the largest launch: ceil(nb / G) over the launch sizes of a call
+int compose_max_groups(const hypic_compose_desc *d)
+{
+    int best = 0;
+    const int sizes[2] = {std::min(d->n, (int)kMaxSeg), d->n % kMaxSeg};
+    for (int nb : sizes) {
+        if (nb <= 0) continue;
+        const int G = compose_group_len(d, nb);
+        if (G > 1) best = std::max(best, (nb + G - 1) / G);
+    }
+    return best;
+}
+
+size_t ws_align(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// seam operators (if any), then the group pairs T [ng, h_v, d, d] and S0 likewise
+size_t compose_ops_bytes(const hypic_compose_desc *d)
 {
     if (!d->seams || !compose_uses_split(d) || d->n <= 1) return 0;
-    return (size_t)seam_ops_floats(d->d_k, d->seams->w, d->n - 1, d->h_v) * sizeof(float);
+    return ws_align((size_t)seam_ops_floats(d->d_k, d->seams->w, d->n - 1, d->h_v) * sizeof(float));
+}
+
+size_t compose_group_bytes(const hypic_compose_desc *d)
+{
+    return (size_t)compose_max_groups(d) * d->h_v * d->d_k * d->d_v * sizeof(float);
+}
+
+size_t compose_ws_bytes(const hypic_compose_desc *d)
+{
+    return compose_ops_bytes(d) + 2 * compose_group_bytes(d);
 }
 
 SeamArgs seam_args(const hypic_seam_desc *s)
@@ -264,7 +305,7 @@ hypic_status hypic_compose(const hypic_compose_desc *d, void *ws, size_t ws_byte
     if (!d) return HYPIC_E_INVALID;
     if (d->tform < HYPIC_T_SCALAR || d->tform > HYPIC_T_DENSE) return HYPIC_E_INVALID;
     if (d->prec != HYPIC_PREC_FP32 && d->prec != HYPIC_PREC_SPLIT) return HYPIC_E_INVALID;
-    if (d->h_v <= 0 || d->n < 0) return HYPIC_E_INVALID;
+    if (d->h_v <= 0 || d->n < 0 || d->group_len < 0) return HYPIC_E_INVALID;
     if (d->d_k != d->d_v || !dim_ok(d->d_k)) return HYPIC_E_UNSUPPORTED;
     if (!d->S_out || !aligned16(d->S_out) || (d->S_init && !aligned16(d->S_init))) return HYPIC_E_INVALID;
     if (d->n > 0) {
@@ -304,14 +345,32 @@ hypic_status hypic_compose(const hypic_compose_desc *d, void *ws, size_t ws_byte
         a.S_in = d->S_init; a.S_out = d->S_out; a.n = 0;
         return from_hip(launch_compose(a, D, HYPIC_T_SCALAR, d->prec, in_kind, hs));
     }
+    float *gT = nullptr, *gS = nullptr;
+    if (compose_group_bytes(d) > 0) {
+        gT = reinterpret_cast<float *>(static_cast<char *>(ws) + compose_ops_bytes(d));
+        gS = gT + compose_group_bytes(d) / sizeof(float);
+    }
     for (int b = 0; b < d->n; b += kMaxSeg) {
         a.n = std::min(kMaxSeg, d->n - b);
         a.first_pos = b;
         a.S_in = b == 0 ? d->S_init : d->S_out;
         a.S_out = d->S_out;
         for (int i = 0; i < a.n; ++i) a.order[i] = d->order[b + i];
-        st = split ? from_hip(launch_compose_split(a, D, ops, hs))
-                   : from_hip(launch_compose(a, D, d->tform, d->prec, in_kind, hs));
+        const int G = compose_group_len(d, a.n);
+        if (G > 1) {
+            // level 1: every group of G positions folded into one pair; level 2:
+            // the serial fold over the group pairs
+            const int ng = (a.n + G - 1) / G;
+            if ((st = from_hip(launch_compose_group(a, D, ops, G, ng, gT, gS, hs))) != HYPIC_OK) return st;
+            ComposeArgs a2 = a;
+            a2.T_pool = gT; a2.S0_pool = gS;
+            a2.n = ng; a2.first_pos = 0; a2.has_seams = 0;
+            for (int i = 0; i < ng; ++i) a2.order[i] = i;
+            st = from_hip(launch_compose_split(a2, D, nullptr, hs));
+        } else {
+            st = split ? from_hip(launch_compose_split(a, D, ops, hs))
+                       : from_hip(launch_compose(a, D, d->tform, d->prec, in_kind, hs));
+        }
         if (st != HYPIC_OK) return st;
     }
     return HYPIC_OK;

@@ -99,5 +99,10 @@ int64_t seam_ops_floats(int D, int w, int n_win, int h_v);
 hipError_t launch_seam_ops(const ComposeArgs &a, int D, int in_kind, int n_win, float *ops,
                            hipStream_t st);
 hipError_t launch_compose_split(const ComposeArgs &a, int D, const float *ops, hipStream_t st);
+// level 1 of the two-level split compose (d in {64, 128}): the a.n positions in
+// ng groups of G consecutive ones, each (group, head) folded into one pair,
+// written to gT / gS [ng, h_v, D, D]
+hipError_t launch_compose_group(const ComposeArgs &a, int D, const float *ops, int G, int ng, float *gT,
+                                float *gS, hipStream_t st);
 
 }  // namespace hy

@@ -70,8 +70,9 @@ class DeviceWorkload:
                              k_l2norm=1 if conv else 0, stream=stream)
 
     def compose(self, T, S0, S_init=None, order=None, seams=True, prec=None, S_out=None,
-                stream=None):
+                stream=None, group_len=0):
         order = list(range(S0.shape[0])) if order is None else list(order)
         return compose(T, S0, order, S_init=S_init, tform=self.tform,
                        prec=self.prec if prec is None else prec,
-                       seams=self.seams if seams else None, S_out=S_out, stream=stream)
+                       seams=self.seams if seams else None, S_out=S_out, stream=stream,
+                       group_len=group_len)

@@ -301,6 +301,71 @@ def test_split_compose_seams_across_launches():
     assert e <= 2e-5
 
 
+@pytest.mark.parametrize("d,G", [(64, 2), (64, 5), (128, 3), (128, 7)])
+def test_group_compose_with_seams(d, G):
+    """The two-level compose (groups of G consecutive positions folded in
+    parallel, then the group pairs in order) with seams and a random prefix
+    state, ragged last group: against the oracle's sequential composition of
+    the same pairs, against the serial GPU fold, and against full recompute."""
+    need_gpu()
+    lens = [40, 64, 33, 70, 21, 64, 50, 90, 17, 64, 45, 80, 66, 29, 55, 64, 38]
+    wl = synth.gdn(110 + d + G, lens, 1, 2, d, torch.bfloat16, alpha_div=64.0, conv_w=4,
+                   seam_w=8)
+    sca, DW = _lib()
+    dw = DW(wl)
+    T, S0 = dw.build()
+    S_init = synth.random_state(111 + d, 2, d, d)
+    case(f"group compose with seams d={d} G={G} n={len(lens)}")
+    S = dw.compose(T, S0, S_init=S_init.cuda(), group_len=G)
+    S_ser = dw.compose(T, S0, S_init=S_init.cuda(), group_len=1)
+    torch.cuda.synchronize()
+    S_or = oracle.compose(np64(T), np64(S0), S_init=np64(S_init), wl=wl, seams=True)
+    full = oracle.full_recompute(wl, S_init=np64(S_init))
+    e1, e2, e3 = (oracle.relF(np64(S), S_or), oracle.relF(np64(S), np64(S_ser)),
+                  oracle.relF(np64(S), full))
+    print(f"  relF vs oracle compose {e1:.3e}, vs serial GPU fold {e2:.3e}, vs full recompute {e3:.3e}")
+    assert e1 <= 2e-5 and e2 <= 2e-5 and e3 <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_group_compose_no_seams(d):
+    """The two-level compose without seams (automatic and fixed group lengths,
+    and a group length beyond n), dense random pairs: against the oracle."""
+    need_gpu()
+    sca, _ = _lib()
+    n, h = 37, 3
+    T, S0 = synth.random_pairs(120 + d, n, h, d, d, tform="dense", rho=0.95)
+    S_init = synth.random_state(121 + d, h, d, d)
+    order = list(np.random.default_rng(122 + d).permutation(n))
+    ref = oracle.compose(np64(T)[order], np64(S0)[order], np64(S_init))
+    for G in (0, 4, 9, 64):
+        case(f"group compose no seams d={d} G={G}")
+        S = sca.compose(T.cuda(), S0.cuda(), order, S_init=S_init.cuda(), group_len=G)
+        torch.cuda.synchronize()
+        e = oracle.relF(np64(S), ref)
+        print(f"  G={G}: relF vs oracle {e:.3e}")
+        assert e <= 2e-5
+
+
+def test_group_compose_seams_across_launches():
+    """The two-level compose over more positions than one launch holds, with
+    seams: group pairs per launch, windows by prompt position, the running
+    state carried between launches."""
+    need_gpu()
+    wl = synth.gdn(131, [12] * 150, 1, 1, 64, torch.bfloat16, alpha_div=16.0, conv_w=4,
+                   seam_w=8)
+    sca, DW = _lib()
+    dw = DW(wl)
+    T, S0 = dw.build()
+    case("group compose with seams, 150 segments, G=6")
+    S = dw.compose(T, S0, group_len=6)
+    torch.cuda.synchronize()
+    S_or = oracle.compose(np64(T), np64(S0), wl=wl, seams=True)
+    e = oracle.relF(np64(S), S_or)
+    print(f"  relF vs oracle compose of the same pairs {e:.3e}")
+    assert e <= 2e-5
+
+
 def test_gdn_100_segments_seams_sampled():
     need_gpu()
     wl = synth.workload("gdn_d128_32h_100x1024_seams_bf16")
