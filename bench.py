@@ -40,6 +40,7 @@ KERNEL_SOURCES = {
     "build_delta_f16_kernel": ["build_delta_f16.hip", "common.h", "launch.h"],
     "seam_ops_kernel": ["seam.h", "compose_split.hip", "common.h", "launch.h"],
     "compose_split_kernel": ["compose_split.hip", "seam.h", "common.h", "launch.h"],
+    "compose_group_kernel": ["compose_group.hip", "seam.h", "common.h", "launch.h"],
 }
 
 
@@ -273,10 +274,12 @@ def main():
                 "head_compositions_per_s": wl4.n_seg * wl4.h_v / (k4 * 1e-3),
                 "ms_per_compose": k4, "wall_ms_per_step": wall4,
                 "roofline": {"bound": "hbm",
-                             "kernel": "hypic_compose = seam_ops_kernel<128> + compose_split_kernel<128,seams>",
+                             "kernel": "hypic_compose = seam_ops_kernel<128> + compose_group_kernel<128,seams> "
+                                       "(groups of 13 positions) + compose_split_kernel<128> (8 group pairs)",
                              "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
                              "frac": gbs / PEAK_HBM,
-                             "traffic": counter_traffic(["seam_ops_kernel", "compose_split_kernel"], "gdn_100_segments_seams"),
+                             "traffic": counter_traffic(["seam_ops_kernel", "compose_group_kernel", "compose_split_kernel"],
+                                                        "gdn_100_segments_seams"),
                              "algorithmic_bytes": by,
                              "mfma_tflops": compose_flops(wl4) / (k4 * 1e-3) / 1e12}}
         out["compose"] = comp

@@ -12,15 +12,16 @@
 // parallel; level 2 is the ordinary serial fold over the group pairs (the
 // no-seam compose kernel), G times shorter than the fold over the segments.
 //
-// One workgroup of d/32 waves (one per SIMD at d = 128) per (group, value
-// head).  A wave owns 64 columns of X (all d rows, fp32 in matrix-core
-// accumulator layout): the first half of the waves the T half, the others the
-// S half.  The products run on bf16 hi/lo splits (three matrix-core products
+// One workgroup of d/16 waves (two per SIMD at d = 128, so one wave's VALU and
+// LDS work overlaps the other's matrix products) per (group, value head).  A
+// wave owns 32 columns of X (all d rows, fp32 in matrix-core accumulator
+// layout): the first half of the waves the T half, the others the S half.  The products run on bf16 hi/lo splits (three matrix-core products
 // per term), A operands from LDS, B operands from the wave's own accumulators,
 // so X never leaves the registers until the group ends.  T of the next position
 // is streamed through the T half's registers and split into the other LDS
 // buffer while the current product runs (one barrier per position); the S
-// half streams S0 the same way into its registers.  The window operators
+// half streams S0 the same way into its registers.  (A variant with 64 columns
+// per wave, one wave per SIMD, is kept for comparison: HY_CG_NN = 4.)  The window operators
 // (W = M diag(b) K, K, U^T, gw; w <= 8) come from the per-(window, head)
 // records that seam_ops_kernel writes.
 #include <type_traits>
@@ -31,23 +32,27 @@
 
 namespace hy {
 
-template <int D>
+// NN 16-column tiles of X per wave: 4 (d/32 waves, one per SIMD at d = 128) or
+// 2 (d/16 waves, two per SIMD)
+template <int D, int NN_>
 struct CgCfg {
-    static constexpr int NW = D / 32;    // waves, 64 columns of X = [T | S] each
-    static constexpr int NWH = NW / 2;   // waves per half
+    static constexpr int NN = NN_;
+    static constexpr int NP = NN / 2;             // column pairs per wave
+    static constexpr int NW = 2 * D / (16 * NN);  // waves
+    static constexpr int NWH = NW / 2;            // waves per half
     static constexpr int NT = 64 * NW;
-    static constexpr int NN = 4;         // 16-column tiles per wave
-    static constexpr int MT = D / 16;    // 16-row tiles of X
-    static constexpr int KB = D / 32;    // 32-deep k blocks of a product
-    static constexpr int LDA = D + 8;    // split row stride (bf16 elements)
-    static constexpr int WR = 8;         // window rows held (w <= 8)
-    static constexpr int QH = D / 8;     // float4 per lane of the T half's ring: half of T's rows,
-                                         // D*D/8 / (64 NWH)
+    static constexpr int MT = D / 16;             // 16-row tiles of X
+    static constexpr int KB = D / 32;             // 32-deep k blocks of a product
+    static constexpr int LDA = D + 8;             // split row stride (bf16 elements)
+    static constexpr int WR = 8;                  // window rows held (w <= 8)
+    static constexpr int TP = 2 * NP;             // parts of T's rows in the T half's ring
+    static constexpr int QH = D * D / 4 / (64 * NWH * TP);   // float4 per lane per part
+    static constexpr bool WK_SPLIT = NT >= 4 * D; // W and K staged by separate threads
 };
 
-template <int D>
+template <int D, int NN>
 struct CgSmem {
-    using C = CgCfg<D>;
+    using C = CgCfg<D, NN>;
     // double-buffered by position parity
     uint16_t AH[2][D][C::LDA];       // T of the position, hi, k-permuted within 32-column blocks
     uint16_t AL[2][D][C::LDA];       // lo
@@ -104,14 +109,15 @@ __device__ __forceinline__ f4 cg_mma3(const b8 &ah, const b8 &al, const b8 &bh, 
     return mma(ah, bh, c);
 }
 
-template <int D, bool SEAMS>
-__global__ void __launch_bounds__((CgCfg<D>::NT)) compose_group_kernel(const ComposeArgs a, const float *ops,
-                                                                       int G, float *gT, float *gS)
+template <int D, bool SEAMS, int NN>
+__global__ void __launch_bounds__((CgCfg<D, NN>::NT)) compose_group_kernel(const ComposeArgs a, const float *ops,
+                                                                           int G, float *gT, float *gS)
 {
-    using C = CgCfg<D>;
-    constexpr int MT = C::MT, KB = C::KB, QH = C::QH, LDA = C::LDA, NWH = C::NWH, NN = C::NN, WR = C::WR;
+    using C = CgCfg<D, NN>;
+    constexpr int MT = C::MT, KB = C::KB, QH = C::QH, LDA = C::LDA, NWH = C::NWH, NP = C::NP, WR = C::WR,
+                  TP = C::TP;
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    CgSmem<D> &sm = *reinterpret_cast<CgSmem<D> *>(smem_raw);
+    CgSmem<D, NN> &sm = *reinterpret_cast<CgSmem<D, NN> *>(smem_raw);
 
     // the wave index as a scalar, so the branches on the wave's half are uniform
     const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -120,10 +126,14 @@ __global__ void __launch_bounds__((CgCfg<D>::NT)) compose_group_kernel(const Com
     const int j0 = gi * G, j1 = min(j0 + G, a.n);
     const int64_t hoff = (int64_t)h * D * D;
     const bool thalf = wv < NWH;
-    const int cb = 64 * (thalf ? wv : wv - NWH); // first column of this wave within its half
+    const int cb = 16 * NN * (thalf ? wv : wv - NWH);   // first column of this wave within its half
 
     const int w = SEAMS ? a.seam.w : 0, wp = winop_wp(w);
-    const int srow = tid / (D / 4), scol = 4 * (tid % (D / 4));
+    // W / K staging: one float4 of each per thread, or (WK_SPLIT) W by the first
+    // 2D threads and K by the others
+    const int wkt = C::WK_SPLIT ? tid % (2 * D) : tid;
+    const bool do_w = !C::WK_SPLIT || tid < 2 * D, do_k = !C::WK_SPLIT || tid >= 2 * D;
+    const int srow = wkt / (D / 4), scol = 4 * (wkt % (D / 4));
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
     auto win_rec = [&](int pos) { return ops + ((int64_t)max(pos - 1, 0) * a.h_v + h) * winop_floats<D>(w); };
 
@@ -143,17 +153,18 @@ __global__ void __launch_bounds__((CgCfg<D>::NT)) compose_group_kernel(const Com
                     X[mt][nt][i] = (TH && 16 * mt + 4 * g + i == cb + 16 * nt + r16) ? 1.f : 0.f;
 
         // prefetch rings, refilled as they are consumed so that each load has about
-        // one column pair's work (a quarter of a position) to land:
-        //   T half: half of the next position's T rows (float4 f = tid + 64 NWH q
-        //           + hf D*D/8 of the row-major matrix), fetched at the start of
-        //           pair hf and staged into the other buffer at its end;
+        // half a column pair's work to land:
+        //   T half: part hf of the next position's T rows (float4 f = tid + 64 NWH q
+        //           + hf D*D/(4 TP) of the row-major matrix), fetched at the start
+        //           (or the middle) of pair hf/2 and staged into the other buffer at
+        //           its middle (or end);
         //   S half: the S0 tiles (mt, 2p + q) of the current pair, each slot
-        //           reloaded with the next pair's tile once it is added.
+        //           reloaded with the next pair's tile once it is used.
         float4 tq[TH ? QH : 1];
         float4 s0q[TH ? 1 : MT][2];
         auto fetch_t = [&](int j, int hf) {
             if constexpr (TH) {
-                const float *Tp = a.T_pool + (int64_t)a.order[j] * a.h_v * D * D + hoff + hf * (D * D / 2);
+                const float *Tp = a.T_pool + (int64_t)a.order[j] * a.h_v * D * D + hoff + hf * (D * D / TP);
 #pragma unroll
                 for (int q = 0; q < QH; ++q) tq[q] = *reinterpret_cast<const float4 *>(Tp + 4 * (tid + 64 * NWH * q));
             }
@@ -162,7 +173,7 @@ __global__ void __launch_bounds__((CgCfg<D>::NT)) compose_group_kernel(const Com
             if constexpr (TH) {
 #pragma unroll
                 for (int q = 0; q < QH; ++q) {
-                    const int f = tid + 64 * NWH * q + hf * (D * D / 8), row = f / (D / 4), c = 4 * (f % (D / 4));
+                    const int f = tid + 64 * NWH * q + hf * (D * D / 4 / TP), row = f / (D / 4), c = 4 * (f % (D / 4));
                     uint2 hi, lo;
                     cg_split4(tq[q], hi, lo);
                     *reinterpret_cast<uint2 *>(&sm.AH[buf][row][cg_perm(c)]) = hi;
@@ -191,8 +202,8 @@ __global__ void __launch_bounds__((CgCfg<D>::NT)) compose_group_kernel(const Com
                 hwq = pos >= 1;
                 const float *o = win_rec(pos);
                 const bool rin = hwq && srow < w;
-                Wq = *reinterpret_cast<const float4 *>(o + (int64_t)(rin ? srow : 0) * D + scol);
-                Kq = *reinterpret_cast<const float4 *>(o + (int64_t)wp * D + (int64_t)(rin ? srow : 0) * D + scol);
+                if (do_w) Wq = *reinterpret_cast<const float4 *>(o + (int64_t)(rin ? srow : 0) * D + scol);
+                if (do_k) Kq = *reinterpret_cast<const float4 *>(o + (int64_t)wp * D + (int64_t)(rin ? srow : 0) * D + scol);
                 if (!rin) { Wq = z4; Kq = z4; }
                 gwq = hwq ? o[(int64_t)3 * wp * D] : 1.f;
             }
@@ -200,12 +211,16 @@ __global__ void __launch_bounds__((CgCfg<D>::NT)) compose_group_kernel(const Com
         auto stage_win = [&](int buf) {   // W, K of the fetched window into buffer buf; gw current
             if constexpr (SEAMS) {
                 uint2 hi, lo;
-                cg_split4(Wq, hi, lo);
-                *reinterpret_cast<uint2 *>(&sm.WH[buf][srow][cg_perm(scol)]) = hi;
-                *reinterpret_cast<uint2 *>(&sm.WL[buf][srow][cg_perm(scol)]) = lo;
-                cg_split4(Kq, hi, lo);
-                *reinterpret_cast<uint2 *>(&sm.KH[buf][srow][scol]) = hi;
-                *reinterpret_cast<uint2 *>(&sm.KL[buf][srow][scol]) = lo;
+                if (do_w) {
+                    cg_split4(Wq, hi, lo);
+                    *reinterpret_cast<uint2 *>(&sm.WH[buf][srow][cg_perm(scol)]) = hi;
+                    *reinterpret_cast<uint2 *>(&sm.WL[buf][srow][cg_perm(scol)]) = lo;
+                }
+                if (do_k) {
+                    cg_split4(Kq, hi, lo);
+                    *reinterpret_cast<uint2 *>(&sm.KH[buf][srow][scol]) = hi;
+                    *reinterpret_cast<uint2 *>(&sm.KL[buf][srow][scol]) = lo;
+                }
                 gwc = gwq;
                 hwc = hwq;
             }
@@ -220,8 +235,8 @@ __global__ void __launch_bounds__((CgCfg<D>::NT)) compose_group_kernel(const Com
         // prologue: position j0 staged in buffer 0 (T half), the S0 tiles of its
         // first pair in flight (S half), the window of j0 + 1 in flight
         if constexpr (TH) {
-            fetch_t(j0, 0); stage_t(0, 0);
-            fetch_t(j0, 1); stage_t(0, 1);
+#pragma unroll
+            for (int hf = 0; hf < TP; ++hf) { fetch_t(j0, hf); stage_t(0, hf); }
         } else {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) fetch_s0(j0, 0, mt);
@@ -250,11 +265,11 @@ __global__ void __launch_bounds__((CgCfg<D>::NT)) compose_group_kernel(const Com
             }
             const int jn = min(j + 1, j1 - 1);
 #pragma unroll
-            for (int p = 0; p < NN / 2; ++p) {
+            for (int p = 0; p < NP; ++p) {
                 // scheduling regions per pair and per part: with one wave per SIMD the
                 // scheduler would otherwise overlap the parts beyond the register file
                 __builtin_amdgcn_sched_barrier(0);
-                fetch_t(jn, p);
+                fetch_t(jn, 2 * p);
                 if constexpr (SEAMS) {
                     // P = W X (window rows t = r16 < 8), E = U~ - gw P, X <- gw X + K^T E;
                     // branch-free: position 0 runs it with W = K = U = 0, gw = 1, which
@@ -312,11 +327,19 @@ __global__ void __launch_bounds__((CgCfg<D>::NT)) compose_group_kernel(const Com
                 // first pair of the next one (clamped to the group)
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    if (p == 0) fetch_s0(j, 1, mt);
+                    if (p + 1 < NP) fetch_s0(j, p + 1, mt);
                     else fetch_s0(jn, 0, mt);
                 }
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
+                    if (kb == KB / 2) {
+                        // the pair's first part of the next position's T into the other
+                        // buffer (read only after the next barrier), the second in flight
+                        __builtin_amdgcn_sched_barrier(0);
+                        stage_t(buf ^ 1, 2 * p);
+                        fetch_t(jn, 2 * p + 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                     b8 bh[2], bl[2];
                     split_kb(p, kb, bh, bl);
 #pragma unroll
@@ -331,9 +354,7 @@ __global__ void __launch_bounds__((CgCfg<D>::NT)) compose_group_kernel(const Com
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int q = 0; q < 2; ++q) X[mt][2 * p + q] = acc[mt][q];
-                // half of the next position's T into the other buffer (read only
-                // after the next barrier)
-                stage_t(buf ^ 1, p);
+                stage_t(buf ^ 1, 2 * p + 1);
             }
             stage_win(buf ^ 1);
             fetch_win(a.first_pos + min(j + 2, j1 - 1));
@@ -353,34 +374,38 @@ __global__ void __launch_bounds__((CgCfg<D>::NT)) compose_group_kernel(const Com
     else run(std::false_type{});
 }
 
-template <int D, bool SEAMS>
+template <int D, bool SEAMS, int NN>
 static hipError_t launch_cg(const ComposeArgs &a, const float *ops, int G, int ng, float *gT, float *gS,
                             hipStream_t st)
 {
-    const size_t smem = sizeof(CgSmem<D>);
+    const size_t smem = sizeof(CgSmem<D, NN>);
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&compose_group_kernel<D, SEAMS>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&compose_group_kernel<D, SEAMS, NN>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;
         attr = true;
     }
-    hipLaunchKernelGGL((compose_group_kernel<D, SEAMS>), dim3(ng * a.h_v), dim3(CgCfg<D>::NT), smem, st,
+    hipLaunchKernelGGL((compose_group_kernel<D, SEAMS, NN>), dim3(ng * a.h_v), dim3(CgCfg<D, NN>::NT), smem, st,
                        a, ops, G, gT, gS);
     return hipGetLastError();
 }
+
+#ifndef HY_CG_NN
+#define HY_CG_NN 2
+#endif
 
 hipError_t launch_compose_group(const ComposeArgs &a, int D, const float *ops, int G, int ng, float *gT,
                                 float *gS, hipStream_t st)
 {
     if (G < 1 || ng < 1 || (int64_t)(ng - 1) * G >= a.n || (int64_t)ng * G < a.n) return hipErrorInvalidValue;
-    if (a.has_seams && a.seam.w > CgCfg<128>::WR) return hipErrorInvalidValue;
+    if (a.has_seams && a.seam.w > CgCfg<128, HY_CG_NN>::WR) return hipErrorInvalidValue;
     // the seam variant needs at least one window record in this launch
     const bool seams = a.has_seams && a.first_pos + a.n >= 2;
-    if (D == 128) return seams ? launch_cg<128, true>(a, ops, G, ng, gT, gS, st)
-                               : launch_cg<128, false>(a, ops, G, ng, gT, gS, st);
-    if (D == 64) return seams ? launch_cg<64, true>(a, ops, G, ng, gT, gS, st)
-                              : launch_cg<64, false>(a, ops, G, ng, gT, gS, st);
+    if (D == 128) return seams ? launch_cg<128, true, HY_CG_NN>(a, ops, G, ng, gT, gS, st)
+                               : launch_cg<128, false, HY_CG_NN>(a, ops, G, ng, gT, gS, st);
+    if (D == 64) return seams ? launch_cg<64, true, HY_CG_NN>(a, ops, G, ng, gT, gS, st)
+                              : launch_cg<64, false, HY_CG_NN>(a, ops, G, ng, gT, gS, st);
     return hipErrorInvalidValue;
 }
 
