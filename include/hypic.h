@@ -23,6 +23,8 @@
  *   DECAY + DIAG       : T_i = diag(g_i),      u_i = k_i v_i^T  (GLA)        T_C diagonal
  *   DELTA + SCALAR     : T_i = a_i(I - b_i k_i k_i^T), u_i = b_i k_i v_i^T
  *                        (GDN; DeltaNet is a_i = 1)                           T_C dense
+ *   DELTA + DIAG       : T_i = (I - b_i k_i k_i^T) diag(g_i), u_i = b_i k_i v_i^T
+ *                        (KDA; fp32 matrix products for every input dtype)    T_C dense
  *
  * Conventions shared by every call
  *   - Every data pointer is a DEVICE pointer owned by the caller; arrays are
@@ -109,8 +111,9 @@ typedef enum {
  * Workspace: hypic_workspace_size(desc, HYPIC_WS_BUILD) bytes (0 without conv
  * or key normalisation; ws may then be NULL).  Empty ranges give T = I, S0 = 0.
  * Errors: HYPIC_E_INVALID (null pointers, negative lengths, h_v % h_k != 0),
- * HYPIC_E_UNSUPPORTED (dimensions, h_v * d_k >= 2^24, DECAY+DIAG with conv,
- * DELTA+DIAG), HYPIC_E_WORKSPACE, HYPIC_E_HIP.
+ * HYPIC_E_UNSUPPORTED (dimensions, h_v * d_k >= 2^24, DECAY+DIAG with conv),
+ * HYPIC_E_WORKSPACE, HYPIC_E_HIP.  DELTA+DIAG: a gate below 2^-126 is taken
+ * as 2^-126.
  */
 typedef struct {
     int32_t rule, gate_kind, in_dtype;

@@ -66,7 +66,7 @@ hypic_status validate_build(const hypic_build_desc *d)
     if (d->d_k != d->d_v || !dim_ok(d->d_k)) return HYPIC_E_UNSUPPORTED;
     // row pitches h * d enter 24-bit multiplies in the build kernels
     if ((int64_t)d->h_v * d->d_k >= (1 << 24)) return HYPIC_E_UNSUPPORTED;
-    if (d->rule == HYPIC_RULE_DELTA && d->gate_kind != HYPIC_GATE_SCALAR) return HYPIC_E_UNSUPPORTED;
+    if (d->rule == HYPIC_RULE_DELTA && d->gate_kind == HYPIC_GATE_HEAD_CONST) return HYPIC_E_UNSUPPORTED;
     if (d->rule == HYPIC_RULE_DECAY && build_needs_prep(d)) return HYPIC_E_UNSUPPORTED;
     if (!d->k || !d->v || !d->gate || !d->T_out || !d->S0_out) return HYPIC_E_INVALID;
     if (d->rule == HYPIC_RULE_DELTA && !d->beta) return HYPIC_E_INVALID;
@@ -213,7 +213,8 @@ hypic_status hypic_segment_build(const hypic_build_desc *d, void *ws, size_t ws_
     const int in_kind = d->in_dtype == HYPIC_BF16 ? IN_BF16 : IN_F32;
     const bool prep = build_needs_prep(d);
     // the fp16-operand build (bf16 inputs, d >= 64) takes fp16 keys from the conv
-    const bool khalf = prep && d->in_dtype == HYPIC_BF16 && D >= 64 && d->rule == HYPIC_RULE_DELTA;
+    const bool kda = d->rule == HYPIC_RULE_DELTA && d->gate_kind == HYPIC_GATE_DIAG;
+    const bool khalf = prep && d->in_dtype == HYPIC_BF16 && D >= 64 && d->rule == HYPIC_RULE_DELTA && !kda;
     float *wk = nullptr, *wvv = nullptr, *wvs = nullptr;
     if (prep) {
         const int64_t rows = build_rows(d);
@@ -280,8 +281,9 @@ hypic_status hypic_segment_build(const hypic_build_desc *d, void *ws, size_t ws_
                 a.ldk = (int64_t)d->h_k * D; a.ldv = (int64_t)d->h_v * D;
             }
             const int kv_kind = khalf ? IN_F16K : (prep ? IN_F32 : in_kind);
-            st = from_hip(launch_build_delta(a, D, kv_kind, in_kind, d->in_dtype == HYPIC_BF16,
-                                             nb * d->h_v, hs));
+            st = kda ? from_hip(launch_build_kda(a, D, kv_kind, in_kind, nb * d->h_v, hs))
+                     : from_hip(launch_build_delta(a, D, kv_kind, in_kind, d->in_dtype == HYPIC_BF16,
+                                                   nb * d->h_v, hs));
         } else {
             DecayArgs a;
             memset(&a, 0, sizeof(a));

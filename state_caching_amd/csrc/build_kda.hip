@@ -1,0 +1,367 @@
+// build_kda.hip -- chunkwise build of the cached pair (T_C, S_{C|0}) for the
+// delta rule with a diagonal gate, T_i = (I - b_i k_i k_i^T) diag(g_i),
+// u_i = b_i k_i v_i^T (HYPIC reading notes, ch.2 sec.3 Table 1, the KDA row;
+// pair definition ch.2 sec.2, built there by two runs of the recurrence,
+// ch.2 sec.4).
+//
+// One pass over the segment in chunks of b = 64 tokens carries X = [T | S]
+// (d_k x 2d, fp32 in matrix-core accumulators).  The per-channel gate does
+// not commute with the rank-one erase, so it cannot be factored out of the
+// product as a scalar gate can; it is carried inside the chunk algebra.
+// Within a chunk, with cl_r[d] = sum_{s <= r} log2 g_s[d] (cumulative from
+// the chunk start) and Gam_r = diag(2^cl_r):
+//   A_r = diag(g_r) S_{r-1},   S_r = A_r + k_r e_r^T,
+//   e_r = b_r (v_r - (Gam_r k_r)^T S_0 - sum_{s<r} L_rs e_s),
+//   L_rs = sum_d k_r[d] k_s[d] 2^(cl_r[d] - cl_s[d])          (s < r)
+// so with M = (I + diag(b) L)^-1 (unit lower triangular),
+//   W = M diag(b) Kt,  Kt_r = Gam_r k_r,   U = M diag(b) V,
+//   E = [0 | U] - W X,   X <- Gam_b X + Kh^T E,  Kh_s = (Gam_b Gam_s^-1) k_s.
+// Every decay factor applied is 2^(non-positive); the Gram tiles take a
+// reference token per tile pair so that both operand factors stay bounded
+// (off the diagonal both are <= 1; on a diagonal 16-token tile the reference
+// is its middle token).  Products are fp32 16x16x4 on the matrix cores.
+#include <type_traits>
+
+#include "common.h"
+#include "launch.h"
+
+namespace hy {
+
+template <int D>
+struct KdaCfg {
+    static constexpr int MT = D / 16;         // 16-row tiles of the state
+    static constexpr int NW = D / 16;         // waves; wave w owns column tiles 2w, 2w+1 of X
+    static constexpr int NT = 64 * NW;
+    static constexpr int LDT = 68;            // token-contiguous row stride (floats)
+    static constexpr int LDG = 68;
+};
+
+template <int D>
+struct KdaSmem {
+    using C = KdaCfg<D>;
+    float KT[D][C::LDT];     // keys (dim-major); then Gam k; then W^T
+    float CL[D][C::LDT];     // cumulative log2 gates (dim-major); then Kh^T
+    float VT[D][C::LDT];     // values (dim-major)
+    float Gm[64][C::LDG];    // b_r L_rs for s < r, else 0
+    float Mm[64][C::LDG];    // M = (I + Gm)^-1
+    float beta[64];
+    float clb[D];            // cl of the chunk's last token per channel
+    float gamb[D];           // 2^clb
+};
+
+// Gram tiles on or below the diagonal of the 4x4 token-tile grid
+__constant__ int kKdaTi[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+__constant__ int kKdaTj[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+
+template <int D, typename TKV, typename TG>
+__global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_kernel(const DeltaArgs a)
+{
+    using C = KdaCfg<D>;
+    constexpr int MT = C::MT, NW = C::NW;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    KdaSmem<D> &sm = *reinterpret_cast<KdaSmem<D> *>(smem_raw);
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int unit = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int s = unit / a.h_v, h = unit % a.h_v;
+    const int kh = h / (a.h_v / a.h_k);
+    const int len = a.len[s];
+    const TKV *kp = reinterpret_cast<const TKV *>(a.k) + a.tok0[s] * a.ldk + (int64_t)kh * D;
+    const TKV *vp = reinterpret_cast<const TKV *>(a.v) + a.tok0[s] * a.ldv + (int64_t)h * D;
+    const TG *bp = reinterpret_cast<const TG *>(a.beta) + a.gtok0[s] * a.h_v + h;
+    const TG *gp = reinterpret_cast<const TG *>(a.alpha) + (a.gtok0[s] * a.h_v + h) * (int64_t)D;
+    const int64_t ldg = (int64_t)a.h_v * D;
+
+    // upper tile blocks of M are never written: zero them once
+    for (int idx = tid; idx < 64 * 64; idx += C::NT) {
+        const int r = idx >> 6, c = idx & 63;
+        if ((c >> 4) > (r >> 4)) sm.Mm[r][c] = 0.f;
+    }
+
+    // X = [T | S] in accumulator layout: X[mt][jn] holds rows 16 mt .., column tile 2w + jn
+    f4 X[MT][2];
+#pragma unroll
+    for (int jn = 0; jn < 2; ++jn) {
+        const int n = 2 * w + jn;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                X[mt][jn][i] = (n < MT && 16 * mt + 4 * g + i == 16 * n + r16) ? 1.f : 0.f;
+    }
+
+    // register prefetch of one chunk: rows prow and prow + 32, columns pcol .. pcol + 7
+    constexpr int CPR = D / 8;
+    const int prow = tid / CPR, pcol = 8 * (tid % CPR);
+    typename Raw8<TKV>::type kraw[2], vraw[2];
+    typename Raw8<TG>::type graw[2];
+    float br = 0.f;
+    auto fetch = [&](int c) {
+        const int t0 = 64 * c;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int t = t0 + prow + 32 * p;
+            if (t < len) {
+                ld_raw8(kp + (int64_t)t * a.ldk + pcol, kraw[p]);
+                ld_raw8(vp + (int64_t)t * a.ldv + pcol, vraw[p]);
+                ld_raw8(gp + (int64_t)t * ldg + pcol, graw[p]);
+            } else {
+                zero_raw8(kraw[p]);
+                zero_raw8(vraw[p]);
+                zero_raw8(graw[p]);
+            }
+        }
+        if (w == 0) {
+            const int t = t0 + lane;
+            br = t < len ? ld1(bp + (int64_t)t * a.h_v) : 0.f;
+        }
+    };
+
+    const int nch = (len + 63) / 64;
+    if (nch > 0) fetch(0);
+
+    for (int c = 0; c < nch; ++c) {
+        lds_barrier();   // readers of the previous chunk are done
+
+        // ---- stage keys, values, log2 gates (dim-major), betas -------------------
+        {
+            float kr[2][8], vr[2][8], gr[2][8];
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                widen8(kraw[p], kr[p]);
+                widen8(vraw[p], vr[p]);
+                widen8(graw[p], gr[p]);
+            }
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int t = prow + 32 * p;
+                const bool in = 64 * c + t < len;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sm.KT[pcol + e][t] = kr[p][e];
+                    sm.VT[pcol + e][t] = vr[p][e];
+                    // past the segment end the transition is the identity (g = 1); a
+                    // gate below 2^-126 is taken as 2^-126 (the state is wiped either way)
+                    sm.CL[pcol + e][t] = in ? fmaxf(log2f(gr[p][e]), -126.f) : 0.f;
+                }
+            }
+            if (w == 0) sm.beta[lane] = br;
+        }
+        if (c + 1 < nch) fetch(c + 1);
+        lds_barrier();
+
+        // ---- cumulative log2 gates over the chunk, per channel (one wave scan each)
+        for (int d = w; d < D; d += NW) {
+            const float cl = wave_prefix_incl(sm.CL[d][lane]);
+            sm.CL[d][lane] = cl;
+            if (lane == 63) {
+                sm.clb[d] = cl;
+                sm.gamb[d] = exp2f(cl);
+            }
+        }
+        lds_barrier();
+
+        // ---- decay-aware Gram: b_r sum_d k_r k_s 2^(cl_r - cl_s), s < r ------------
+        for (int q = w; q < 10; q += NW) {
+            const int ti = kKdaTi[q], tj = kKdaTj[q];
+            const int ref = ti == tj ? 16 * ti + 8 : 16 * tj + 15;
+            f4 acc = zero4();
+#pragma unroll 4
+            for (int ks = 0; ks < D / 4; ++ks) {
+                const int k = g * (D / 4) + ks;
+                const float cr = sm.CL[k][ref];
+                const float A = sm.KT[k][16 * ti + r16] * exp2f(sm.CL[k][16 * ti + r16] - cr);
+                const float B = sm.KT[k][16 * tj + r16] * exp2f(cr - sm.CL[k][16 * tj + r16]);
+                acc = mma(A, B, acc);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 16 * ti + 4 * g + i, cc = 16 * tj + r16;
+                sm.Gm[rr][cc] = (cc < rr) ? sm.beta[rr] * acc[i] : 0.f;
+            }
+        }
+        lds_barrier();
+
+        // ---- M = (I + Gm)^-1: diagonal 16x16 blocks by forward substitution ----
+        if (w == 0) {
+            const int o = 16 * (lane >> 4), cc = lane & 15;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+                for (int q = 0; q < r; ++q) acc -= sm.Gm[o + r][o + q] * x[q];
+                x[r] = acc;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.Mm[o + r][o + cc] = x[r];
+        }
+        lds_barrier();
+        // 32x32 blocks: M10 = -M11 (L10 M00)
+        for (int p = w; p < 2; p += NW) {
+            const int o0 = 32 * p, o1 = 32 * p + 16;
+            f4 y = zero4();
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int k = 4 * g + ks;
+                y = mma(sm.Gm[o1 + r16][o0 + k], sm.Mm[o0 + k][o0 + r16], y);
+            }
+            f4 m = zero4();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) m = mma(sm.Mm[o1 + r16][o1 + 4 * g + i], y[i], m);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.Mm[o1 + 4 * g + i][o0 + r16] = -m[i];
+        }
+        lds_barrier();
+        // 64x64: rows 32..63, columns of tile tj: M[hi][lo] = -M[hi][hi] (L[hi][lo] M[lo][lo])
+        for (int tj = w; tj < 2; tj += NW) {
+            f4 y2 = zero4(), y3 = zero4();
+            for (int tk = tj; tk < 2; ++tk) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const int k = 4 * g + ks;
+                    const float bm = sm.Mm[16 * tk + k][16 * tj + r16];
+                    y2 = mma(sm.Gm[32 + r16][16 * tk + k], bm, y2);
+                    y3 = mma(sm.Gm[48 + r16][16 * tk + k], bm, y3);
+                }
+            }
+            f4 m2 = zero4(), m3 = zero4();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                m2 = mma(sm.Mm[32 + r16][32 + 4 * g + i], y2[i], m2);
+                m3 = mma(sm.Mm[48 + r16][32 + 4 * g + i], y2[i], m3);
+                m3 = mma(sm.Mm[48 + r16][48 + 4 * g + i], y3[i], m3);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sm.Mm[32 + 4 * g + i][16 * tj + r16] = -m2[i];
+                sm.Mm[48 + 4 * g + i][16 * tj + r16] = -m3[i];
+            }
+        }
+
+        // ---- decayed keys: KT <- Gam k, CL <- (Gam_b / Gam) k ----------------------
+        for (int idx = tid; idx < D * 64; idx += C::NT) {
+            const int d = idx >> 6, t = idx & 63;
+            const float kv = sm.KT[d][t], cl = sm.CL[d][t];
+            sm.KT[d][t] = kv * exp2f(cl);
+            sm.CL[d][t] = kv * exp2f(sm.clb[d] - cl);
+        }
+        lds_barrier();
+
+        // ---- W^T = (M diag(b) Kt)^T in place of Kt^T: wave w owns key rows 16w .. --
+        {
+            const int td = w;
+            f4 acc[4];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) {
+                acc[ti] = zero4();
+#pragma unroll
+                for (int ks = 0; ks < 16; ++ks) {
+                    const int k = 16 * g + ks;
+                    acc[ti] = mma(sm.Mm[16 * ti + r16][k] * sm.beta[k], sm.KT[16 * td + r16][k], acc[ti]);
+                }
+            }
+            // every read of this wave's rows is issued above (LDS operations of a
+            // wave complete in order)
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.KT[16 * td + r16][16 * ti + 4 * g + i] = acc[ti][i];
+        }
+        lds_barrier();
+
+        // ---- state update of this wave's two column tiles ----------------------
+#pragma unroll
+        for (int jn = 0; jn < 2; ++jn) {
+            const int n = 2 * w + jn;
+            const bool isS = n >= MT;
+            f4 E[4];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) E[ti] = zero4();
+            if (isS) {   // U = M diag(b) V for the value columns of this tile
+                const int cc = 16 * (n - MT);
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) {
+#pragma unroll
+                    for (int ks = 0; ks < 16; ++ks) {
+                        const int k = 16 * g + ks;
+                        E[ti] = mma(sm.Mm[16 * ti + r16][k] * sm.beta[k], sm.VT[cc + r16][k], E[ti]);
+                    }
+                }
+            }
+            // E -= W X (X before the chunk)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti)
+                        E[ti] = mma(sm.KT[16 * mt + 4 * g + i][16 * ti + r16], -X[mt][jn][i], E[ti]);
+            // X <- Gam_b X + Kh^T E
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const float4 gq = *reinterpret_cast<const float4 *>(&sm.gamb[16 * mt + 4 * g]);
+                X[mt][jn] *= f4{gq.x, gq.y, gq.z, gq.w};
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        X[mt][jn] = mma(sm.CL[16 * mt + r16][16 * ti + 4 * g + i], E[ti][i], X[mt][jn]);
+            }
+        }
+    }
+
+    float *Tu = a.T_out + (int64_t)unit * D * D;
+    float *Su = a.S0_out + (int64_t)unit * D * D;
+#pragma unroll
+    for (int jn = 0; jn < 2; ++jn) {
+        const int n = 2 * w + jn;
+        const bool isS = n >= MT;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * mt + 4 * g + i;
+                if (isS) Su[row * D + 16 * (n - MT) + r16] = X[mt][jn][i];
+                else     Tu[row * D + 16 * n + r16] = X[mt][jn][i];
+            }
+    }
+}
+
+template <int D, typename TKV, typename TG>
+static hipError_t launch_kda_one(const DeltaArgs &a, int n_units, hipStream_t st)
+{
+    const size_t smem = sizeof(KdaSmem<D>);
+    static bool attr_set = false;   // benign race: every setter writes the same value
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&build_kda_kernel<D, TKV, TG>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((build_kda_kernel<D, TKV, TG>), dim3(n_units), dim3(KdaCfg<D>::NT), smem, st, a);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_kda_d(const DeltaArgs &a, int kv_kind, int g_kind, int n_units, hipStream_t st)
+{
+    if (kv_kind == IN_BF16 && g_kind == IN_BF16) return launch_kda_one<D, bf16_t, bf16_t>(a, n_units, st);
+    if (kv_kind == IN_F32 && g_kind == IN_BF16) return launch_kda_one<D, float, bf16_t>(a, n_units, st);
+    if (kv_kind == IN_F32 && g_kind == IN_F32) return launch_kda_one<D, float, float>(a, n_units, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_build_kda(const DeltaArgs &a, int D, int kv_kind, int g_kind, int n_units, hipStream_t st)
+{
+    switch (D) {
+    case 16: return launch_kda_d<16>(a, kv_kind, g_kind, n_units, st);
+    case 32: return launch_kda_d<32>(a, kv_kind, g_kind, n_units, st);
+    case 64: return launch_kda_d<64>(a, kv_kind, g_kind, n_units, st);
+    case 128: return launch_kda_d<128>(a, kv_kind, g_kind, n_units, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace hy

@@ -86,6 +86,8 @@ hipError_t launch_build_delta(const DeltaArgs &a, int D, int kv_kind, int g_kind
                               int n_units, hipStream_t st);
 hipError_t launch_build_delta_f16(const DeltaArgs &a, int D, int kv_kind, int g_kind, int n_units,
                                   hipStream_t st);
+// delta rule with a diagonal gate (KDA): alpha is the gate [N, h_v, D]
+hipError_t launch_build_kda(const DeltaArgs &a, int D, int kv_kind, int g_kind, int n_units, hipStream_t st);
 hipError_t launch_build_decay(const DecayArgs &a, int D, int in_kind, int n_units,
                               hipStream_t st);
 hipError_t launch_conv(const ConvArgs &a, int D, int in_kind, bool out_f16, int64_t total_rows,

@@ -149,6 +149,32 @@ def gdn(seed, seg_len, h_k, h_v, d, dtype, alpha_div=1.0, name="gdn",
                     seam_w=seam_w, seed=seed)
 
 
+def kda(seed, seg_len, h_k, h_v, d, dtype, gate_div=1.0, name="kda", conv_w=0):
+    """Delta rule with a diagonal gate (KDA row of Table 1).
+
+    k ~ N(0,1) L2-normalised per (token, key head) (raw N(0,1) when conv_w>0),
+    v ~ N(0,1), beta = sigmoid(N(0,1)), g = exp(-softplus(N(0,1))/gate_div) per
+    key dimension and value head, [N, h_v, d].  Draw order as for gdn.
+    """
+    rng = np.random.default_rng(seed)
+    n = int(sum(seg_len))
+    k = rng.standard_normal((n, h_k, d))
+    if conv_w == 0:
+        k = _unit_rows(k)
+    v = rng.standard_normal((n, h_v, d))
+    beta = _sigmoid(rng.standard_normal((n, h_v)))
+    g = np.exp(-_softplus(rng.standard_normal((n, h_v, d))) / gate_div)
+    wk = wv = None
+    if conv_w > 0:
+        sd = 1.0 / np.sqrt(conv_w)
+        wk = _round(rng.standard_normal((h_k * d, conv_w)) * sd, torch.float32)
+        wv = _round(rng.standard_normal((h_v * d, conv_w)) * sd, torch.float32)
+    return Workload(name=name, rule=RULE_DELTA, gate_kind=GATE_DIAG, dtype=dtype,
+                    h_k=h_k, h_v=h_v, d_k=d, d_v=d, seg_len=list(seg_len),
+                    k=_round(k, dtype), v=_round(v, dtype), beta=_round(beta, dtype),
+                    gate=_round(g, dtype), conv_w=conv_w, conv_wk=wk, conv_wv=wv, seed=seed)
+
+
 def retnet(seed, seg_len, h, d, dtype=torch.float32, name="retnet", gammas=None):
     """Scalar-decay workload: gamma_h = 1 - 2^-(5+h), k, v ~ N(0,1)/sqrt(d)."""
     rng = np.random.default_rng(seed)

@@ -244,6 +244,33 @@ def pin_gdn_bounds(path):
     assert abs(np.trace(T1) - 7.0) < 1e-13
 
 
+def pin_kda_reductions(path):
+    """Delta rule with a diagonal gate (KDA row of Table 1), against the other
+    families and the norm bound:
+    - equal gates on every channel (g_i = a_i 1) give the gated-delta pair;
+    - b = 0 gives the gate-only product diag(prod g) and S0 = 0 (the diagonal
+      gate's closed form, T = diag(exp(cl_m)));
+    - ||k|| = 1, b in [0,1]: ||T_i||_2 <= max_d g_i[d], hence ||T_C||_2 <= prod max g;
+    - the gate acts before the erase: T_1 = (I - b k k^T) diag(g), not diag(g)(I - b k k^T)."""
+    rng = np.random.default_rng(15)
+    m, dk, dv = 21, 6, 5
+    k, v, b, _ = rand_unit(rng, "delta", "scalar", m, dk, dv)
+    a = rng.uniform(0.5, 1.0, m)
+    T1, S1, _ = one_unit(path, "delta", "diag", k, v, b, np.repeat(a[:, None], dk, axis=1))
+    T2, S2, _ = one_unit(path, "delta", "scalar", k, v, b, a)
+    assert np.allclose(T1, T2, rtol=0, atol=1e-14) and np.allclose(S1, S2, rtol=0, atol=1e-13)
+    g = rng.uniform(0.3, 1.0, (m, dk))
+    T0, S0, _ = one_unit(path, "delta", "diag", k, v, np.zeros(m), g)
+    assert np.allclose(T0, np.diag(np.exp(np.log(g).sum(axis=0))), rtol=1e-13, atol=0)
+    assert np.all(S0 == 0.0)
+    T, _, _ = one_unit(path, "delta", "diag", k, v, b, g)
+    assert np.linalg.norm(T, 2) <= np.prod(g.max(axis=1)) * (1 + 1e-12)
+    Tf, _, _ = one_unit(path, "delta", "diag", k[:1], v[:1], b[:1], g[:1])
+    P = np.eye(dk) - b[0] * np.outer(k[0], k[0])
+    assert np.allclose(Tf, P @ np.diag(g[0]), rtol=0, atol=1e-15)
+    assert not np.allclose(Tf, np.diag(g[0]) @ P, rtol=0, atol=1e-6)
+
+
 def pin_conv(path):
     """Depthwise causal conv against numpy's full convolution, with history."""
     rng = np.random.default_rng(9)
@@ -318,4 +345,4 @@ def pin_readout(path):
 
 ALL = [pin_readout, pin_worked_example, pin_table2, pin_news_22pct, pin_naive_error_identity,
        pin_brute_force, pin_affine, pin_decay_closed_forms, pin_identity_transition,
-       pin_composition_laws, pin_gdn_bounds, pin_conv, pin_l2norm, pin_compose_equals_full]
+       pin_composition_laws, pin_gdn_bounds, pin_kda_reductions, pin_conv, pin_l2norm, pin_compose_equals_full]

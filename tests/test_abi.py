@@ -67,7 +67,7 @@ def _build_desc(sca, **over):
     (dict(beta=None), -1),                   # delta rule needs beta
     (dict(d_k=96, d_v=96), -2),
     (dict(d_k=64, d_v=128), -2),
-    (dict(gate_kind=2), -2),                 # delta + diagonal gate (KDA) not built
+    (dict(gate_kind=0), -2),                 # delta rule with a per-head constant gate
     (dict(in_dtype=7), -1),
     (dict(k=8), -1),                         # misaligned pointer
     (dict(conv_w=5), -1),

@@ -366,6 +366,54 @@ def test_group_compose_seams_across_launches():
     assert e <= 2e-5
 
 
+# --------------------------------------------- delta rule with a diagonal gate (KDA)
+
+@pytest.mark.parametrize("d,dtype", [(16, torch.float32), (32, torch.bfloat16), (64, torch.float32),
+                                     (64, torch.bfloat16), (128, torch.float32), (128, torch.bfloat16)])
+def test_kda_build_compose(d, dtype):
+    """KDA pairs (T dense) on ragged and empty segments with GQA, against the
+    oracle's two-run pairs; their composition from a random state against full
+    recompute of the prompt."""
+    need_gpu()
+    lens = [0, 1, 63, 65, 130, 200]
+    wl = synth.kda(400 + d, lens, 2, 4, d, dtype, gate_div=32.0, name=f"kda-d{d}")
+    dw, T, S0 = _check_build(wl, tol=1e-5 if dtype == torch.float32 else 2e-5)
+    S_init = synth.random_state(401 + d, 4, d, d)
+    case(f"compose kda d={d}")
+    S = dw.compose(T, S0, S_init=S_init.cuda())
+    torch.cuda.synchronize()
+    full = oracle.full_recompute(wl, S_init=np64(S_init))
+    e = oracle.relF(np64(S), full)
+    print(f"  compose relF vs full recompute {e:.3e}")
+    assert e <= TOL[dtype]
+
+
+def test_kda_build_fast_gates():
+    """KDA with the unscaled gate draw (g = exp(-softplus(N(0,1))), strong
+    per-channel decay): the chunk's tile references keep every decay factor in
+    range; T_C decays towards 0 and S0 rests on the last tokens."""
+    need_gpu()
+    wl = synth.kda(410, [64, 100, 300], 1, 2, 64, torch.float32, gate_div=1.0, name="kda-fast")
+    _check_build(wl, tol=1e-5)
+
+
+def test_kda_build_conv():
+    """KDA with a width-4 causal conv and key L2 normalisation before the build."""
+    need_gpu()
+    wl = synth.kda(420, [70, 64, 129], 2, 2, 64, torch.bfloat16, gate_div=16.0, conv_w=4,
+                   name="kda-conv")
+    _check_build(wl, tol=2e-5)
+
+
+def test_kda_sampled_4096():
+    """KDA at a long segment length (2 x 4096 tokens, 32 value / 16 key heads,
+    d = 128, bf16), sampled (segment, head) units."""
+    need_gpu()
+    wl = synth.kda(430, [4096, 4096], 16, 32, 128, torch.bfloat16, gate_div=256.0,
+                   name="kda-gqa-2x4096")
+    _check_build(wl, segs=[1], heads=[0, 31], tol=2e-5, label="(sampled units)")
+
+
 def test_gdn_100_segments_seams_sampled():
     need_gpu()
     wl = synth.workload("gdn_d128_32h_100x1024_seams_bf16")
