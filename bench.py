@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "segment-build tokens/s + compositions/s per GPU, % of MFMA/HBM roofline"
 PEAK_MFMA_F16 = 2500.0     # TFLOP/s, MI355X dense fp16/bf16 matrix cores
 PEAK_HBM = 8000.0          # GB/s, MI355X HBM3E
+PEAK_MFMA_F32 = 157.3      # TFLOP/s, MI355X dense fp32 matrix cores
 
 # HBM traffic per launch comes from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
 # summarised in profiles/hbm_counters.md; a row counts only while the digest of
@@ -41,6 +42,7 @@ KERNEL_SOURCES = {
     "seam_ops_kernel": ["seam.h", "compose_split.hip", "common.h", "launch.h"],
     "compose_split_kernel": ["compose_split.hip", "seam.h", "common.h", "launch.h"],
     "compose_group_kernel": ["compose_group.hip", "seam.h", "common.h", "launch.h"],
+    "build_kda_kernel": ["build_kda.hip", "common.h", "launch.h"],
 }
 
 
@@ -177,7 +179,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--leg", choices=["build", "compose", "all"], default="all")
+    ap.add_argument("--leg", choices=["build", "compose", "kda", "all"], default="all")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -287,6 +289,38 @@ def main():
             out.update({"value": comp["compositions_per_s"], "unit": "compositions/s",
                         "ms_per_step": wall4,
                         "config": {"workload": comp["workload"]}, "roofline": comp["roofline"]})
+
+    if args.leg in ("kda", "all"):
+        log("generating the 32k-token prompt with diagonal gates (KDA; 8 x 4096, 32/16 heads, d=128, bf16)")
+        wl5 = synth.workload("kda_gqa_d128_8x4096_bf16")
+        dw5 = DeviceWorkload(wl5, dev)
+        T5 = torch.empty((wl5.n_seg, wl5.h_v, 128, 128), dtype=torch.float32, device=dev)
+        S05 = torch.empty_like(T5)
+        from state_caching_amd import segment_build
+
+        def step5(ev):
+            if ev: ev["kda"][0].record()
+            segment_build(dw5.rule, dw5.gate_kind, dw5.k, dw5.v, dw5.beta, dw5.gate,
+                          dw5.seg_start, dw5.seg_len, T_out=T5, S0_out=S05)
+            if ev: ev["kda"][1].record()
+
+        wall5, per5 = time_leg(step5, args.steps, args.warmup, torch, ["kda"])
+        k5 = sum(per5["kda"]) / len(per5["kda"])
+        # per token and value head: the gate on [T | S], k^T of it and the rank-one
+        # update, 5 d_k (d_k + d_v) flop
+        fl5 = 5.0 * wl5.n_tokens * wl5.h_v * wl5.d_k * (wl5.d_k + wl5.d_v)
+        ach5 = fl5 / (k5 * 1e-3) / 1e12
+        out["kda"] = {"workload": "cold prompt, delta rule with a diagonal gate (KDA), 32768 tokens = "
+                                  "8 segments x 4096, 32 value heads over 16 key heads, d = 128, bf16 "
+                                  "inputs, fp32 pairs",
+                      "ms_per_build": k5, "tokens_per_s": wl5.n_tokens / (k5 * 1e-3),
+                      "roofline": {"bound": "mfma", "kernel": "build_kda_kernel<128,bf16,bf16> (fp32 products)",
+                                   "achieved": ach5, "peak": PEAK_MFMA_F32, "unit": "TFLOP/s",
+                                   "frac": ach5 / PEAK_MFMA_F32,
+                                   "traffic": counter_traffic(["build_kda_kernel"], "kda_32k_prompt"),
+                                   "algorithmic_flop": fl5}}
+        del dw5, T5, S05
+        torch.cuda.empty_cache()
 
     if not args.no_cpu:
         log("timing the fp64 oracle on a bounded sample")
