@@ -18,7 +18,9 @@ steps the HYPIC reading notes describe:
   zero-padded only at the prompt start (the reference the composition must
   match, ch.2 sec.4);
 * naive addition of zero-initial end states and its structural error
-  (ch.1 sec.2, Eqs. (3)-(5), Table 2).
+  (ch.1 sec.2, Eqs. (3)-(5), Table 2);
+* rotary re-rotation of cached keys, K_b = R(b - a) K_a, and of the state of a
+  scalar-transition layer, S_{C|b} = R(b - a) S_{C|a} (ch.2 sec.6, Eqs. (7)-(8)).
 
 Readings of points the pages leave open are listed in the repository's
 design notes; the ones that shape code here: GQA value head h reads key head
@@ -85,6 +87,8 @@ class _Lib:
         lib.orc_causal_conv.argtypes = [ctypes.c_int] * 3 + [
             _d, ctypes.c_long, _d, ctypes.c_long, _d, _d, ctypes.c_long]
         lib.orc_l2norm_rows.argtypes = [ctypes.c_long, ctypes.c_int, _d, ctypes.c_long]
+        lib.orc_rope_rows.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_double, _d, _d]
         self.lib = lib
 
 
@@ -385,3 +389,25 @@ def angle_deg(x, ref):
         return 0.0 if nx == nr else 90.0
     c = float(np.dot(x, ref) / (nx * nr))
     return float(np.degrees(np.arccos(min(1.0, max(-1.0, c)))))
+
+
+def rope_rotate(x, delta, rot_dim=None, pairing=0, base=10000.0, path=None):
+    """R(delta) applied to the last axis of x (every vector; delta a scalar, or an
+    array broadcast over the leading axes).  rot_dim leading entries form the
+    rotated pairs (pairing 0: (i, i + rot_dim/2); 1: (2i, 2i + 1)), theta_i =
+    base^(-2i/rot_dim); the rest pass through.  fp64 copy returned."""
+    x = np.array(x, dtype=np.float64, copy=True)
+    d = x.shape[-1]
+    rot = d if rot_dim is None else int(rot_dim)
+    rows = np.ascontiguousarray(x.reshape(-1, d))
+    # delta: a scalar, or an array broadcast over the leading axes of x
+    dl = np.ascontiguousarray(np.broadcast_to(np.asarray(delta, dtype=np.float64), x.shape[:-1]).reshape(-1))
+    lib(path).lib.orc_rope_rows(rows.shape[0], d, rot, int(pairing), float(base), _dp(dl), _dp(rows))
+    return rows.reshape(x.shape)
+
+
+def rope_rotate_state(S, delta, rot_dim=None, pairing=0, base=10000.0, path=None):
+    """S [..., d_k, d_v] with R(delta) applied along d_k (every column of S), the
+    linear-state form of ch.2 sec.6, Eq. (7)."""
+    St = np.swapaxes(np.asarray(S, dtype=np.float64), -1, -2)
+    return np.swapaxes(rope_rotate(St, delta, rot_dim, pairing, base, path), -1, -2).copy()

@@ -20,6 +20,8 @@
  *                                                         (ch.2 sec.2, Eq. (6))
  *   causal conv       depthwise, width W, history = previous W-1 raw rows
  *                                                         (ch.2 sec.6)
+ *   rotary shift      x <- R(delta) x, pairs of entries turned by delta theta_i
+ *                                                         (ch.2 sec.6, Eqs. (7)-(8))
  *
  * Families (rule, gate):
  *   decay, scalar : T_i = g_i I,                 u_i = k_i v_i^T    (RetNet, Mamba2)
@@ -219,6 +221,34 @@ void orc_l2norm_rows(long n, int d, double *x, long ld)
         if (s > 0.0) {
             double inv = 1.0 / sqrt(s);
             for (i = 0; i < d; ++i) x[r * ld + i] *= inv;
+        }
+    }
+}
+
+/*
+ * Rotary re-rotation x <- R(delta_r) x of n row vectors of length d (row r at
+ * x + r * d).  The leading rot_dim entries form rot_dim / 2 pairs, pair i being
+ * entries (i, i + rot_dim/2) (pairing 0) or (2i, 2i + 1) (pairing 1); pair i is
+ * turned by the angle delta_r * theta_i, theta_i = base^(-2i / rot_dim):
+ *   (x1, x2) <- (x1 cos - x2 sin, x1 sin + x2 cos).
+ * Entries past rot_dim are unchanged.  Moving cached keys from start position
+ * a to b is delta = b - a (K_b = R(b - a) K_a, ch.2 sec.6, Eq. (8)).
+ */
+void orc_rope_rows(long n, int d, int rot_dim, int pairing, double base, const double *delta, double *x)
+{
+    long r;
+    int half = rot_dim / 2;
+    for (r = 0; r < n; ++r) {
+        double *v = x + r * d;
+        int i;
+        for (i = 0; i < half; ++i) {
+            double th = delta[r] * pow(base, -2.0 * (double)i / (double)rot_dim);
+            double c = cos(th), sn = sin(th);
+            int a = pairing == 0 ? i : 2 * i;
+            int b = pairing == 0 ? i + half : 2 * i + 1;
+            double x1 = v[a], x2 = v[b];
+            v[a] = x1 * c - x2 * sn;
+            v[b] = x1 * sn + x2 * c;
         }
     }
 }

@@ -271,6 +271,83 @@ def pin_kda_reductions(path):
     assert not np.allclose(Tf, np.diag(g[0]) @ P, rtol=0, atol=1e-6)
 
 
+def pin_rope(path):
+    """Rotary re-rotation (ch.2 sec.6, Eq. (8): K_b = R(b - a) K_a), against the
+    rotation's own algebra and a direct 2x2 construction:
+    - R(0) = I, R(b) R(a) = R(a + b), R(-a) R(a) = I, every pair keeps its norm;
+    - relative positions: <R(m) q, R(n) k> = <R(m - n) q, k>;
+    - the first pair turns by exactly delta radians (theta_0 = 1) and the last
+      by delta base^(-(rot-2)/rot), written out as 2x2 rotations;
+    - the interleaved pairing is the half pairing conjugated by the permutation
+      that interleaves the two halves; entries past rot_dim pass through;
+    - a key encoded at a + p and moved by b - a equals the key encoded at b + p."""
+    rng = np.random.default_rng(16)
+    d, base = 16, 10000.0
+    x = rng.standard_normal((5, d))
+    assert np.array_equal(oracle.rope_rotate(x, 0.0, path=path), x)
+    a, b = 37.0, -1250.0
+    xa = oracle.rope_rotate(x, a, path=path)
+    assert np.allclose(oracle.rope_rotate(xa, b, path=path), oracle.rope_rotate(x, a + b, path=path), atol=1e-12)
+    assert np.allclose(oracle.rope_rotate(xa, -a, path=path), x, atol=1e-13)
+    h = d // 2
+    n0 = x[:, :h] ** 2 + x[:, h:] ** 2
+    n1 = xa[:, :h] ** 2 + xa[:, h:] ** 2
+    assert np.allclose(n0, n1, rtol=1e-13)
+    q, k = rng.standard_normal(d), rng.standard_normal(d)
+    for m, n in ((3.0, 11.0), (1000.0, 7.0)):
+        lhs = oracle.rope_rotate(q, m, path=path) @ oracle.rope_rotate(k, n, path=path)
+        assert abs(lhs - oracle.rope_rotate(q, m - n, path=path) @ k) < 1e-12
+    th_last = 5.0 * base ** (-(d - 2) / d)
+    for i, th in ((0, 5.0), (h - 1, th_last)):
+        c, s_ = np.cos(th), np.sin(th)
+        y = oracle.rope_rotate(x, 5.0, path=path)
+        assert np.allclose(y[:, i], c * x[:, i] - s_ * x[:, i + h], atol=1e-14)
+        assert np.allclose(y[:, i + h], s_ * x[:, i] + c * x[:, i + h], atol=1e-14)
+    perm = np.empty(d, dtype=int)
+    perm[0::2], perm[1::2] = np.arange(h), np.arange(h) + h     # interleaved slot -> half slot
+    yi = oracle.rope_rotate(x[:, perm], 5.0, pairing=1, path=path)
+    assert np.allclose(yi, oracle.rope_rotate(x, 5.0, path=path)[:, perm], atol=1e-14)
+    yp = oracle.rope_rotate(x, 5.0, rot_dim=8, path=path)
+    assert np.array_equal(yp[:, 8:], x[:, 8:])
+    assert np.allclose(yp[:, :8], oracle.rope_rotate(x[:, :8], 5.0, path=path), atol=0)
+    pos = np.arange(6, dtype=np.float64)
+    kx = rng.standard_normal((6, d))
+    ka = oracle.rope_rotate(kx, 40.0 + pos, path=path)
+    kb = oracle.rope_rotate(kx, 900.0 + pos, path=path)
+    assert np.allclose(oracle.rope_rotate(ka, 860.0, path=path), kb, atol=1e-12)
+
+
+def pin_rope_state(path):
+    """Eq. (7), S_{C|b} = R(b - a) S_{C|a}: a segment whose keys carry RoPE at
+    positions a + p, moved to b + p.  Holds for the scalar transition (gamma I
+    commutes with R) and for the gated delta rule, whose transition is built
+    from the moved keys (T_C -> R T_C R^T); fails for a diagonal gate, which
+    does not commute with R."""
+    rng = np.random.default_rng(17)
+    m, d, dv = 9, 8, 3
+    k0 = rng.standard_normal((m, d))
+    k0 /= np.linalg.norm(k0, axis=1, keepdims=True)
+    v = rng.standard_normal((m, dv))
+    beta = rng.uniform(0.1, 0.9, m)
+    pa, pb = 100.0 + np.arange(m), 4321.0 + np.arange(m)
+    ka = oracle.rope_rotate(k0, pa, path=path)
+    kb = oracle.rope_rotate(k0, pb, path=path)
+    dlt = 4321.0 - 100.0
+    _, Sa, _ = one_unit(path, "decay", "scalar", ka, v, None, np.full(m, 0.97))
+    _, Sb, _ = one_unit(path, "decay", "scalar", kb, v, None, np.full(m, 0.97))
+    assert np.allclose(oracle.rope_rotate_state(Sa, dlt, path=path), Sb, atol=1e-12)
+    alpha = rng.uniform(0.6, 1.0, m)
+    Ta, Sa, _ = one_unit(path, "delta", "scalar", ka, v, beta, alpha)
+    Tb, Sb, _ = one_unit(path, "delta", "scalar", kb, v, beta, alpha)
+    assert np.allclose(oracle.rope_rotate_state(Sa, dlt, path=path), Sb, atol=1e-12)
+    R = oracle.rope_rotate_state(np.eye(d), dlt, path=path)
+    assert np.allclose(R @ Ta @ R.T, Tb, atol=1e-12)
+    g = rng.uniform(0.3, 1.0, (m, d))
+    _, Sa, _ = one_unit(path, "decay", "diag", ka, v, None, g)
+    _, Sb, _ = one_unit(path, "decay", "diag", kb, v, None, g)
+    assert not np.allclose(oracle.rope_rotate_state(Sa, dlt, path=path), Sb, atol=1e-6)
+
+
 def pin_conv(path):
     """Depthwise causal conv against numpy's full convolution, with history."""
     rng = np.random.default_rng(9)
@@ -345,4 +422,4 @@ def pin_readout(path):
 
 ALL = [pin_readout, pin_worked_example, pin_table2, pin_news_22pct, pin_naive_error_identity,
        pin_brute_force, pin_affine, pin_decay_closed_forms, pin_identity_transition,
-       pin_composition_laws, pin_gdn_bounds, pin_kda_reductions, pin_conv, pin_l2norm, pin_compose_equals_full]
+       pin_composition_laws, pin_gdn_bounds, pin_kda_reductions, pin_rope, pin_rope_state, pin_conv, pin_l2norm, pin_compose_equals_full]

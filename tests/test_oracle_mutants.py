@@ -31,6 +31,11 @@ MUTANTS = {
     "l2norm_no_sqrt": ("double inv = 1.0 / sqrt(s);", "double inv = 1.0 / s;"),
     "transition_init_not_identity": ("T[u * (long)dk * dk + (long)i * dk + i] = 1.0;",
                                      "T[u * (long)dk * dk + (long)i * dk + i] = 0.5;"),
+    "rope_sin_sign": ("v[a] = x1 * c - x2 * sn;", "v[a] = x1 * c + x2 * sn;"),
+    "rope_frequency_exponent": ("pow(base, -2.0 * (double)i / (double)rot_dim)",
+                                "pow(base, -1.0 * (double)i / (double)rot_dim)"),
+    "rope_half_pairing_offset": ("int b = pairing == 0 ? i + half : 2 * i + 1;",
+                                 "int b = pairing == 0 ? i + half - 1 : 2 * i + 1;"),
 }
 
 
