@@ -43,6 +43,7 @@ KERNEL_SOURCES = {
     "compose_split_kernel": ["compose_split.hip", "seam.h", "common.h", "launch.h"],
     "compose_group_kernel": ["compose_group.hip", "seam.h", "common.h", "launch.h"],
     "build_kda_kernel": ["build_kda.hip", "common.h", "launch.h"],
+    "rope_keys_kernel": ["rope.hip", "common.h", "launch.h"],
 }
 
 
@@ -179,7 +180,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--leg", choices=["build", "compose", "kda", "all"], default="all")
+    ap.add_argument("--leg", choices=["build", "compose", "kda", "rope", "all"], default="all")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -320,6 +321,35 @@ def main():
                                    "traffic": counter_traffic(["build_kda_kernel"], "kda_32k_prompt"),
                                    "algorithmic_flop": fl5}}
         del dw5, T5, S05
+        torch.cuda.empty_cache()
+
+    if args.leg in ("rope", "all"):
+        log("rotary re-rotation of the cached keys of a 32k-token prompt (16 heads, d=128, bf16)")
+        from state_caching_amd import rope_rerotate
+        g6 = torch.Generator(device="cpu").manual_seed(6)
+        n6, h6, d6 = 8 * 4096, 16, 128
+        K6 = torch.randn((n6, h6, d6), generator=g6).to(torch.bfloat16).to(dev)
+        K6o = torch.empty_like(K6)
+        st6, ln6 = [4096 * i for i in range(8)], [4096] * 8
+        dl6 = [4096 * i + 517 for i in range(8)]
+
+        def step6(ev):
+            if ev: ev["rope"][0].record()
+            rope_rerotate(K6, st6, ln6, dl6, out=K6o)
+            if ev: ev["rope"][1].record()
+
+        wall6, per6 = time_leg(step6, args.steps, args.warmup, torch, ["rope"])
+        k6 = sum(per6["rope"]) / len(per6["rope"])
+        by6 = 2.0 * K6.numel() * K6.element_size()     # every key read once and written once
+        gbs6 = by6 / (k6 * 1e-3) / 1e9
+        out["rope"] = {"workload": "cached full-attention keys of a 32768-token prompt (8 segments x 4096, "
+                                   "16 KV heads, d = 128, bf16) moved to new start positions, out of place",
+                       "ms_per_call": k6, "rows_per_s": n6 * h6 / (k6 * 1e-3),
+                       "roofline": {"bound": "hbm", "kernel": "rope_keys_kernel<bf16, half pairs>",
+                                    "achieved": gbs6, "peak": PEAK_HBM, "unit": "GB/s", "frac": gbs6 / PEAK_HBM,
+                                    "traffic": counter_traffic(["rope_keys_kernel"], "rope_32k_keys"),
+                                    "algorithmic_bytes": by6}}
+        del K6, K6o
         torch.cuda.empty_cache()
 
     if not args.no_cpu:

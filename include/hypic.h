@@ -16,6 +16,10 @@
  *                        tokens of an inner segment recomputed from the prefix
  *                        state, with the causal-conv warm-up from the previous
  *                        segment's tail rows (ch.2 secs.5-6)
+ *   hypic_rope_rerotate  move cached full-attention keys to their positions in
+ *                        the request, K_b = R(b - a) K_a (ch.2 sec.6, Eq. (8));
+ *                        hypic_rope_rerotate_state moves a scalar-transition
+ *                        state the same way (Eq. (7))
  *
  * Transition families (ch.2 sec.3, Table 1), chosen by (rule, gate_kind):
  *   DECAY + HEAD_CONST : T_i = gamma_h I,      u_i = k_i v_i^T  (RetNet)     T_C scalar
@@ -169,6 +173,59 @@ typedef struct {
  * HYPIC_E_UNSUPPORTED (rule, dimensions, w > 64), HYPIC_E_HIP.
  */
 hypic_status hypic_seam_advance(const hypic_seam_desc *d, float *S_inout, void *stream);
+
+/*
+ * hypic_rope_rerotate -- move cached full-attention keys to new positions
+ * (ch.2 sec.6, Eq. (8): K_b = R(b - a) K_a).  Keys stored from a segment-local
+ * start a are turned by R(delta) with delta = b - a, the segment's start in the
+ * request: for every row t in [seg_start[s], seg_start[s] + seg_len[s]) and head
+ *   x_out[t, head, :] = R(delta[s]) x_in[t, head, :].
+ * R(delta) turns pair i of the leading rot_dim entries by delta * theta_i,
+ * theta_i = base^(-2 i / rot_dim); pairing HYPIC_ROPE_HALF pairs entries
+ * (i, i + rot_dim/2), HYPIC_ROPE_INTERLEAVED pairs (2i, 2i + 1).  Entries past
+ * rot_dim are copied (x_out != x_in) or left as they are (in place).  The angle
+ * is reduced modulo 2 pi in double precision; cos and sin are then rounded to
+ * fp32 (relative error ~1e-7 per element; bf16 data is rounded once on output).
+ *
+ *   x_in, x_out [N, h, d], dtype HYPIC_F32 or HYPIC_BF16; x_out may equal x_in
+ *   seg_start, seg_len, delta  HOST [n_seg]
+ *   d in 8 .. 512, d % 8 == 0; rot_dim % 8 == 0, 8 <= rot_dim <= d; base > 0
+ *
+ * Rows of different segments must not overlap.  Errors: HYPIC_E_INVALID,
+ * HYPIC_E_UNSUPPORTED (d, rot_dim), HYPIC_E_HIP.
+ */
+typedef enum { HYPIC_ROPE_HALF = 0, HYPIC_ROPE_INTERLEAVED = 1 } hypic_rope_pairing;
+
+typedef struct {
+    int32_t n_seg;
+    const int64_t *seg_start;   /* HOST [n_seg] */
+    const int64_t *seg_len;     /* HOST [n_seg] */
+    const int64_t *delta;       /* HOST [n_seg]: new start minus cached start */
+    int32_t h, d, rot_dim, pairing;
+    int32_t dtype;              /* hypic_dtype of x_in and x_out */
+    double base;
+    const void *x_in;
+    void *x_out;
+} hypic_rope_desc;
+
+hypic_status hypic_rope_rerotate(const hypic_rope_desc *d, void *stream);
+
+/*
+ * hypic_rope_rerotate_state -- the state of a scalar-transition layer whose
+ * keys carry RoPE, moved from start a to b (ch.2 sec.6, Eq. (7)):
+ *   S_out[head] = R(delta) S_in[head]   (R acting on the d_k rows)
+ * with R(delta) as in hypic_rope_rerotate.  The identity holds for a scalar
+ * transition (gamma I commutes with R); a diagonal gate does not commute with
+ * R, and the identity does not hold there (the caller's responsibility).
+ *
+ *   S_in, S_out [h, d_k, d_v] fp32 (S_out may equal S_in); d_v % 4 == 0,
+ *   rot_dim % 8 == 0, 8 <= rot_dim <= d_k, d_k <= 512
+ *
+ * Errors: HYPIC_E_INVALID, HYPIC_E_UNSUPPORTED, HYPIC_E_HIP.
+ */
+hypic_status hypic_rope_rerotate_state(int32_t h, int32_t d_k, int32_t d_v, int32_t rot_dim,
+                                       int32_t pairing, double base, int64_t delta,
+                                       const float *S_in, float *S_out, void *stream);
 
 /*
  * hypic_compose -- fold cached pairs into a running state (Eq. (6)):

@@ -56,6 +56,12 @@ class SeamDesc(ctypes.Structure):
                 ("q", _vp), ("o", _vp), ("T_w", _vp), ("S_w0", _vp)]
 
 
+class RopeDesc(ctypes.Structure):
+    _fields_ = [("n_seg", _i32), ("seg_start", _pi64), ("seg_len", _pi64), ("delta", _pi64),
+                ("h", _i32), ("d", _i32), ("rot_dim", _i32), ("pairing", _i32), ("dtype", _i32),
+                ("base", ctypes.c_double), ("x_in", _vp), ("x_out", _vp)]
+
+
 class ComposeDesc(ctypes.Structure):
     _fields_ = [("tform", _i32), ("prec", _i32), ("h_v", _i32), ("d_k", _i32), ("d_v", _i32),
                 ("n", _i32), ("n_slots", _i32), ("order", _pi32),
@@ -84,6 +90,11 @@ def _lib():
         lib.hypic_compose.restype = ctypes.c_int
         lib.hypic_seam_advance.argtypes = [ctypes.POINTER(SeamDesc), _vp, _vp]
         lib.hypic_seam_advance.restype = ctypes.c_int
+        lib.hypic_rope_rerotate.argtypes = [ctypes.POINTER(RopeDesc), _vp]
+        lib.hypic_rope_rerotate.restype = ctypes.c_int
+        lib.hypic_rope_rerotate_state.argtypes = [_i32, _i32, _i32, _i32, _i32, ctypes.c_double,
+                                                  ctypes.c_int64, _vp, _vp, _vp]
+        lib.hypic_rope_rerotate_state.restype = ctypes.c_int
         lib.hypic_workspace_size.argtypes = [_vp, ctypes.c_int]
         lib.hypic_workspace_size.restype = ctypes.c_size_t
         lib.hypic_status_string.argtypes = [ctypes.c_int]
@@ -299,3 +310,44 @@ def seam_advance(S: torch.Tensor, seams: Seams, stream=None):
            "hypic_seam_advance")
     return S
 
+
+ROPE_HALF, ROPE_INTERLEAVED = 0, 1
+
+
+def rope_rerotate(x: torch.Tensor, seg_start: Sequence[int], seg_len: Sequence[int],
+                  delta: Sequence[int], rot_dim: Optional[int] = None, pairing: int = ROPE_HALF,
+                  base: float = 10000.0, out: Optional[torch.Tensor] = None, stream=None):
+    """Cached keys x [N, h, d] (fp32 or bf16) moved to new positions: rows of
+    segment s turned by R(delta[s]) (hypic_rope_rerotate).  out=None: in place."""
+    if x.dim() != 3:
+        raise ValueError("x must be [N, h, d]")
+    if out is None:
+        out = x
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x")
+    n = len(seg_start)
+    if len(seg_len) != n or len(delta) != n:
+        raise ValueError("seg_start, seg_len and delta must have one entry per segment")
+    ss, sl, dl = _i64_array(seg_start), _i64_array(seg_len), _i64_array(delta)
+    d = RopeDesc(n_seg=n, seg_start=ctypes.cast(ss, _pi64), seg_len=ctypes.cast(sl, _pi64),
+                 delta=ctypes.cast(dl, _pi64), h=x.shape[1], d=x.shape[2],
+                 rot_dim=x.shape[2] if rot_dim is None else int(rot_dim), pairing=int(pairing),
+                 dtype=_dtype_code(x), base=float(base), x_in=_ptr(x), x_out=_ptr(out))
+    _check(_lib().hypic_rope_rerotate(ctypes.byref(d), _stream(stream)), "hypic_rope_rerotate")
+    return out
+
+
+def rope_rerotate_state(S: torch.Tensor, delta: int, rot_dim: Optional[int] = None,
+                        pairing: int = ROPE_HALF, base: float = 10000.0,
+                        out: Optional[torch.Tensor] = None, stream=None):
+    """States S [h, d_k, d_v] fp32 turned by R(delta) along d_k
+    (hypic_rope_rerotate_state).  out=None: in place."""
+    if S.dim() != 3 or S.dtype != torch.float32:
+        raise ValueError("S must be fp32 [h, d_k, d_v]")
+    if out is None:
+        out = S
+    h, d_k, d_v = S.shape
+    _check(_lib().hypic_rope_rerotate_state(h, d_k, d_v, d_k if rot_dim is None else int(rot_dim),
+                                            int(pairing), float(base), int(delta), _ptr(S), _ptr(out),
+                                            _stream(stream)), "hypic_rope_rerotate_state")
+    return out

@@ -3,6 +3,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 
 #include "hypic.h"
@@ -376,6 +377,60 @@ hypic_status hypic_compose(const hypic_compose_desc *d, void *ws, size_t ws_byte
         if (st != HYPIC_OK) return st;
     }
     return HYPIC_OK;
+}
+
+hypic_status hypic_rope_rerotate(const hypic_rope_desc *d, void *stream)
+{
+    if (!d || d->n_seg < 0 || d->h <= 0) return HYPIC_E_INVALID;
+    if (d->dtype != HYPIC_F32 && d->dtype != HYPIC_BF16) return HYPIC_E_INVALID;
+    if (d->pairing != HYPIC_ROPE_HALF && d->pairing != HYPIC_ROPE_INTERLEAVED) return HYPIC_E_INVALID;
+    if (!(d->base > 0.0) || !std::isfinite(d->base)) return HYPIC_E_INVALID;
+    if (d->d < 8 || d->d > 512 || d->d % 8 != 0) return HYPIC_E_UNSUPPORTED;
+    if (d->rot_dim < 8 || d->rot_dim > d->d || d->rot_dim % 8 != 0) return HYPIC_E_UNSUPPORTED;
+    if (d->n_seg == 0) return HYPIC_OK;
+    if (!d->seg_start || !d->seg_len || !d->delta) return HYPIC_E_INVALID;
+    if (!d->x_in || !d->x_out || !aligned16(d->x_in) || !aligned16(d->x_out)) return HYPIC_E_INVALID;
+    for (int i = 0; i < d->n_seg; ++i)
+        if (d->seg_start[i] < 0 || d->seg_len[i] < 0 || d->seg_len[i] > INT32_MAX) return HYPIC_E_INVALID;
+    hypic_status st = device_check();
+    if (st != HYPIC_OK) return st;
+    RopeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.x_in = d->x_in; a.x_out = d->x_out;
+    a.h = d->h; a.d = d->d; a.rot = d->rot_dim; a.pairing = d->pairing;
+    a.copy_rest = d->x_out != d->x_in && d->rot_dim < d->d;
+    a.log2_base = std::log2(d->base);
+    for (int b = 0; b < d->n_seg; b += kMaxSeg) {
+        const int nb = std::min(kMaxSeg, d->n_seg - b);
+        for (int i = 0; i < nb; ++i) {
+            a.start[i] = d->seg_start[b + i];
+            a.len[i] = d->seg_len[b + i];
+            a.delta[i] = d->delta[b + i];
+        }
+        if ((st = from_hip(launch_rope_keys(a, d->dtype == HYPIC_BF16, nb, reinterpret_cast<hipStream_t>(stream)))) != HYPIC_OK)
+            return st;
+    }
+    return HYPIC_OK;
+}
+
+hypic_status hypic_rope_rerotate_state(int32_t h, int32_t d_k, int32_t d_v, int32_t rot_dim, int32_t pairing,
+                                       double base, int64_t delta, const float *S_in, float *S_out, void *stream)
+{
+    if (h <= 0 || d_v <= 0 || !S_in || !S_out || !aligned16(S_in) || !aligned16(S_out)) return HYPIC_E_INVALID;
+    if (pairing != HYPIC_ROPE_HALF && pairing != HYPIC_ROPE_INTERLEAVED) return HYPIC_E_INVALID;
+    if (!(base > 0.0) || !std::isfinite(base)) return HYPIC_E_INVALID;
+    if (d_k < 8 || d_k > 512 || d_v % 4 != 0) return HYPIC_E_UNSUPPORTED;
+    if (rot_dim < 8 || rot_dim > d_k || rot_dim % 8 != 0) return HYPIC_E_UNSUPPORTED;
+    hypic_status st = device_check();
+    if (st != HYPIC_OK) return st;
+    RopeStateArgs a;
+    memset(&a, 0, sizeof(a));
+    a.S_in = S_in; a.S_out = S_out;
+    a.h = h; a.d_k = d_k; a.d_v = d_v; a.rot = rot_dim; a.pairing = pairing;
+    a.copy_rest = S_out != S_in && rot_dim < d_k;
+    a.log2_base = std::log2(base);
+    a.delta = delta;
+    return from_hip(launch_rope_state(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
 hypic_status hypic_seam_advance(const hypic_seam_desc *d, float *S_inout, void *stream)

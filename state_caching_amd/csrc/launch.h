@@ -82,6 +82,27 @@ struct ComposeArgs {
     int32_t order[kMaxSeg];
 };
 
+// Rotary re-rotation of cached keys [N, h, d], per segment shift delta.
+struct RopeArgs {
+    const void *x_in;
+    void *x_out;
+    int h, d, rot, pairing, copy_rest;   // pairing 0: (i, i + rot/2); 1: (2i, 2i + 1)
+    double log2_base;
+    int64_t start[kMaxSeg], len[kMaxSeg], delta[kMaxSeg];
+};
+
+// Rotary re-rotation of states [h, d_k, d_v] fp32 along d_k.
+struct RopeStateArgs {
+    const float *S_in;
+    float *S_out;
+    int h, d_k, d_v, rot, pairing, copy_rest;
+    double log2_base;
+    int64_t delta;
+};
+
+hipError_t launch_rope_keys(const RopeArgs &a, int dtype_bf16, int n_seg, hipStream_t st);
+hipError_t launch_rope_state(const RopeStateArgs &a, hipStream_t st);
+
 hipError_t launch_build_delta(const DeltaArgs &a, int D, int kv_kind, int g_kind, bool f16,
                               int n_units, hipStream_t st);
 hipError_t launch_build_delta_f16(const DeltaArgs &a, int D, int kv_kind, int g_kind, int n_units,

@@ -155,3 +155,47 @@ def test_binding_rejects_out_of_range_rows(sca):
     with pytest.raises(ValueError):
         sca.segment_build(sca.RULE_DELTA, sca.GATE_SCALAR, k, torch.zeros(10, 1, 16),
                           torch.zeros(10, 1), torch.ones(10, 1), [5], [6])
+
+
+def _rope_desc(sca, **over):
+    ss = (ctypes.c_int64 * 1)(0)
+    sl = (ctypes.c_int64 * 1)(4)
+    dl = (ctypes.c_int64 * 1)(7)
+    f = dict(n_seg=1, seg_start=ctypes.cast(ss, ctypes.POINTER(ctypes.c_int64)),
+             seg_len=ctypes.cast(sl, ctypes.POINTER(ctypes.c_int64)),
+             delta=ctypes.cast(dl, ctypes.POINTER(ctypes.c_int64)), h=2, d=64, rot_dim=64,
+             pairing=0, dtype=sca.BF16, base=10000.0, x_in=ctypes.c_void_p(4096),
+             x_out=ctypes.c_void_p(4096))
+    f.update(over)
+    d = sca.RopeDesc(**f)
+    d._keep = (ss, sl, dl)
+    return d
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(d=60, rot_dim=56), -2),            # d not a multiple of 8
+    (dict(rot_dim=12), -2),                  # rot_dim not a multiple of 8
+    (dict(rot_dim=72), -2),                  # rot_dim > d
+    (dict(d=1024, rot_dim=64), -2),
+    (dict(pairing=2), -1),
+    (dict(dtype=7), -1),
+    (dict(base=0.0), -1),
+    (dict(base=float("inf")), -1),
+    (dict(h=0), -1),
+    (dict(x_in=ctypes.c_void_p(4100)), -1),  # misaligned
+    (dict(x_out=None), -1),
+    (dict(seg_len=None), -1),
+])
+def test_rope_validation(sca, over, code):
+    d = _rope_desc(sca, **over)
+    assert sca.library().hypic_rope_rerotate(ctypes.byref(d), None) == code
+
+
+def test_rope_state_validation(sca):
+    L = sca.library()
+    p = ctypes.c_void_p(4096)
+    assert L.hypic_rope_rerotate_state(2, 64, 62, 64, 0, 10000.0, 5, p, p, None) == -2   # d_v % 4
+    assert L.hypic_rope_rerotate_state(2, 64, 64, 20, 0, 10000.0, 5, p, p, None) == -2   # rot_dim % 8
+    assert L.hypic_rope_rerotate_state(2, 64, 64, 64, 3, 10000.0, 5, p, p, None) == -1   # pairing
+    assert L.hypic_rope_rerotate_state(2, 64, 64, 64, 0, -1.0, 5, p, p, None) == -1     # base
+    assert L.hypic_rope_rerotate_state(2, 64, 64, 64, 0, 10000.0, 5, None, p, None) == -1

@@ -414,6 +414,101 @@ def test_kda_sampled_4096():
     _check_build(wl, segs=[1], heads=[0, 31], tol=2e-5, label="(sampled units)")
 
 
+# ------------------------------------------------------------- rotary re-rotation
+
+@pytest.mark.parametrize("dtype,pairing,rot,inplace", [
+    (torch.float32, 0, 128, False), (torch.float32, 1, 128, True), (torch.bfloat16, 0, 128, True),
+    (torch.bfloat16, 1, 64, False), (torch.float32, 0, 96, False), (torch.bfloat16, 0, 8, True)])
+def test_rope_keys(dtype, pairing, rot, inplace):
+    """Cached keys moved to new positions (Eq. (8)) against the oracle: several
+    segments with their own shifts (negative, zero, 1e5), an empty one, partial
+    rotary width, both pairings, in place and out of place."""
+    need_gpu()
+    import state_caching_amd as sca
+    rng = np.random.default_rng(500 + rot + pairing)
+    h, d = 3, 128
+    starts, lens, deltas = [0, 37, 37, 300], [37, 0, 263, 129], [4096, 11, -250, 100000]
+    x64 = rng.standard_normal((429, h, d))
+    x = torch.from_numpy(x64).to(torch.float32).to(dtype)
+    xin = x.cuda()
+    out = None if inplace else torch.empty_like(xin)
+    case(f"rope keys {dtype} pairing={pairing} rot={rot} inplace={inplace}")
+    y = sca.rope_rerotate(xin, starts, lens, deltas, rot_dim=rot, pairing=pairing, out=out)
+    torch.cuda.synchronize()
+    xr = np64(x)
+    ref = xr.copy()
+    for s0, n, dl in zip(starts, lens, deltas):
+        ref[s0:s0 + n] = oracle.rope_rotate(xr[s0:s0 + n], float(dl), rot_dim=rot, pairing=pairing)
+    got = np64(y)
+    if dtype == torch.float32:
+        e = oracle.relF(got, ref)
+        print(f"  relF {e:.3e}")
+        assert e <= 1e-6
+    else:
+        # bf16: the oracle's value rounded once; an fp32 computation may land on the
+        # other side of a rounding boundary, one unit in the last place at most
+        rb = np64(torch.from_numpy(ref).to(torch.float32).to(torch.bfloat16))
+        # one bf16 unit in the last place of the larger of the two values, plus the
+        # fp32 arithmetic of the rotation (cos, sin and the two products rounded):
+        # at most 2^-22 (|x1| + |x2|) for a rotated entry whose pair is (x1, x2)
+        mag = np.maximum(np.maximum(np.abs(rb), np.abs(got)), 2.0 ** -126)
+        ulp = 2.0 ** (np.floor(np.log2(mag)) - 7)
+        idx = np.arange(d)
+        part = np.where(idx < rot, (idx + rot // 2) % rot if pairing == 0 else idx ^ 1, idx)
+        arith = np.where(idx < rot, 2.0 ** -22, 0.0) * (np.abs(xr) + np.abs(xr[..., part]))
+        diff = np.abs(got - rb)
+        frac = np.mean(diff > 0)
+        print(f"  elements differing from the rounded oracle: {frac:.2e}, "
+              f"max {np.max(diff / (ulp + arith)):.2f} of the bound")
+        assert np.all(diff <= ulp + arith) and frac < 1e-3
+        assert oracle.relF(got, ref) <= 2e-3
+    if rot < d:
+        assert np.array_equal(got[..., rot:], xr[..., rot:])
+
+
+@pytest.mark.parametrize("pairing,rot", [(0, 128), (1, 64)])
+def test_rope_state(pairing, rot):
+    """A state moved along its key dimension (Eq. (7)) against the oracle."""
+    need_gpu()
+    import state_caching_amd as sca
+    S = synth.random_state(510 + rot, 4, 128, 128)
+    out = torch.empty_like(S).cuda()
+    case(f"rope state pairing={pairing} rot={rot}")
+    sca.rope_rerotate_state(S.cuda(), 77777, rot_dim=rot, pairing=pairing, out=out)
+    torch.cuda.synchronize()
+    ref = oracle.rope_rotate_state(np64(S), 77777.0, rot_dim=rot, pairing=pairing)
+    e = oracle.relF(np64(out), ref)
+    print(f"  relF {e:.3e}")
+    assert e <= 1e-6
+
+
+def test_rope_state_identity_on_gpu():
+    """Eq. (7) end to end on the GPU: a scalar-decay segment whose keys carry RoPE
+    from start a, built; the same segment moved to start b (its keys re-rotated
+    by the key kernel), built again; the first state moved by the state kernel
+    equals the second."""
+    need_gpu()
+    import state_caching_amd as sca
+    from state_caching_amd.runner import DeviceWorkload
+    wl = synth.retnet(520, [200], 4, 64)
+    dw = DeviceWorkload(wl)
+    pos = list(range(200))
+    ka = sca.rope_rerotate(dw.k.clone(), [p for p in pos], [1] * 200, [1000 + p for p in pos])
+    kb = sca.rope_rerotate(ka.clone(), [0], [200], [5000 - 1000])
+    case("rope state identity, scalar decay")
+
+    def build(k):
+        T, S0 = sca.segment_build(dw.rule, dw.gate_kind, k, dw.v, None, dw.gate, [0], [200])
+        return S0
+
+    Sa, Sb = build(ka), build(kb)
+    Sm = sca.rope_rerotate_state(Sa[0].clone(), 4000)
+    torch.cuda.synchronize()
+    e = oracle.relF(np64(Sm), np64(Sb[0]))
+    print(f"  relF {e:.3e}")
+    assert e <= 1e-5
+
+
 def test_gdn_100_segments_seams_sampled():
     need_gpu()
     wl = synth.workload("gdn_d128_32h_100x1024_seams_bf16")
