@@ -211,7 +211,7 @@ def gla(seed, seg_len, h, d, dtype=torch.bfloat16, literal=True, name="gla"):
 WORKLOADS = ("gdn_d16_2x64_fp32", "retnet_d64_8h_4x256_fp32", "gla_d128_16h_8x512_bf16",
              "gdn_gqa_d128_8x4096_bf16", "gdn_d128_32h_100x1024_seams_bf16",
              "gla_d128_16h_8x512_bf16_slow", "gdn_gqa_d128_8x4096_bf16_slow",
-             "kda_gqa_d128_8x4096_bf16")
+             "kda_gqa_d128_8x4096_bf16", "gdn_d128_32h_100x1024_seams_bf16_slow")
 
 
 def workload(name: str) -> Workload:
@@ -229,6 +229,9 @@ def workload(name: str) -> Workload:
         return gdn(4, [1024] * 100, 32, 32, 128, torch.bfloat16, conv_w=4, seam_w=8, name=name)
     if name == "gla_d128_16h_8x512_bf16_slow":
         return gla(2, [512] * 8, 16, 128, literal=False, name=name)
+    if name == "gdn_d128_32h_100x1024_seams_bf16_slow":
+        return gdn(4, [1024] * 100, 32, 32, 128, torch.bfloat16, alpha_div=1024.0, conv_w=4, seam_w=8,
+                   name=name)
     if name == "kda_gqa_d128_8x4096_bf16":
         return kda(5, [4096] * 8, 16, 32, 128, torch.bfloat16, name=name)
     if name == "gdn_gqa_d128_8x4096_bf16_slow":

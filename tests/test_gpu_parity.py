@@ -366,6 +366,33 @@ def test_group_compose_seams_across_launches():
     assert e <= 2e-5
 
 
+def test_gdn_100_segments_seams_slow_group_compose():
+    """The 100-segment prompt with slow decay (alpha = exp(-softplus(z)/1024), so
+    T_C stays far from 0 and every group pair carries the earlier positions):
+    the automatic two-level compose, in the bench's launch configuration, against
+    the oracle's sequential composition of the same GPU-built pairs with the same
+    windows, on sampled heads; and against the serial GPU fold on all heads."""
+    need_gpu()
+    wl = synth.workload("gdn_d128_32h_100x1024_seams_bf16_slow")
+    sca, DW = _lib()
+    dw = DW(wl)
+    T, S0 = dw.build()
+    case("100-segment slow-decay compose, two-level (automatic) and serial")
+    S = dw.compose(T, S0)
+    S_ser = dw.compose(T, S0, group_len=1)
+    torch.cuda.synchronize()
+    heads = [3, 30]
+    Tn, Sn = np64(T)[:, heads], np64(S0)[:, heads]
+    S_or = oracle.compose(Tn, Sn, wl=wl, heads=heads, seams=True)
+    e1 = oracle.relF(np64(S)[heads], S_or)
+    e2 = oracle.relF(np64(S), np64(S_ser))
+    tn = float(np.linalg.norm(np64(T)[-1, heads[0]]))
+    print(f"  ||T_C|| (last segment, head {heads[0]}) {tn:.3e}; relF vs oracle compose {e1:.3e}, "
+          f"vs serial GPU fold {e2:.3e}")
+    assert tn > 1e-3
+    assert e1 <= 2e-5 and e2 <= 2e-5
+
+
 # --------------------------------------------- delta rule with a diagonal gate (KDA)
 
 @pytest.mark.parametrize("d,dtype", [(16, torch.float32), (32, torch.bfloat16), (64, torch.float32),
