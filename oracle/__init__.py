@@ -326,35 +326,57 @@ def build_pairs(wl, segs=None, heads=None, path=None):
     return T, S0
 
 
-def recur_range(wl, start, end, S, heads=None, path=None):
+def recur_range(wl, start, end, S, heads=None, path=None, q=None):
     """Advance per-head states S [len(heads), d_k, d_v] over tokens [start, end).
 
     For conv workloads the history is the concatenation's previous W-1 raw
     rows (the cached segment-tail conv state at a seam; zeros at token 0).
+    With q [end - start, h_k, d_k] (final queries of those tokens, all key
+    heads) also returns the read-outs o_t = q_t^T S_t with the post-update
+    state (Eq. (2)), [end - start, len(heads), d_v]: (S, o).
     """
     sl = Slice(wl, start, end, heads, path=path)
     S = np.array(S, dtype=np.float64, copy=True, order="C")
-    recur_units(wl.rule, sl.gate_kind, sl.units(), wl.d_k, wl.d_v,
-                sl.k, sl.v, sl.beta, sl.g, S, path=path)
-    return S
+    if q is None:
+        recur_units(wl.rule, sl.gate_kind, sl.units(), wl.d_k, wl.d_v,
+                    sl.k, sl.v, sl.beta, sl.g, S, path=path)
+        return S
+    u = sl.units()
+    qs = np.ascontiguousarray(_f64(q)[:, sl.kheads])   # laid out like sl.k
+    o = np.zeros((sl.n, len(sl.heads), wl.d_v))         # laid out like sl.v
+    recur_units(wl.rule, sl.gate_kind, u, wl.d_k, wl.d_v, sl.k, sl.v, sl.beta, sl.g, S,
+                q=qs, o=o, off_q=u.off_k, ldq=u.ldk, off_o=u.off_v, ldo=u.ldv, path=path)
+    return S, o
 
 
-def compose(T, S0, S_init=None, wl=None, heads=None, seams=False, path=None):
+def compose(T, S0, S_init=None, wl=None, heads=None, seams=False, path=None, q=None):
     """Fold S <- T_j S + S0_j over j in prompt order (Eq. (6)).
 
     T, S0: [n, H, ...] dense fp64 (expand_dense turns scalar/diag forms into
     dense).  With seams=True (needs wl) the seam window of each inner
-    segment is advanced token by token from the running state first.
+    segment is advanced token by token from the running state first.  With
+    q [n - 1, w, h_k, d_k] (the final queries of every window, seams=True)
+    the windows also read out o_t = q_t^T S_t as they advance (ch.2 sec.5:
+    the recomputed tokens produce their outputs from the true prefix state);
+    returns (S, o) with o [n - 1, w, len(heads), d_v].
     """
     n, H, dk, dv = S0.shape
     S = np.zeros((H, dk, dv)) if S_init is None else np.array(S_init, dtype=np.float64)
     wins = wl.window_ranges() if seams else []
+    outs = []
     for j in range(n):
         if seams and j > 0:
             s, e = wins[j - 1]
-            S = recur_range(wl, s, e, S, heads=heads, path=path)
+            if q is None:
+                S = recur_range(wl, s, e, S, heads=heads, path=path)
+            else:
+                S, oj = recur_range(wl, s, e, S, heads=heads, path=path, q=q[j - 1])
+                outs.append(oj)
         apply_pair(np.ascontiguousarray(T[j]), np.ascontiguousarray(S0[j]), S, path)
-    return S
+    if q is None:
+        return S
+    o = np.stack(outs) if outs else np.zeros((0, 0, H, dv))
+    return S, o
 
 
 def full_recompute(wl, S_init=None, heads=None, path=None):

@@ -420,6 +420,33 @@ def pin_readout(path):
         assert np.allclose(S[0], S_ref, atol=1e-13)
 
 
-ALL = [pin_readout, pin_worked_example, pin_table2, pin_news_22pct, pin_naive_error_identity,
+def pin_compose_readouts(path):
+    """Read-outs of the seam windows along a composed chain equal the read-outs
+    of the full token recurrence at the same tokens (ch.2 sec.5: the recomputed
+    window tokens see the true prefix state; Eq. (2)), GQA heads and a subset
+    of value heads included."""
+    import synth
+    import torch
+    rng = np.random.default_rng(15)
+    for seam_w, heads in ((8, None), (3, [1])):
+        wl = synth.gdn(16, [40, 37, 45, 30], 1, 2, 8, torch.float32, alpha_div=32.0,
+                       conv_w=4, seam_w=seam_w)
+        q_all = rng.standard_normal((wl.n_tokens, wl.h_k, wl.d_k))
+        hs = list(range(wl.h_v)) if heads is None else heads
+        _, o_full = oracle.recur_range(wl, 0, wl.n_tokens, np.zeros((len(hs), wl.d_k, wl.d_v)),
+                                       heads=hs, path=path, q=q_all)
+        wins = wl.window_ranges()
+        q_win = np.stack([q_all[s:e] for s, e in wins])
+        T, S0 = oracle.build_pairs(wl, heads=hs, path=path)
+        S, o = oracle.compose(T, S0, wl=wl, heads=hs, seams=True, path=path, q=q_win)
+        assert o.shape == (len(wins), seam_w, len(hs), wl.d_v)
+        for j, (s, e) in enumerate(wins):
+            assert oracle.relF(o[j], o_full[s:e]) < 1e-12, (seam_w, j)
+        S_full = oracle.recur_range(wl, 0, wl.n_tokens, np.zeros((len(hs), wl.d_k, wl.d_v)),
+                                    heads=hs, path=path)
+        assert oracle.relF(S, S_full) < 1e-12
+
+
+ALL = [pin_readout, pin_compose_readouts, pin_worked_example, pin_table2, pin_news_22pct, pin_naive_error_identity,
        pin_brute_force, pin_affine, pin_decay_closed_forms, pin_identity_transition,
        pin_composition_laws, pin_gdn_bounds, pin_kda_reductions, pin_rope, pin_rope_state, pin_conv, pin_l2norm, pin_compose_equals_full]
