@@ -109,8 +109,20 @@ bool compose_uses_split(const hypic_compose_desc *d)
 // Group length of the two-level compose for a launch of nb positions (1: the
 // serial fold).  Automatic (group_len 0): enough (group, head) workgroups to
 // fill the chip once, when the serial fold is long enough to gain from it.
+// window read-outs requested (seam q / o)
+bool compose_readouts(const hypic_compose_desc *d) { return d->seams && d->seams->q && d->seams->o; }
+
 int compose_group_len(const hypic_compose_desc *d, int nb)
 {
+    if (compose_readouts(d) && compose_uses_split(d)) {
+        // read-outs ride on the group kernel: every launch takes the two-level
+        // path, one group for a short launch
+        if (d->group_len >= 1) return std::min(d->group_len, std::max(nb, 1));
+        if (nb < 16) return std::max(nb, 1);
+        const int per_cu = d->d_k == 128 ? 1 : 2;
+        const int ng = std::max(1, 256 * per_cu / d->h_v);
+        return (nb + ng - 1) / ng;
+    }
     if (!compose_uses_split(d) || nb < 2 || d->group_len == 1) return 1;
     if (d->seams && d->seams->w > 8) return 1;   // the group kernel holds windows of up to 8 rows
     if (d->group_len > 1) return std::min(d->group_len, nb);
@@ -129,7 +141,7 @@ int compose_max_groups(const hypic_compose_desc *d)
     for (int nb : sizes) {
         if (nb <= 0) continue;
         const int G = compose_group_len(d, nb);
-        if (G > 1) best = std::max(best, (nb + G - 1) / G);
+        if (G > 1 || (compose_readouts(d) && compose_uses_split(d))) best = std::max(best, (nb + G - 1) / G);
     }
     return best;
 }
@@ -140,7 +152,8 @@ size_t ws_align(size_t b) { return (b + 255) & ~(size_t)255; }
 size_t compose_ops_bytes(const hypic_compose_desc *d)
 {
     if (!d->seams || !compose_uses_split(d) || d->n <= 1) return 0;
-    return ws_align((size_t)seam_ops_floats(d->d_k, d->seams->w, d->n - 1, d->h_v) * sizeof(float));
+    return ws_align((size_t)seam_ops_floats(d->d_k, d->seams->w, d->n - 1, d->h_v, compose_readouts(d)) *
+                    sizeof(float));
 }
 
 size_t compose_group_bytes(const hypic_compose_desc *d)
@@ -148,9 +161,17 @@ size_t compose_group_bytes(const hypic_compose_desc *d)
     return (size_t)compose_max_groups(d) * d->h_v * d->d_k * d->d_v * sizeof(float);
 }
 
+// read-outs of the two-level path: the rows Y [n - 1, h_v, 8, 2 d] and the
+// states entering the groups [groups, h_v, d, d]
+size_t compose_readout_bytes(const hypic_compose_desc *d)
+{
+    if (!compose_readouts(d) || !compose_uses_split(d) || d->n <= 1) return 0;
+    return ws_align((size_t)(d->n - 1) * d->h_v * 8 * 2 * d->d_k * sizeof(float)) + compose_group_bytes(d);
+}
+
 size_t compose_ws_bytes(const hypic_compose_desc *d)
 {
-    return compose_ops_bytes(d) + 2 * compose_group_bytes(d);
+    return compose_ops_bytes(d) + 2 * compose_group_bytes(d) + compose_readout_bytes(d);
 }
 
 SeamArgs seam_args(const hypic_seam_desc *s)
@@ -324,7 +345,9 @@ hypic_status hypic_compose(const hypic_compose_desc *d, void *ws, size_t ws_byte
         hypic_status st = validate_seams(d->seams, d->h_v, D, 16);
         if (st != HYPIC_OK) return st;
         if (d->seams->n_win != std::max(0, d->n - 1)) return HYPIC_E_INVALID;
-        if (d->seams->q || d->seams->o || d->seams->T_w || d->seams->S_w0) return HYPIC_E_INVALID;
+        if (d->seams->T_w || d->seams->S_w0) return HYPIC_E_INVALID;
+        // read-outs on the split path ride on the group kernel (windows of up to 8 rows)
+        if (compose_readouts(d) && compose_uses_split(d) && d->seams->w > 8) return HYPIC_E_UNSUPPORTED;
         in_kind = d->seams->in_dtype == HYPIC_BF16 ? IN_BF16 : IN_F32;
     }
     const size_t need = compose_ws_bytes(d);
@@ -348,10 +371,15 @@ hypic_status hypic_compose(const hypic_compose_desc *d, void *ws, size_t ws_byte
         a.S_in = d->S_init; a.S_out = d->S_out; a.n = 0;
         return from_hip(launch_compose(a, D, HYPIC_T_SCALAR, d->prec, in_kind, hs));
     }
-    float *gT = nullptr, *gS = nullptr;
+    float *gT = nullptr, *gS = nullptr, *Y = nullptr, *S_steps = nullptr;
     if (compose_group_bytes(d) > 0) {
         gT = reinterpret_cast<float *>(static_cast<char *>(ws) + compose_ops_bytes(d));
         gS = gT + compose_group_bytes(d) / sizeof(float);
+    }
+    const bool ro = split && compose_readouts(d) && d->n > 1;
+    if (ro) {
+        Y = reinterpret_cast<float *>(static_cast<char *>(ws) + compose_ops_bytes(d) + 2 * compose_group_bytes(d));
+        S_steps = Y + ws_align((size_t)(d->n - 1) * d->h_v * 8 * 2 * D * sizeof(float)) / sizeof(float);
     }
     for (int b = 0; b < d->n; b += kMaxSeg) {
         a.n = std::min(kMaxSeg, d->n - b);
@@ -360,16 +388,23 @@ hypic_status hypic_compose(const hypic_compose_desc *d, void *ws, size_t ws_byte
         a.S_out = d->S_out;
         for (int i = 0; i < a.n; ++i) a.order[i] = d->order[b + i];
         const int G = compose_group_len(d, a.n);
-        if (G > 1) {
+        if (G > 1 || ro) {
             // level 1: every group of G positions folded into one pair; level 2:
-            // the serial fold over the group pairs
+            // the serial fold over the group pairs (with read-outs also the state
+            // entering each group, then the windows' read-outs)
             const int ng = (a.n + G - 1) / G;
-            if ((st = from_hip(launch_compose_group(a, D, ops, G, ng, gT, gS, hs))) != HYPIC_OK) return st;
+            if ((st = from_hip(launch_compose_group(a, D, ops, G, ng, gT, gS, Y, hs))) != HYPIC_OK) return st;
             ComposeArgs a2 = a;
             a2.T_pool = gT; a2.S0_pool = gS;
             a2.n = ng; a2.first_pos = 0; a2.has_seams = 0;
+            a2.S_steps = S_steps;
             for (int i = 0; i < ng; ++i) a2.order[i] = i;
             st = from_hip(launch_compose_split(a2, D, nullptr, hs));
+            if (st == HYPIC_OK && ro) {
+                ComposeArgs a3 = a;
+                a3.S_steps = S_steps;
+                st = from_hip(launch_seam_readout(a3, D, ops, Y, G, hs));
+            }
         } else {
             st = split ? from_hip(launch_compose_split(a, D, ops, hs))
                        : from_hip(launch_compose(a, D, d->tform, d->prec, in_kind, hs));

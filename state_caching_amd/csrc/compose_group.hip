@@ -50,7 +50,7 @@ struct CgCfg {
     static constexpr bool WK_SPLIT = NT >= 4 * D; // W and K staged by separate threads
 };
 
-template <int D, int NN>
+template <int D, int NN, bool RO>
 struct CgSmem {
     using C = CgCfg<D, NN>;
     // double-buffered by position parity
@@ -60,6 +60,10 @@ struct CgSmem {
     uint16_t WL[2][C::WR][C::LDA];
     uint16_t KH[2][C::WR][C::LDA];   // window K, hi, natural [t][d]; rows >= w zero
     uint16_t KL[2][C::WR][C::LDA];
+    // window read-out rows A (with read-outs only), hi/lo, k-permuted; one buffer,
+    // restaged after a barrier in the middle of each position
+    uint16_t RH[RO ? C::WR : 0][C::LDA];
+    uint16_t RL[RO ? C::WR : 0][C::LDA];
 };
 
 typedef __bf16 cg_bf2 __attribute__((ext_vector_type(2)));
@@ -109,15 +113,15 @@ __device__ __forceinline__ f4 cg_mma3(const b8 &ah, const b8 &al, const b8 &bh, 
     return mma(ah, bh, c);
 }
 
-template <int D, bool SEAMS, int NN>
+template <int D, bool SEAMS, int NN, bool RO>
 __global__ void __launch_bounds__((CgCfg<D, NN>::NT)) compose_group_kernel(const ComposeArgs a, const float *ops,
-                                                                           int G, float *gT, float *gS)
+                                                                           int G, float *gT, float *gS, float *Y)
 {
     using C = CgCfg<D, NN>;
     constexpr int MT = C::MT, KB = C::KB, QH = C::QH, LDA = C::LDA, NWH = C::NWH, NP = C::NP, WR = C::WR,
                   TP = C::TP;
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    CgSmem<D, NN> &sm = *reinterpret_cast<CgSmem<D, NN> *>(smem_raw);
+    CgSmem<D, NN, RO> &sm = *reinterpret_cast<CgSmem<D, NN, RO> *>(smem_raw);
 
     // the wave index as a scalar, so the branches on the wave's half are uniform
     const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -135,7 +139,7 @@ __global__ void __launch_bounds__((CgCfg<D, NN>::NT)) compose_group_kernel(const
     const bool do_w = !C::WK_SPLIT || tid < 2 * D, do_k = !C::WK_SPLIT || tid >= 2 * D;
     const int srow = wkt / (D / 4), scol = 4 * (wkt % (D / 4));
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    auto win_rec = [&](int pos) { return ops + ((int64_t)max(pos - 1, 0) * a.h_v + h) * winop_floats<D>(w); };
+    auto win_rec = [&](int pos) { return ops + ((int64_t)max(pos - 1, 0) * a.h_v + h) * winop_floats<D>(w, RO); };
 
     // The two halves run the same loop (one barrier per position) in separate
     // code, so that neither half's prefetch registers are live in the other's.
@@ -194,7 +198,7 @@ __global__ void __launch_bounds__((CgCfg<D, NN>::NT)) compose_group_kernel(const
         // window operators of position pos (pos >= 1) one position ahead of their
         // staging: this thread's float4 of W and of K (row tid / (D/4)), gw; the S
         // half's U^T slices are read at the start of the position's step
-        float4 Wq = z4, Kq = z4;
+        float4 Wq = z4, Kq = z4, Rq = z4;
         float gwq = 1.f, gwc = 1.f;
         bool hwq = false, hwc = false;
         auto fetch_win = [&](int pos) {
@@ -204,8 +208,10 @@ __global__ void __launch_bounds__((CgCfg<D, NN>::NT)) compose_group_kernel(const
                 const bool rin = hwq && srow < w;
                 if (do_w) Wq = *reinterpret_cast<const float4 *>(o + (int64_t)(rin ? srow : 0) * D + scol);
                 if (do_k) Kq = *reinterpret_cast<const float4 *>(o + (int64_t)wp * D + (int64_t)(rin ? srow : 0) * D + scol);
-                if (!rin) { Wq = z4; Kq = z4; }
-                gwq = hwq ? o[(int64_t)3 * wp * D] : 1.f;
+                if constexpr (RO)
+                    if (do_w) Rq = *reinterpret_cast<const float4 *>(o + (int64_t)3 * wp * D + (int64_t)(rin ? srow : 0) * D + scol);
+                if (!rin) { Wq = z4; Kq = z4; Rq = z4; }
+                gwq = hwq ? o[winop_gw<D>(w, RO)] : 1.f;
             }
         };
         auto stage_win = [&](int buf) {   // W, K of the fetched window into buffer buf; gw current
@@ -223,6 +229,16 @@ __global__ void __launch_bounds__((CgCfg<D, NN>::NT)) compose_group_kernel(const
                 }
                 gwc = gwq;
                 hwc = hwq;
+            }
+        };
+        auto stage_r = [&]() {   // read-out rows of the fetched window (single buffer)
+            if constexpr (RO) {
+                if (do_w) {
+                    uint2 hi, lo;
+                    cg_split4(Rq, hi, lo);
+                    *reinterpret_cast<uint2 *>(&sm.RH[srow][cg_perm(scol)]) = hi;
+                    *reinterpret_cast<uint2 *>(&sm.RL[srow][cg_perm(scol)]) = lo;
+                }
             }
         };
         // B operands of the column tiles 2 p, 2 p + 1 for the k block kb (rows
@@ -243,6 +259,7 @@ __global__ void __launch_bounds__((CgCfg<D, NN>::NT)) compose_group_kernel(const
         }
         fetch_win(a.first_pos + j0);
         stage_win(0);
+        stage_r();
         fetch_win(a.first_pos + min(j0 + 1, j1 - 1));
 
 #pragma unroll 1
@@ -282,9 +299,30 @@ __global__ void __launch_bounds__((CgCfg<D, NN>::NT)) compose_group_kernel(const
                         split_kb(p, kb, bh, bl);
                         b8 ah = *reinterpret_cast<const b8 *>(&sm.WH[buf][wl ? r16 : 0][32 * kb + 8 * g]);
                         b8 al = *reinterpret_cast<const b8 *>(&sm.WL[buf][wl ? r16 : 0][32 * kb + 8 * g]);
-                        if (!wl) { ah = b8{}; al = b8{}; }
+                        if constexpr (RO) {
+                            // rows 8 .. 15 of the product: the read-out rows, Y = A X
+                            if (!wl) {
+                                ah = *reinterpret_cast<const b8 *>(&sm.RH[r16 - WR][32 * kb + 8 * g]);
+                                al = *reinterpret_cast<const b8 *>(&sm.RL[r16 - WR][32 * kb + 8 * g]);
+                            }
+                        } else if (!wl) {
+                            ah = b8{};
+                            al = b8{};
+                        }
 #pragma unroll
                         for (int q = 0; q < 2; ++q) P[q] = cg_mma3(ah, al, bh[q], bl[q], P[q]);
+                    }
+                    if constexpr (RO) {
+                        // rows 4g + i >= 8 of P are Y rows t = 4g + i - 8 (their E rows meet
+                        // zero key columns below)
+                        if (hwc && g >= 2) {
+                            float *yp = Y + ((int64_t)(a.first_pos + j - 1) * a.h_v + h) * 8 * 2 * D +
+                                        (int64_t)(4 * g - WR) * 2 * D + (TH ? 0 : D) + cb + r16;
+#pragma unroll
+                            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) yp[(int64_t)i * 2 * D + 16 * (2 * p + q)] = P[q][i];
+                        }
                     }
                     b8 Eh[2], El[2];
 #pragma unroll
@@ -338,6 +376,14 @@ __global__ void __launch_bounds__((CgCfg<D, NN>::NT)) compose_group_kernel(const
                         __builtin_amdgcn_sched_barrier(0);
                         stage_t(buf ^ 1, 2 * p);
                         fetch_t(jn, 2 * p + 1);
+                        if constexpr (RO) {
+                            // every wave is past this position's window product: the
+                            // read-out rows of the next position go into the one buffer
+                            if (p == NP - 1) {
+                                lds_barrier();
+                                stage_r();
+                            }
+                        }
                         __builtin_amdgcn_sched_barrier(0);
                     }
                     b8 bh[2], bl[2];
@@ -374,20 +420,20 @@ __global__ void __launch_bounds__((CgCfg<D, NN>::NT)) compose_group_kernel(const
     else run(std::false_type{});
 }
 
-template <int D, bool SEAMS, int NN>
-static hipError_t launch_cg(const ComposeArgs &a, const float *ops, int G, int ng, float *gT, float *gS,
+template <int D, bool SEAMS, int NN, bool RO>
+static hipError_t launch_cg(const ComposeArgs &a, const float *ops, int G, int ng, float *gT, float *gS, float *Y,
                             hipStream_t st)
 {
-    const size_t smem = sizeof(CgSmem<D, NN>);
+    const size_t smem = sizeof(CgSmem<D, NN, RO>);
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&compose_group_kernel<D, SEAMS, NN>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&compose_group_kernel<D, SEAMS, NN, RO>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;
         attr = true;
     }
-    hipLaunchKernelGGL((compose_group_kernel<D, SEAMS, NN>), dim3(ng * a.h_v), dim3(CgCfg<D, NN>::NT), smem, st,
-                       a, ops, G, gT, gS);
+    hipLaunchKernelGGL((compose_group_kernel<D, SEAMS, NN, RO>), dim3(ng * a.h_v), dim3(CgCfg<D, NN>::NT), smem, st,
+                       a, ops, G, gT, gS, Y);
     return hipGetLastError();
 }
 
@@ -396,16 +442,21 @@ static hipError_t launch_cg(const ComposeArgs &a, const float *ops, int G, int n
 #endif
 
 hipError_t launch_compose_group(const ComposeArgs &a, int D, const float *ops, int G, int ng, float *gT,
-                                float *gS, hipStream_t st)
+                                float *gS, float *Y, hipStream_t st)
 {
     if (G < 1 || ng < 1 || (int64_t)(ng - 1) * G >= a.n || (int64_t)ng * G < a.n) return hipErrorInvalidValue;
     if (a.has_seams && a.seam.w > CgCfg<128, HY_CG_NN>::WR) return hipErrorInvalidValue;
     // the seam variant needs at least one window record in this launch
     const bool seams = a.has_seams && a.first_pos + a.n >= 2;
-    if (D == 128) return seams ? launch_cg<128, true, HY_CG_NN>(a, ops, G, ng, gT, gS, st)
-                               : launch_cg<128, false, HY_CG_NN>(a, ops, G, ng, gT, gS, st);
-    if (D == 64) return seams ? launch_cg<64, true, HY_CG_NN>(a, ops, G, ng, gT, gS, st)
-                              : launch_cg<64, false, HY_CG_NN>(a, ops, G, ng, gT, gS, st);
+    // read-out records are laid out with the read-out rows: the kernel must match
+    const bool ro = seams && a.seam.q != nullptr;
+    if (ro && !Y) return hipErrorInvalidValue;
+    if (D == 128) return ro ? launch_cg<128, true, HY_CG_NN, true>(a, ops, G, ng, gT, gS, Y, st)
+                    : seams ? launch_cg<128, true, HY_CG_NN, false>(a, ops, G, ng, gT, gS, Y, st)
+                            : launch_cg<128, false, HY_CG_NN, false>(a, ops, G, ng, gT, gS, Y, st);
+    if (D == 64) return ro ? launch_cg<64, true, HY_CG_NN, true>(a, ops, G, ng, gT, gS, Y, st)
+                   : seams ? launch_cg<64, true, HY_CG_NN, false>(a, ops, G, ng, gT, gS, Y, st)
+                           : launch_cg<64, false, HY_CG_NN, false>(a, ops, G, ng, gT, gS, Y, st);
     return hipErrorInvalidValue;
 }
 

@@ -203,6 +203,11 @@ __global__ void __launch_bounds__((CsCfg<D, SEAMS>::NT)) compose_split_kernel(co
         put_state(0, Sown);
         int cur = 0;
         auto step = [&](const int j, const int s) __attribute__((always_inline)) {
+            if (a.S_steps) {   // the state entering step j, for the window read-outs
+                float *sp = a.S_steps + ((int64_t)j * a.h_v + h) * D * D + c0 + r16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sp[(int64_t)(row0 + 4 * g + i) * D] = Sown[i];
+            }
             lds_barrier();   // S_j complete in buffer cur
             const f4 acc = product(S0b[s], cur);
             Sown = acc;
@@ -238,11 +243,11 @@ __global__ void __launch_bounds__((CsCfg<D, SEAMS>::NT)) compose_split_kernel(co
         const bool wrow = r16 < w, wtok = 4 * g < wp, ktok = kt < w;
         auto fetch_win = [&](int pos, int st) {
             const int wi = min(max(pos - 1, 0), win_hi);   // clamped: always in range
-            const float *o = ops + ((int64_t)wi * a.h_v + h) * winop_floats<D>(w);
+            const float *o = ops + ((int64_t)wi * a.h_v + h) * winop_floats<D>(w, a.seam.q != nullptr);
             Wv[st] = *reinterpret_cast<const float4 *>(o + (int64_t)(wrow ? r16 : 0) * D + row0 + 4 * g);
             Kg[st] = *reinterpret_cast<const float4 *>(o + (int64_t)wp * D + (int64_t)(ktok ? kt : 0) * D + kd);
             Uv[st] = *reinterpret_cast<const float4 *>(o + (int64_t)2 * wp * D + (int64_t)(c0 + r16) * wp + (wtok ? 4 * g : 0));
-            gw[st] = o[(int64_t)3 * wp * D];
+            gw[st] = o[winop_gw<D>(w, a.seam.q != nullptr)];
             hw[st] = pos >= 1;
         };
         // this wave's part of W S from its own rows (masked beyond the window)
@@ -366,6 +371,60 @@ static hipError_t launch_ops(const ComposeArgs &a, int n_win, float *ops, hipStr
     return hipGetLastError();
 }
 
+// Window read-outs of a two-level compose: for the window of prompt position
+// pos (launch-local j = pos - first_pos, group j / G) with state S_g entering
+// its group, Y = A [P | Q] the read-out rows times the group-local prefix pair
+// at the window (written by the group kernel), o = Y_P S_g + Y_Q + C.  One
+// 256-thread workgroup per (window, value head); thread (row set, column c)
+// forms o_t[c] for its rows t, the Y rows broadcast from LDS.
+template <int D>
+__global__ void __launch_bounds__(256) seam_readout_kernel(const ComposeArgs a, const float *ops, const float *Y,
+                                                           int G, int j_begin)
+{
+    constexpr int RS = 256 / D, RPT = 8 / RS;   // row sets, rows per thread
+    __shared__ float Ys[8][2 * D];
+    const int j = j_begin + (int)(blockIdx.x / a.h_v), h = blockIdx.x % a.h_v;
+    const int pos = a.first_pos + j, win = pos - 1;
+    const int w = a.seam.w, wp = winop_wp(w);
+    const float *yr = Y + ((int64_t)win * a.h_v + h) * 8 * 2 * D;
+    for (int e = threadIdx.x; e < 8 * 2 * D / 4; e += 256)
+        reinterpret_cast<float4 *>(&Ys[0][0])[e] = reinterpret_cast<const float4 *>(yr)[e];
+    __syncthreads();
+    const int c = threadIdx.x % D, rs = threadIdx.x / D;
+    const float *Sg = a.S_steps + ((int64_t)(j / G) * a.h_v + h) * D * D + c;
+    float acc[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) acc[i] = 0.f;
+#pragma unroll 8
+    for (int k = 0; k < D; ++k) {
+        const float sv = Sg[(int64_t)k * D];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) acc[i] += Ys[rs + RS * i][k] * sv;
+    }
+    const float *Cr = ops + ((int64_t)win * a.h_v + h) * winop_floats<D>(w, true) + (int64_t)4 * wp * D;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int t = rs + RS * i;
+        if (t < w)
+            a.seam.o[(((int64_t)win * w + t) * a.h_v + h) * D + c] = acc[i] + Ys[t][D + c] + Cr[(int64_t)t * D + c];
+    }
+}
+
+hipError_t launch_seam_readout(const ComposeArgs &a, int D, const float *ops, const float *Y, int G,
+                               hipStream_t st)
+{
+    // windows of this launch: positions first_pos + j >= 1
+    const int j_begin = a.first_pos == 0 ? 1 : 0;
+    const int nw = a.n - j_begin;
+    if (nw <= 0) return hipSuccess;
+    if (a.seam.w > 8 || !a.S_steps || !a.seam.o) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(nw * a.h_v));
+    if (D == 128) hipLaunchKernelGGL((seam_readout_kernel<128>), grid, dim3(256), 0, st, a, ops, Y, G, j_begin);
+    else if (D == 64) hipLaunchKernelGGL((seam_readout_kernel<64>), grid, dim3(256), 0, st, a, ops, Y, G, j_begin);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 template <int D, bool SEAMS>
 static hipError_t launch_cs(const ComposeArgs &a, const float *ops, hipStream_t st)
 {
@@ -375,9 +434,9 @@ static hipError_t launch_cs(const ComposeArgs &a, const float *ops, hipStream_t 
     return hipGetLastError();
 }
 
-int64_t seam_ops_floats(int D, int w, int n_win, int h_v)
+int64_t seam_ops_floats(int D, int w, int n_win, int h_v, bool ro)
 {
-    const int64_t per = (D == 128) ? winop_floats<128>(w) : winop_floats<64>(w);
+    const int64_t per = (D == 128) ? winop_floats<128>(w, ro) : winop_floats<64>(w, ro);
     return per * n_win * h_v;
 }
 

@@ -79,6 +79,7 @@ struct ComposeArgs {
     int first_pos;              // prompt position of order[0] (seam i uses window first_pos+i-1)
     int has_seams;
     SeamArgs seam;
+    float *S_steps;             // or null: the no-seam fold writes the state entering each step [n, h_v, D, D]
     int32_t order[kMaxSeg];
 };
 
@@ -118,14 +119,20 @@ hipError_t launch_compose(const ComposeArgs &a, int D, int tform, int prec, int 
 hipError_t launch_seam(const ComposeArgs &a, int D, int in_kind, float *S, int n_win,
                        hipStream_t st);
 // split-bf16 dense compose for d in {64, 128}, seam windows from precomputed operators
-int64_t seam_ops_floats(int D, int w, int n_win, int h_v);
+int64_t seam_ops_floats(int D, int w, int n_win, int h_v, bool ro);
 hipError_t launch_seam_ops(const ComposeArgs &a, int D, int in_kind, int n_win, float *ops,
                            hipStream_t st);
 hipError_t launch_compose_split(const ComposeArgs &a, int D, const float *ops, hipStream_t st);
 // level 1 of the two-level split compose (d in {64, 128}): the a.n positions in
 // ng groups of G consecutive ones, each (group, head) folded into one pair,
-// written to gT / gS [ng, h_v, D, D]
+// written to gT / gS [ng, h_v, D, D].  With window read-outs (a.seam.q set) also
+// Y [n_win, h_v, 8, 2D]: the read-out rows A of every window times the
+// group-local prefix pair at that window.
 hipError_t launch_compose_group(const ComposeArgs &a, int D, const float *ops, int G, int ng, float *gT,
-                                float *gS, hipStream_t st);
+                                float *gS, float *Y, hipStream_t st);
+// o of the windows of a launch from Y, the group-start states a.S_steps and
+// the windows' read-out records (w <= 8)
+hipError_t launch_seam_readout(const ComposeArgs &a, int D, const float *ops, const float *Y, int G,
+                               hipStream_t st);
 
 }  // namespace hy

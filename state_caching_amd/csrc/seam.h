@@ -211,10 +211,95 @@ __device__ void seam_apply(WinSmem<D, WMAX, 16> &ws, float *ST, int ldst, const 
 //   W  [wp][D]  M diag(b) K                       (token-major)
 //   K  [wp][D]  keys after conv and normalisation (token-major)
 //   UT [D][wp]  (M diag(b dec) V)^T               (value column-major)
+// with read-outs (ro) also, o_t = A_t^T S + C_t for the state S entering the
+// window (the read-out formula above, split into its state-linear part and
+// the rest):
+//   A  [wp][D]  gam_t (q_t - sum_{s<=t} (q_t.k_s) W_s)
+//   C  [wp][D]  sum_{r<=t} H_tr b_r (gam_t / gam_r) v_r
+// and last
 //   gw          gate product over the window
 __host__ __device__ __forceinline__ int winop_wp(int w) { return (w + 3) & ~3; }
 template <int D>
-__host__ __device__ __forceinline__ int64_t winop_floats(int w) { return (int64_t)3 * winop_wp(w) * D + 4; }
+__host__ __device__ __forceinline__ int64_t winop_gw(int w, bool ro) { return (int64_t)(ro ? 5 : 3) * winop_wp(w) * D; }
+template <int D>
+__host__ __device__ __forceinline__ int64_t winop_floats(int w, bool ro) { return winop_gw<D>(w, ro) + 4; }
+
+// Read-out operators of one (window, head) (one wave; K, V rows of this lane's
+// columns d = lane + 64 c in registers, M and the gates in LDS):
+//   A_t = gam_t (q_t - sum_{s<=t} (q_t.k_s) W_s),  W_s = sum_{r<=s} M_sr b_r k_r,
+//   C_t = sum_{r<=t} H_tr b_r (gam_t / gam_r) v_r, H_tr = sum_{r<=s<=t} (q_t.k_s) M_sr.
+template <int D, int WM, typename TIN>
+__device__ __forceinline__ void seam_ops_readout(const SeamArgs &a, int win, int h, const float (&K)[WM][D / 64],
+                                                 const float (&V)[WM][D / 64], float (&QK)[WM][WM + 1],
+                                                 float (&H)[WM][WM + 1], const float (&M)[WM][WM + 1],
+                                                 const float *bq, const float *cl, float *o)
+{
+    constexpr int C = D / 64, NQ = WM * (WM + 1) / 2;
+    const int lane = threadIdx.x, w = a.w, wp = winop_wp(w);
+    const int kh = h / (a.h_v / a.h_k);
+    const int64_t ldk = (int64_t)a.h_k * D;
+    const TIN *qp = reinterpret_cast<const TIN *>(a.q) + (int64_t)win * w * ldk + (int64_t)kh * D;
+    float Q[WM][C];
+#pragma unroll
+    for (int t = 0; t < WM; ++t)
+#pragma unroll
+        for (int c = 0; c < C; ++c) Q[t][c] = t < w ? ld1(qp + (int64_t)(t < w ? t : 0) * ldk + lane + 64 * c) : 0.f;
+    {   // q_t.k_s for s <= t, all reduced together
+        float dot[NQ];
+#pragma unroll
+        for (int t = 0, p = 0; t < WM; ++t)
+#pragma unroll
+            for (int s = 0; s <= t; ++s, ++p) {
+                dot[p] = 0.f;
+#pragma unroll
+                for (int c = 0; c < C; ++c) dot[p] += Q[t][c] * K[s][c];
+            }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1)
+#pragma unroll
+            for (int p = 0; p < NQ; ++p) dot[p] += __shfl_xor(dot[p], m);
+        if (lane == 0) {
+#pragma unroll
+            for (int t = 0, p = 0; t < WM; ++t)
+#pragma unroll
+                for (int s = 0; s <= t; ++s, ++p) QK[t][s] = dot[p];
+        }
+    }
+    __syncthreads();
+    for (int e = lane; e < WM * WM; e += 64) {   // H_tr, r <= t
+        const int t = e / WM, r = e % WM;
+        float acc = 0.f;
+        for (int s = r; s <= t; ++s) acc += QK[t][s] * M[s][r];
+        H[t][r] = r <= t ? acc : 0.f;
+    }
+    __syncthreads();
+    float *oA = o + (int64_t)3 * wp * D, *oC = o + (int64_t)4 * wp * D;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int d = lane + 64 * c;
+        float Wd[WM];
+#pragma unroll
+        for (int t = 0; t < WM; ++t) {
+            float sw = 0.f;
+#pragma unroll
+            for (int r = 0; r <= t; ++r) sw += M[t][r] * bq[r] * K[r][c];
+            Wd[t] = sw;
+        }
+#pragma unroll
+        for (int t = 0; t < WM; ++t) {
+            float sa = Q[t][c], sc = 0.f;
+#pragma unroll
+            for (int s = 0; s <= t; ++s) sa -= QK[t][s] * Wd[s];
+#pragma unroll
+            for (int r = 0; r <= t; ++r) sc += H[t][r] * bq[r] * exp2f(cl[t] - cl[r]) * V[r][c];
+            const bool in = t < w;
+            if (t < wp) {
+                oA[(int64_t)t * D + d] = in ? exp2f(cl[t]) * sa : 0.f;
+                oC[(int64_t)t * D + d] = in ? sc : 0.f;
+            }
+        }
+    }
+}
 
 // One wave per (window, value head): every operator of the window, with the
 // key and value rows held in registers (C = D/64 columns per lane) and the
@@ -227,6 +312,9 @@ __global__ void __launch_bounds__(64) seam_ops_kernel(const SeamArgs a, float *o
     __shared__ float G[WM][WM + 1];   // b_r k_r.k_s, s < r
     __shared__ float M[WM][WM + 1];   // (I + G)^-1, unit lower triangular
     __shared__ float bq[WM], bd[WM];  // b_q and b_q dec_q
+    __shared__ float QK[WM][WM + 1];  // q_t.k_s, s <= t (read-outs)
+    __shared__ float H[WM][WM + 1];   // sum_{r<=s<=t} QK_ts M_sr (read-outs)
+    __shared__ float cl[WM];          // log2 gam_t (read-outs)
     const int lane = threadIdx.x;
     const int win = blockIdx.x / a.h_v, h = blockIdx.x % a.h_v;
     const int w = a.w, Wc = a.conv_w, wp = winop_wp(w);
@@ -236,7 +324,8 @@ __global__ void __launch_bounds__(64) seam_ops_kernel(const SeamArgs a, float *o
     const TIN *xv = reinterpret_cast<const TIN *>(a.xv) + (int64_t)win * w * ldv + (int64_t)h * D;
     const TIN *tk = Wc > 1 ? reinterpret_cast<const TIN *>(a.tail_k) + (int64_t)win * (Wc - 1) * ldk + (int64_t)kh * D : nullptr;
     const TIN *tv = Wc > 1 ? reinterpret_cast<const TIN *>(a.tail_v) + (int64_t)win * (Wc - 1) * ldv + (int64_t)h * D : nullptr;
-    float *o = ops + ((int64_t)win * a.h_v + h) * winop_floats<D>(w);
+    const bool ro = a.q != nullptr;
+    float *o = ops + ((int64_t)win * a.h_v + h) * winop_floats<D>(w, ro);
 
     // gates first (their loads overlap the row loads): b, suffix decay, window product
     float gb = 0.f, gl2 = 0.f;
@@ -315,7 +404,11 @@ __global__ void __launch_bounds__(64) seam_ops_kernel(const SeamArgs a, float *o
             bq[lane] = gb;
             bd[lane] = gb * exp2f(sfx);
         }
-        if (lane == 0) o[(int64_t)3 * wp * D] = scale_pow2(1.f, tot);
+        if (lane == 0) o[winop_gw<D>(w, ro)] = scale_pow2(1.f, tot);
+        if (ro) {   // log2 gam_t, inclusive prefix
+            const float pre = wave_prefix_incl(gl2);
+            if (lane < WM) cl[lane] = pre;
+        }
     }
     // Gram pairs r > q, all reduced together
     {
@@ -383,6 +476,8 @@ __global__ void __launch_bounds__(64) seam_ops_kernel(const SeamArgs a, float *o
             if (t4 < wp)
                 *reinterpret_cast<float4 *>(oUT + (int64_t)d * wp + t4) = make_float4(Ud[t4], Ud[t4 + 1], Ud[t4 + 2], Ud[t4 + 3]);
     }
+    if constexpr (WM <= 8)   // read-outs ride on windows of up to 8 rows
+        if (ro) seam_ops_readout<D, WM, TIN>(a, win, h, K, V, QK, H, M, bq, cl, o);
 }
 
 }  // namespace hy

@@ -137,6 +137,20 @@ def test_compose_seam_validation(sca):
     d2 = _compose_desc(sca, tform=sca.T_DIAG, seams=ctypes.pointer(sd))
     sd.rule = sca.RULE_DELTA
     assert L.hypic_compose(ctypes.byref(d2), None, 0, None) == -2
+    sd.q = 16                                     # read-outs: q and o together
+    assert L.hypic_compose(ctypes.byref(d), None, 0, None) == -1
+    sd.o = 16
+    sd.w = 12                                     # split-path read-outs hold windows of <= 8 rows
+    assert L.hypic_compose(ctypes.byref(d), None, 0, None) == -2
+    sd.w = 8
+    sd.T_w = 16                                   # window pairs are a standalone-call output
+    assert L.hypic_compose(ctypes.byref(d), None, 0, None) == -1
+    sd.T_w = None
+    # a valid read-out request that only lacks its workspace
+    assert L.hypic_compose(ctypes.byref(d), None, 0, None) == -3
+    need = L.hypic_workspace_size(ctypes.byref(d), sca.WS_COMPOSE)
+    sd.q = sd.o = None
+    assert need > L.hypic_workspace_size(ctypes.byref(d), sca.WS_COMPOSE)
 
 
 def test_seam_validation(sca):

@@ -393,6 +393,118 @@ def test_gdn_100_segments_seams_slow_group_compose():
     assert e1 <= 2e-5 and e2 <= 2e-5
 
 
+# ------------------------------------------------ window read-outs in the compose
+
+def _attach_queries(dw, seed):
+    """Seeded final queries for every seam window (the workload's dtype) and a
+    zeroed fp32 read-out buffer, on the device seams; returns q as fp64."""
+    wl = dw.wl
+    n_win, w = len(wl.window_ranges()), wl.seam_w
+    rng = np.random.default_rng(seed)
+    q = synth._round(rng.standard_normal((n_win, w, wl.h_k, wl.d_k)) / np.sqrt(wl.d_k), wl.dtype)
+    dw.seams.q = q.cuda()
+    dw.seams.o = torch.full((n_win, w, wl.h_v, wl.d_v), float("nan"), dtype=torch.float32,
+                            device="cuda")
+    return np64(q)
+
+
+def _readout_errs(o_gpu, o_ref):
+    """relF over all read-outs, and the largest relF of one window."""
+    whole = oracle.relF(o_gpu, o_ref)
+    per = max(oracle.relF(o_gpu[j], o_ref[j]) for j in range(o_ref.shape[0]))
+    return whole, per
+
+
+@pytest.mark.parametrize("d,G", [(64, 2), (64, 5), (128, 0), (128, 3), (128, 7)])
+def test_group_compose_readouts(d, G):
+    """Window read-outs o_t = q_t^T S_t inside the two-level compose (ch.2 sec.5:
+    the recomputed window tokens produce their outputs from the true prefix
+    state), ragged segments, a random prefix state: o and the final state against
+    the oracle's composition of the same pairs with the same windows."""
+    need_gpu()
+    lens = [40, 64, 33, 70, 21, 64, 50, 90, 17, 64, 45, 80, 66, 29, 55, 64, 38]
+    wl = synth.gdn(140 + d + G, lens, 1, 2, d, torch.bfloat16, alpha_div=64.0, conv_w=4,
+                   seam_w=8)
+    sca, DW = _lib()
+    dw = DW(wl)
+    T, S0 = dw.build()
+    S_init = synth.random_state(141 + d, 2, d, d)
+    q = _attach_queries(dw, 142 + d + G)
+    case(f"group compose with read-outs d={d} G={G} n={len(lens)}")
+    S = dw.compose(T, S0, S_init=S_init.cuda(), group_len=G)
+    torch.cuda.synchronize()
+    S_or, o_or = oracle.compose(np64(T), np64(S0), S_init=np64(S_init), wl=wl, seams=True, q=q)
+    eS = oracle.relF(np64(S), S_or)
+    eo, eo_win = _readout_errs(np64(dw.seams.o), o_or)
+    print(f"  relF S {eS:.3e}, o {eo:.3e} (worst window {eo_win:.3e})")
+    assert eS <= 2e-5 and eo <= 2e-5 and eo_win <= 1e-4
+
+
+def test_compose_readouts_fp32_path():
+    """Read-outs on the fp32 compose path (fp32 inputs, windows in fp32
+    arithmetic), a window wider than 8 rows: against the oracle."""
+    need_gpu()
+    wl = synth.gdn(150, [40, 64, 33, 70, 21], 2, 2, 64, torch.float32, alpha_div=16.0, conv_w=4,
+                   seam_w=12)
+    sca, DW = _lib()
+    dw = DW(wl)
+    T, S0 = dw.build()
+    q = _attach_queries(dw, 151)
+    case("compose with read-outs, fp32 path, w=12")
+    S = dw.compose(T, S0)
+    torch.cuda.synchronize()
+    S_or, o_or = oracle.compose(np64(T), np64(S0), wl=wl, seams=True, q=q)
+    eS = oracle.relF(np64(S), S_or)
+    eo, eo_win = _readout_errs(np64(dw.seams.o), o_or)
+    print(f"  relF S {eS:.3e}, o {eo:.3e} (worst window {eo_win:.3e})")
+    assert eS <= 1e-5 and eo <= 1e-5 and eo_win <= 1e-4
+
+
+def test_group_compose_readouts_across_launches():
+    """Read-outs over more positions than one launch holds: windows indexed by
+    prompt position, group-start states per launch."""
+    need_gpu()
+    wl = synth.gdn(152, [12] * 150, 1, 1, 64, torch.bfloat16, alpha_div=16.0, conv_w=4,
+                   seam_w=8)
+    sca, DW = _lib()
+    dw = DW(wl)
+    T, S0 = dw.build()
+    q = _attach_queries(dw, 153)
+    case("group compose with read-outs, 150 segments, G=6")
+    S = dw.compose(T, S0, group_len=6)
+    torch.cuda.synchronize()
+    S_or, o_or = oracle.compose(np64(T), np64(S0), wl=wl, seams=True, q=q)
+    eS = oracle.relF(np64(S), S_or)
+    eo, eo_win = _readout_errs(np64(dw.seams.o), o_or)
+    print(f"  relF S {eS:.3e}, o {eo:.3e} (worst window {eo_win:.3e})")
+    assert eS <= 2e-5 and eo <= 2e-5 and eo_win <= 1e-4
+
+
+def test_gdn_100_segments_readouts_slow():
+    """The 100-segment slow-decay prompt with read-outs at all 99 windows, in the
+    bench's launch configuration (automatic groups): o on sampled heads against
+    the oracle's composition of the same GPU-built pairs, and the final state
+    against the compose without read-outs."""
+    need_gpu()
+    wl = synth.workload("gdn_d128_32h_100x1024_seams_bf16_slow")
+    sca, DW = _lib()
+    dw = DW(wl)
+    T, S0 = dw.build()
+    S_plain = dw.compose(T, S0)
+    q = _attach_queries(dw, 154)
+    case("100-segment slow-decay compose with read-outs")
+    S = dw.compose(T, S0)
+    torch.cuda.synchronize()
+    heads = [3, 30]
+    _, o_or = oracle.compose(np64(T)[:, heads], np64(S0)[:, heads], wl=wl, heads=heads,
+                             seams=True, q=q)
+    eo, eo_win = _readout_errs(np64(dw.seams.o)[:, :, heads], o_or)
+    eS = oracle.relF(np64(S), np64(S_plain))
+    print(f"  relF o (heads {heads}) {eo:.3e} (worst window {eo_win:.3e}); S vs compose without "
+          f"read-outs {eS:.3e}")
+    assert eo <= 2e-5 and eo_win <= 1e-4 and eS <= 1e-6
+
+
 # --------------------------------------------- delta rule with a diagonal gate (KDA)
 
 @pytest.mark.parametrize("d,dtype", [(16, torch.float32), (32, torch.bfloat16), (64, torch.float32),
