@@ -285,6 +285,37 @@ def main():
                                                         "gdn_100_segments_seams"),
                              "algorithmic_bytes": by,
                              "mfma_tflops": compose_flops(wl4) / (k4 * 1e-3) / 1e12}}
+        # the same compose with the read-outs of all 99 windows (queries of every
+        # window token in, o_t = q_t^T S_t out)
+        import copy
+        import numpy as np
+        n_win, w4 = len(wl4.window_ranges()), wl4.seam_w
+        rng = np.random.default_rng(4004)
+        q4 = synth._round(rng.standard_normal((n_win, w4, wl4.h_k, wl4.d_k)) / np.sqrt(wl4.d_k),
+                          wl4.dtype).to(dev)
+        sm_ro = copy.copy(dw4.seams)
+        sm_ro.q = q4
+        sm_ro.o = torch.empty((n_win, w4, wl4.h_v, wl4.d_v), dtype=torch.float32, device=dev)
+
+        def step4r(ev):
+            if ev: ev["compose"][0].record()
+            compose(T4, S04, order, tform=dw4.tform, prec=dw4.prec, seams=sm_ro, S_out=S4)
+            if ev: ev["compose"][1].record()
+
+        _, per4r = time_leg(step4r, args.steps, args.warmup, torch, ["compose"])
+        k4r = sum(per4r["compose"]) / len(per4r["compose"])
+        by_r = by + q4.numel() * q4.element_size() + sm_ro.o.numel() * 4
+        gbs_r = by_r / (k4r * 1e-3) / 1e9
+        comp["readouts"] = {"workload": "the same compose with the read-outs of all 99 windows (8 tokens each, "
+                                        "bf16 queries of 16 key heads in, fp32 outputs of 32 heads out)",
+                            "ms_per_compose": k4r, "overhead_ms": k4r - k4,
+                            "roofline": {"bound": "hbm",
+                                         "kernel": "hypic_compose with read-outs: seam_ops_kernel + compose_group_kernel"
+                                                   "<128,seams,read-outs> + compose_split_kernel (group-start states) "
+                                                   "+ seam_readout_kernel<128>",
+                                         "achieved": gbs_r, "peak": PEAK_HBM, "unit": "GB/s",
+                                         "frac": gbs_r / PEAK_HBM, "traffic": None, "algorithmic_bytes": by_r}}
+        del sm_ro, q4
         out["compose"] = comp
         if "value" not in out:
             out.update({"value": comp["compositions_per_s"], "unit": "compositions/s",

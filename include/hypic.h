@@ -238,8 +238,13 @@ hypic_status hypic_rope_rerotate_state(int32_t h, int32_t d_k, int32_t d_v, int3
  *   S_init   [h_v, d_k, d_v] fp32, or NULL for the zero state
  *   S_out    [h_v, d_k, d_v] fp32; may equal S_init
  *   seams    NULL, or windows for positions 1..n-1 (seams->n_win == n-1,
- *            seams->w <= 16), dense tform only; seams->q/o/T_w/S_w0 must be
- *            NULL here
+ *            seams->w <= 16), dense tform only; seams->T_w/S_w0 must be NULL
+ *            here.  seams->q and seams->o (both or neither) ask for the
+ *            read-outs of every window token from the true prefix state it
+ *            sees (ch.2 sec.5; Eq. (2): o_t = q_t^T S_t after token t),
+ *            o [n-1, w, h_v, d_v] fp32, written for tokens t < w only.  On the
+ *            split path they need w <= 8 (else HYPIC_E_UNSUPPORTED) and always
+ *            take the group route (group_len 1: groups of one position).
  *   prec     HYPIC_PREC_FP32 or HYPIC_PREC_SPLIT for the dense product
  *   group_len  dense split compose with d_k in {64, 128} only (ignored
  *            otherwise): 1 folds the positions one after another; G >= 2
@@ -255,7 +260,11 @@ hypic_status hypic_rope_rerotate_state(int32_t h, int32_t d_k, int32_t d_v, int3
  *     first and staged there, (3 wp d_k + 4) floats per (window, value head)
  *     with wp = w rounded up to a multiple of 4 (rounded up to 256 bytes);
  *   - with groups, two pools of group pairs follow, [ng, h_v, d_k, d_v] fp32
- *     each, ng = ceil(min(n, HYPIC_MAX_SEG_PER_LAUNCH) / G).
+ *     each, ng = ceil(min(n, HYPIC_MAX_SEG_PER_LAUNCH) / G);
+ *   - with read-outs, the window records hold (5 wp d_k + 4) floats, and
+ *     two more arrays follow: the read-out rows times the group-local prefix
+ *     pair, [n-1, h_v, 8, 2 d_k] fp32 (rounded up to 256 bytes), and the
+ *     state entering each group, [ng, h_v, d_k, d_v] fp32.
  * Errors: HYPIC_E_INVALID, HYPIC_E_UNSUPPORTED, HYPIC_E_WORKSPACE, HYPIC_E_HIP.
  */
 typedef struct {

@@ -364,10 +364,14 @@ template <int D, typename TIN>
 static hipError_t launch_ops(const ComposeArgs &a, int n_win, float *ops, hipStream_t st)
 {
     if (n_win <= 0) return hipSuccess;
-    if (a.seam.w <= 8)
-        hipLaunchKernelGGL((seam_ops_kernel<D, 8, TIN>), dim3(n_win * a.h_v), dim3(64), 0, st, a.seam, ops);
+    const bool ro = a.seam.q != nullptr;
+    if (ro && a.seam.w > 8) return hipErrorInvalidValue;   // read-out records hold windows of <= 8 rows
+    if (ro)
+        hipLaunchKernelGGL((seam_ops_kernel<D, 8, TIN, true>), dim3(n_win * a.h_v), dim3(64), 0, st, a.seam, ops);
+    else if (a.seam.w <= 8)
+        hipLaunchKernelGGL((seam_ops_kernel<D, 8, TIN, false>), dim3(n_win * a.h_v), dim3(64), 0, st, a.seam, ops);
     else
-        hipLaunchKernelGGL((seam_ops_kernel<D, 16, TIN>), dim3(n_win * a.h_v), dim3(64), 0, st, a.seam, ops);
+        hipLaunchKernelGGL((seam_ops_kernel<D, 16, TIN, false>), dim3(n_win * a.h_v), dim3(64), 0, st, a.seam, ops);
     return hipGetLastError();
 }
 
@@ -375,38 +379,80 @@ static hipError_t launch_ops(const ComposeArgs &a, int n_win, float *ops, hipStr
 // pos (launch-local j = pos - first_pos, group j / G) with state S_g entering
 // its group, Y = A [P | Q] the read-out rows times the group-local prefix pair
 // at the window (written by the group kernel), o = Y_P S_g + Y_Q + C.  One
-// 256-thread workgroup per (window, value head); thread (row set, column c)
-// forms o_t[c] for its rows t, the Y rows broadcast from LDS.
+// 256-thread workgroup per (group, value head, 64-column block, chunk of 4
+// windows of the group): the block's columns of S_g and the chunk's Y_P rows in
+// LDS (every global load issued before the first LDS store, so they are all in
+// flight together); thread (row set rs, column c) forms rows rs, rs + 4, ... of
+// the chunk for its column, starting from its Y_Q + C.
 template <int D>
 __global__ void __launch_bounds__(256) seam_readout_kernel(const ComposeArgs a, const float *ops, const float *Y,
                                                            int G, int j_begin)
 {
-    constexpr int RS = 256 / D, RPT = 8 / RS;   // row sets, rows per thread
-    __shared__ float Ys[8][2 * D];
-    const int j = j_begin + (int)(blockIdx.x / a.h_v), h = blockIdx.x % a.h_v;
-    const int pos = a.first_pos + j, win = pos - 1;
+    constexpr int NCB = D / 64, CW = 4, RPT = 8 * CW / 4;   // column blocks, windows per chunk, rows per thread
+    constexpr int SF = D * 16 / 256, YF = 8 * CW * (D / 4) / 256;   // float4 per thread: S_g columns, Y_P rows
+    __shared__ float Ss[D][64];
+    __shared__ float4 Ys[8 * CW][D / 4];
+    const int cb = blockIdx.x % NCB, h = (blockIdx.x / NCB) % a.h_v, gi = blockIdx.x / (NCB * a.h_v);
+    const int jlo = gi * G + CW * (int)blockIdx.y, je = min(min(gi * G + G, a.n), jlo + CW);
+    const int j0 = max(jlo, j_begin);
+    if (j0 >= je) return;   // a chunk with no window
+    const int tid = threadIdx.x, c = tid % 64, rs = tid / 64;
+    const int col = 64 * cb + c;
     const int w = a.seam.w, wp = winop_wp(w);
-    const float *yr = Y + ((int64_t)win * a.h_v + h) * 8 * 2 * D;
-    for (int e = threadIdx.x; e < 8 * 2 * D / 4; e += 256)
-        reinterpret_cast<float4 *>(&Ys[0][0])[e] = reinterpret_cast<const float4 *>(yr)[e];
-    __syncthreads();
-    const int c = threadIdx.x % D, rs = threadIdx.x / D;
-    const float *Sg = a.S_steps + ((int64_t)(j / G) * a.h_v + h) * D * D + c;
+    const int nwc = je - j0;
+    //   S_g columns: float4 f = tid + 256 i -> row f / 16, columns 4 (f % 16) ..
+    //   Y_P rows: float4 f -> row r = f / (D/4) (window j0 + r / 8, token r % 8),
+    //   columns 4 (f % (D/4)) ..; rows past the chunk read a clamped window and
+    //   are never stored
+    float4 sv[SF], yv[YF];
+    {
+        const float *Sg = a.S_steps + ((int64_t)gi * a.h_v + h) * D * D + 64 * cb;
+#pragma unroll
+        for (int i = 0; i < SF; ++i) {
+            const int f = tid + 256 * i;
+            sv[i] = *reinterpret_cast<const float4 *>(Sg + (int64_t)(f / 16) * D + 4 * (f % 16));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < YF; ++i) {
+        const int f = tid + 256 * i, r = f / (D / 4), v = min(r / 8, nwc - 1), t = r % 8;
+        const float *yr = Y + (((int64_t)(a.first_pos + j0 + v - 1) * a.h_v + h) * 8 + t) * 2 * D;
+        yv[i] = *reinterpret_cast<const float4 *>(yr + 4 * (f % (D / 4)));
+    }
     float acc[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) acc[i] = 0.f;
-#pragma unroll 8
-    for (int k = 0; k < D; ++k) {
-        const float sv = Sg[(int64_t)k * D];
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) acc[i] += Ys[rs + RS * i][k] * sv;
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rs + 4 * i, v = min(r / 8, nwc - 1), t = r % 8;
+        const int win = a.first_pos + j0 + v - 1;
+        const float *yr = Y + (((int64_t)win * a.h_v + h) * 8 + t) * 2 * D + D + col;
+        const float *Cr = ops + ((int64_t)win * a.h_v + h) * winop_floats<D>(w, true) + (int64_t)4 * wp * D +
+                          (int64_t)min(t, wp - 1) * D + col;
+        acc[i] = *yr + *Cr;
     }
-    const float *Cr = ops + ((int64_t)win * a.h_v + h) * winop_floats<D>(w, true) + (int64_t)4 * wp * D;
+#pragma unroll
+    for (int i = 0; i < SF; ++i) reinterpret_cast<float4 *>(&Ss[0][0])[tid + 256 * i] = sv[i];
+#pragma unroll
+    for (int i = 0; i < YF; ++i) {
+        const int f = tid + 256 * i;
+        Ys[f / (D / 4)][f % (D / 4)] = yv[i];
+    }
+    __syncthreads();   // S_g columns and the chunk's Y_P rows in LDS
+#pragma unroll 2
+    for (int k4 = 0; k4 < D / 4; ++k4) {
+        const float s0 = Ss[4 * k4][c], s1 = Ss[4 * k4 + 1][c], s2 = Ss[4 * k4 + 2][c], s3 = Ss[4 * k4 + 3][c];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const float4 y = Ys[rs + 4 * i][k4];
+            acc[i] += y.x * s0 + y.y * s1 + y.z * s2 + y.w * s3;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-        const int t = rs + RS * i;
-        if (t < w)
-            a.seam.o[(((int64_t)win * w + t) * a.h_v + h) * D + c] = acc[i] + Ys[t][D + c] + Cr[(int64_t)t * D + c];
+        const int r = rs + 4 * i, v = r / 8, t = r % 8;
+        if (v < nwc && t < w) {
+            const int win = a.first_pos + j0 + v - 1;
+            a.seam.o[(((int64_t)win * w + t) * a.h_v + h) * D + col] = acc[i];
+        }
     }
 }
 
@@ -415,10 +461,10 @@ hipError_t launch_seam_readout(const ComposeArgs &a, int D, const float *ops, co
 {
     // windows of this launch: positions first_pos + j >= 1
     const int j_begin = a.first_pos == 0 ? 1 : 0;
-    const int nw = a.n - j_begin;
-    if (nw <= 0) return hipSuccess;
-    if (a.seam.w > 8 || !a.S_steps || !a.seam.o) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)(nw * a.h_v));
+    if (a.n - j_begin <= 0) return hipSuccess;
+    if (a.seam.w > 8 || G < 1 || !a.S_steps || !a.seam.o) return hipErrorInvalidValue;
+    const int ng = (a.n + G - 1) / G;
+    const dim3 grid((unsigned)(ng * a.h_v * (D / 64)), (unsigned)((G + 3) / 4));
     if (D == 128) hipLaunchKernelGGL((seam_readout_kernel<128>), grid, dim3(256), 0, st, a, ops, Y, G, j_begin);
     else if (D == 64) hipLaunchKernelGGL((seam_readout_kernel<64>), grid, dim3(256), 0, st, a, ops, Y, G, j_begin);
     else return hipErrorInvalidValue;

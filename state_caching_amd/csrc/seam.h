@@ -228,22 +228,15 @@ __host__ __device__ __forceinline__ int64_t winop_floats(int w, bool ro) { retur
 // columns d = lane + 64 c in registers, M and the gates in LDS):
 //   A_t = gam_t (q_t - sum_{s<=t} (q_t.k_s) W_s),  W_s = sum_{r<=s} M_sr b_r k_r,
 //   C_t = sum_{r<=t} H_tr b_r (gam_t / gam_r) v_r, H_tr = sum_{r<=s<=t} (q_t.k_s) M_sr.
-template <int D, int WM, typename TIN>
-__device__ __forceinline__ void seam_ops_readout(const SeamArgs &a, int win, int h, const float (&K)[WM][D / 64],
-                                                 const float (&V)[WM][D / 64], float (&QK)[WM][WM + 1],
-                                                 float (&H)[WM][WM + 1], const float (&M)[WM][WM + 1],
-                                                 const float *bq, const float *cl, float *o)
+template <int D, int WM>
+__device__ __forceinline__ void seam_ops_readout(const SeamArgs &a, const float (&Q)[WM][D / 64],
+                                                 const float (&K)[WM][D / 64], const float (&V)[WM][D / 64],
+                                                 float (&QK)[WM][WM + 1], float (&H)[WM][WM + 1],
+                                                 const float (&M)[WM][WM + 1], const float *bq, const float *cl,
+                                                 float *o)
 {
     constexpr int C = D / 64, NQ = WM * (WM + 1) / 2;
     const int lane = threadIdx.x, w = a.w, wp = winop_wp(w);
-    const int kh = h / (a.h_v / a.h_k);
-    const int64_t ldk = (int64_t)a.h_k * D;
-    const TIN *qp = reinterpret_cast<const TIN *>(a.q) + (int64_t)win * w * ldk + (int64_t)kh * D;
-    float Q[WM][C];
-#pragma unroll
-    for (int t = 0; t < WM; ++t)
-#pragma unroll
-        for (int c = 0; c < C; ++c) Q[t][c] = t < w ? ld1(qp + (int64_t)(t < w ? t : 0) * ldk + lane + 64 * c) : 0.f;
     {   // q_t.k_s for s <= t, all reduced together
         float dot[NQ];
 #pragma unroll
@@ -266,11 +259,11 @@ __device__ __forceinline__ void seam_ops_readout(const SeamArgs &a, int win, int
         }
     }
     __syncthreads();
-    for (int e = lane; e < WM * WM; e += 64) {   // H_tr, r <= t
+    for (int e = lane; e < WM * WM; e += 64) {   // H_tr b_r gam_t / gam_r, r <= t
         const int t = e / WM, r = e % WM;
         float acc = 0.f;
         for (int s = r; s <= t; ++s) acc += QK[t][s] * M[s][r];
-        H[t][r] = r <= t ? acc : 0.f;
+        H[t][r] = r <= t ? acc * bq[r] * exp2f(cl[t] - cl[r]) : 0.f;
     }
     __syncthreads();
     float *oA = o + (int64_t)3 * wp * D, *oC = o + (int64_t)4 * wp * D;
@@ -291,7 +284,7 @@ __device__ __forceinline__ void seam_ops_readout(const SeamArgs &a, int win, int
 #pragma unroll
             for (int s = 0; s <= t; ++s) sa -= QK[t][s] * Wd[s];
 #pragma unroll
-            for (int r = 0; r <= t; ++r) sc += H[t][r] * bq[r] * exp2f(cl[t] - cl[r]) * V[r][c];
+            for (int r = 0; r <= t; ++r) sc += H[t][r] * V[r][c];
             const bool in = t < w;
             if (t < wp) {
                 oA[(int64_t)t * D + d] = in ? exp2f(cl[t]) * sa : 0.f;
@@ -305,7 +298,7 @@ __device__ __forceinline__ void seam_ops_readout(const SeamArgs &a, int win, int
 // key and value rows held in registers (C = D/64 columns per lane) and the
 // small w x w factors in LDS.  WM (8 or 16) bounds w; every loop over tokens
 // runs to WM with rows beyond w zero, so reductions interleave without branches.
-template <int D, int WM, typename TIN>
+template <int D, int WM, typename TIN, bool RO>
 __global__ void __launch_bounds__(64) seam_ops_kernel(const SeamArgs a, float *ops)
 {
     constexpr int C = D / 64, XR = WM + 3, NP = WM * (WM - 1) / 2;
@@ -313,7 +306,7 @@ __global__ void __launch_bounds__(64) seam_ops_kernel(const SeamArgs a, float *o
     __shared__ float M[WM][WM + 1];   // (I + G)^-1, unit lower triangular
     __shared__ float bq[WM], bd[WM];  // b_q and b_q dec_q
     __shared__ float QK[WM][WM + 1];  // q_t.k_s, s <= t (read-outs)
-    __shared__ float H[WM][WM + 1];   // sum_{r<=s<=t} QK_ts M_sr (read-outs)
+    __shared__ float H[WM][WM + 1];   // sum_{r<=s<=t} QK_ts M_sr b_r gam_t / gam_r (read-outs)
     __shared__ float cl[WM];          // log2 gam_t (read-outs)
     const int lane = threadIdx.x;
     const int win = blockIdx.x / a.h_v, h = blockIdx.x % a.h_v;
@@ -324,14 +317,34 @@ __global__ void __launch_bounds__(64) seam_ops_kernel(const SeamArgs a, float *o
     const TIN *xv = reinterpret_cast<const TIN *>(a.xv) + (int64_t)win * w * ldv + (int64_t)h * D;
     const TIN *tk = Wc > 1 ? reinterpret_cast<const TIN *>(a.tail_k) + (int64_t)win * (Wc - 1) * ldk + (int64_t)kh * D : nullptr;
     const TIN *tv = Wc > 1 ? reinterpret_cast<const TIN *>(a.tail_v) + (int64_t)win * (Wc - 1) * ldv + (int64_t)h * D : nullptr;
-    const bool ro = a.q != nullptr;
-    float *o = ops + ((int64_t)win * a.h_v + h) * winop_floats<D>(w, ro);
+    // RO: with the window's read-out operators (the records are laid out for them)
+    constexpr bool ro = RO && WM <= 8;
+    float *o = ops + ((int64_t)win * a.h_v + h) * winop_floats<D>(w, RO);
 
     // gates first (their loads overlap the row loads): b, suffix decay, window product
     float gb = 0.f, gl2 = 0.f;
     if (lane < w) {
         gb = ld1(reinterpret_cast<const TIN *>(a.beta) + ((int64_t)win * w + lane) * a.h_v + h);
         gl2 = log2f(ld1(reinterpret_cast<const TIN *>(a.alpha) + ((int64_t)win * w + lane) * a.h_v + h));
+    }
+
+    // final queries of the window (read-outs), loads in flight with the rows below
+    float Q[WM][C];
+#pragma unroll
+    for (int t = 0; t < WM; ++t)
+#pragma unroll
+        for (int c = 0; c < C; ++c) Q[t][c] = 0.f;
+    if constexpr (ro) {
+        {
+            const TIN *qp = reinterpret_cast<const TIN *>(a.q) + (int64_t)win * w * ldk + (int64_t)kh * D;
+#pragma unroll
+            for (int t = 0; t < WM; ++t)
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    const float x = ld1(qp + (int64_t)(t < w ? t : 0) * ldk + lane + 64 * c);
+                    Q[t][c] = t < w ? x : 0.f;
+                }
+        }
     }
 
     // keys and values after the causal conv: the extended rows (Wc - 1 tail rows,
@@ -404,8 +417,8 @@ __global__ void __launch_bounds__(64) seam_ops_kernel(const SeamArgs a, float *o
             bq[lane] = gb;
             bd[lane] = gb * exp2f(sfx);
         }
-        if (lane == 0) o[winop_gw<D>(w, ro)] = scale_pow2(1.f, tot);
-        if (ro) {   // log2 gam_t, inclusive prefix
+        if (lane == 0) o[winop_gw<D>(w, RO)] = scale_pow2(1.f, tot);
+        if constexpr (ro) {   // log2 gam_t, inclusive prefix
             const float pre = wave_prefix_incl(gl2);
             if (lane < WM) cl[lane] = pre;
         }
@@ -476,8 +489,8 @@ __global__ void __launch_bounds__(64) seam_ops_kernel(const SeamArgs a, float *o
             if (t4 < wp)
                 *reinterpret_cast<float4 *>(oUT + (int64_t)d * wp + t4) = make_float4(Ud[t4], Ud[t4 + 1], Ud[t4 + 2], Ud[t4 + 3]);
     }
-    if constexpr (WM <= 8)   // read-outs ride on windows of up to 8 rows
-        if (ro) seam_ops_readout<D, WM, TIN>(a, win, h, K, V, QK, H, M, bq, cl, o);
+    if constexpr (ro)   // read-outs ride on windows of up to 8 rows
+        seam_ops_readout<D, WM>(a, Q, K, V, QK, H, M, bq, cl, o);
 }
 
 }  // namespace hy
