@@ -44,6 +44,7 @@ KERNEL_SOURCES = {
     "compose_group_kernel": ["compose_group.hip", "seam.h", "common.h", "launch.h"],
     "build_kda_kernel": ["build_kda.hip", "common.h", "launch.h"],
     "rope_keys_kernel": ["rope.hip", "common.h", "launch.h"],
+    "seam_readout_kernel": ["compose_split.hip", "seam.h", "common.h", "launch.h"],
 }
 
 
@@ -314,7 +315,11 @@ def main():
                                                    "<128,seams,read-outs> + compose_split_kernel (group-start states) "
                                                    "+ seam_readout_kernel<128>",
                                          "achieved": gbs_r, "peak": PEAK_HBM, "unit": "GB/s",
-                                         "frac": gbs_r / PEAK_HBM, "traffic": None, "algorithmic_bytes": by_r}}
+                                         "frac": gbs_r / PEAK_HBM,
+                                         "traffic": counter_traffic(["seam_ops_kernel", "compose_group_kernel",
+                                                                     "compose_split_kernel", "seam_readout_kernel"],
+                                                                    "gdn_100_segments_readouts"),
+                                         "algorithmic_bytes": by_r}}
         del sm_ro, q4
         out["compose"] = comp
         if "value" not in out:

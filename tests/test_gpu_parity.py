@@ -415,7 +415,7 @@ def _readout_errs(o_gpu, o_ref):
     return whole, per
 
 
-@pytest.mark.parametrize("d,G", [(64, 2), (64, 5), (128, 0), (128, 3), (128, 7)])
+@pytest.mark.parametrize("d,G", [(64, 1), (64, 2), (64, 5), (128, 0), (128, 1), (128, 3), (128, 7)])
 def test_group_compose_readouts(d, G):
     """Window read-outs o_t = q_t^T S_t inside the two-level compose (ch.2 sec.5:
     the recomputed window tokens produce their outputs from the true prefix
@@ -434,6 +434,27 @@ def test_group_compose_readouts(d, G):
     S = dw.compose(T, S0, S_init=S_init.cuda(), group_len=G)
     torch.cuda.synchronize()
     S_or, o_or = oracle.compose(np64(T), np64(S0), S_init=np64(S_init), wl=wl, seams=True, q=q)
+    eS = oracle.relF(np64(S), S_or)
+    eo, eo_win = _readout_errs(np64(dw.seams.o), o_or)
+    print(f"  relF S {eS:.3e}, o {eo:.3e} (worst window {eo_win:.3e})")
+    assert eS <= 2e-5 and eo <= 2e-5 and eo_win <= 1e-4
+
+
+@pytest.mark.parametrize("n", [2, 5])
+def test_compose_readouts_short_chain(n):
+    """Read-outs on a chain shorter than the automatic grouping threshold (one
+    group holds every position) and with windows narrower than 8 rows."""
+    need_gpu()
+    wl = synth.gdn(160 + n, [30 + 7 * i for i in range(n)], 2, 4, 64, torch.bfloat16, alpha_div=32.0,
+                   conv_w=4, seam_w=5)
+    sca, DW = _lib()
+    dw = DW(wl)
+    T, S0 = dw.build()
+    q = _attach_queries(dw, 161 + n)
+    case(f"compose with read-outs, short chain n={n}, w=5")
+    S = dw.compose(T, S0)
+    torch.cuda.synchronize()
+    S_or, o_or = oracle.compose(np64(T), np64(S0), wl=wl, seams=True, q=q)
     eS = oracle.relF(np64(S), S_or)
     eo, eo_win = _readout_errs(np64(dw.seams.o), o_or)
     print(f"  relF S {eS:.3e}, o {eo:.3e} (worst window {eo_win:.3e})")
