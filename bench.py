@@ -175,6 +175,43 @@ def cpu_baseline(wl, target_s=12.0):
                       f"{dt:.1f} s wall on {thr} threads; tokens/s scaled by {n}/{len(units)}"}
 
 
+def measured_peaks(torch, dev):
+    """What this GPU reaches on plain library work, beside the published peaks
+    the roofline fractions use: a 1 GiB device-to-device copy (read + write
+    bytes) and a bf16 8192^3 GEMM (torch.matmul)."""
+    log("measuring a device copy and a bf16 GEMM for context")
+    x = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    x.fill_(1.0)
+    for _ in range(2):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * x.numel() * 4 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x, y
+    n = 8192
+    a = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+    b = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+    for _ in range(2):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tf = 2.0 * n ** 3 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBps": copy_gbs, "bf16_gemm_TFLOPs": gemm_tf,
+            "note": "context only; roofline fractions use the published peaks"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -388,6 +425,8 @@ def main():
         del K6, K6o
         torch.cuda.empty_cache()
 
+    if args.leg == "all":
+        out["measured_peaks"] = measured_peaks(torch, dev)
     if not args.no_cpu:
         log("timing the fp64 oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(synth.workload("gdn_gqa_d128_8x4096_bf16"))
