@@ -471,14 +471,8 @@ static hipError_t launch_one(const DeltaArgs &a, int n_units, hipStream_t st)
 {
     using C = DeltaCfg<D, F16>;
     const size_t smem = sizeof(DeltaSmem<D, F16>);
-    static bool attr_set = false;   // benign race: every setter writes the same value
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&build_delta_kernel<D, F16, TKV, TG>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (hipError_t e = allow_dyn_lds(&build_delta_kernel<D, F16, TKV, TG>, smem, lds_set); e != hipSuccess) return e;
     hipLaunchKernelGGL((build_delta_kernel<D, F16, TKV, TG>), dim3(n_units), dim3(C::NT), smem, st, a);
     return hipGetLastError();
 }

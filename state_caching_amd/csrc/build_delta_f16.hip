@@ -568,13 +568,9 @@ template <int D, typename TK, typename TV, typename TG>
 hipError_t launch_f16_one(const DeltaArgs &a, int n_units, hipStream_t st)
 {
     const size_t smem = sizeof(F16Smem<D>);
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&build_delta_f16_kernel<D, TK, TV, TG>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (hipError_t e = allow_dyn_lds(&build_delta_f16_kernel<D, TK, TV, TG>, smem, lds_set); e != hipSuccess)
+        return e;
     hipLaunchKernelGGL((build_delta_f16_kernel<D, TK, TV, TG>), dim3(n_units), dim3(F16Cfg<D>::NT), smem, st, a);
     return hipGetLastError();
 }

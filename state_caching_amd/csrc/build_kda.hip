@@ -333,13 +333,8 @@ template <int D, typename TKV, typename TG>
 static hipError_t launch_kda_one(const DeltaArgs &a, int n_units, hipStream_t st)
 {
     const size_t smem = sizeof(KdaSmem<D>);
-    static bool attr_set = false;   // benign race: every setter writes the same value
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&build_kda_kernel<D, TKV, TG>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (hipError_t e = allow_dyn_lds(&build_kda_kernel<D, TKV, TG>, smem, lds_set); e != hipSuccess) return e;
     hipLaunchKernelGGL((build_kda_kernel<D, TKV, TG>), dim3(n_units), dim3(KdaCfg<D>::NT), smem, st, a);
     return hipGetLastError();
 }

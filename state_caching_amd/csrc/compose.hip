@@ -220,24 +220,14 @@ __global__ void __launch_bounds__(256) seam_kernel(const ComposeArgs a, float *S
     }
 }
 
-template <typename K>
-static hipError_t set_smem(K kern, size_t bytes)
-{
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-}
-
 template <int D, bool SPLIT, bool SEAMS, typename TIN>
 static hipError_t launch_dense(const ComposeArgs &a, hipStream_t st)
 {
     using C = ComposeCfg<D, SPLIT>;
     const size_t smem = sizeof(ComposeSmem<D, SEAMS>);
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = set_smem(&compose_dense_kernel<D, SPLIT, SEAMS, TIN>, smem);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (hipError_t e = allow_dyn_lds(&compose_dense_kernel<D, SPLIT, SEAMS, TIN>, smem, lds_set); e != hipSuccess)
+        return e;
     hipLaunchKernelGGL((compose_dense_kernel<D, SPLIT, SEAMS, TIN>), dim3(a.h_v * (D / 16)),
                        dim3(C::NT), smem, st, a);
     return hipGetLastError();
@@ -281,12 +271,8 @@ template <int D, typename TIN>
 static hipError_t launch_seam_t(const ComposeArgs &a, float *S, int n_win, hipStream_t st)
 {
     const size_t smem = sizeof(float) * 16 * (D + 4) + sizeof(WinSmem<D, 64>);
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = set_smem(&seam_kernel<D, TIN>, smem);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (hipError_t e = allow_dyn_lds(&seam_kernel<D, TIN>, smem, lds_set); e != hipSuccess) return e;
     hipLaunchKernelGGL((seam_kernel<D, TIN>), dim3(a.h_v * (D / 16)), dim3(256), smem, st, a, S, n_win);
     return hipGetLastError();
 }

@@ -425,13 +425,9 @@ static hipError_t launch_cg(const ComposeArgs &a, const float *ops, int G, int n
                             hipStream_t st)
 {
     const size_t smem = sizeof(CgSmem<D, NN, RO>);
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&compose_group_kernel<D, SEAMS, NN, RO>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (hipError_t e = allow_dyn_lds(&compose_group_kernel<D, SEAMS, NN, RO>, smem, lds_set); e != hipSuccess)
+        return e;
     hipLaunchKernelGGL((compose_group_kernel<D, SEAMS, NN, RO>), dim3(ng * a.h_v), dim3(CgCfg<D, NN>::NT), smem, st,
                        a, ops, G, gT, gS, Y);
     return hipGetLastError();

@@ -475,6 +475,8 @@ template <int D, bool SEAMS>
 static hipError_t launch_cs(const ComposeArgs &a, const float *ops, hipStream_t st)
 {
     const size_t smem = sizeof(CsSmem<D, SEAMS>);
+    static std::atomic<uint64_t> lds_set{0};
+    if (hipError_t e = allow_dyn_lds(&compose_split_kernel<D, SEAMS>, smem, lds_set); e != hipSuccess) return e;
     hipLaunchKernelGGL((compose_split_kernel<D, SEAMS>), dim3(a.h_v * (D / 16)), dim3(CsCfg<D, SEAMS>::NT), smem,
                        st, a, ops);
     return hipGetLastError();

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "hypic.h"
 
 namespace hy {
@@ -134,5 +136,22 @@ hipError_t launch_compose_group(const ComposeArgs &a, int D, const float *ops, i
 // the windows' read-out records (w <= 8)
 hipError_t launch_seam_readout(const ComposeArgs &a, int D, const float *ops, const float *Y, int G,
                                hipStream_t st);
+
+// Allow `bytes` of dynamic LDS for kernel `kern` on the current device, once
+// per device (bit d of `done`); concurrent first calls may both set the same
+// value, which is harmless, and the flag itself is atomic.
+template <typename K>
+inline hipError_t allow_dyn_lds(K kern, size_t bytes, std::atomic<uint64_t> &done)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 
 }  // namespace hy
