@@ -461,6 +461,27 @@ def test_compose_readouts_short_chain(n):
     assert eS <= 2e-5 and eo <= 2e-5 and eo_win <= 1e-4
 
 
+@pytest.mark.parametrize("d", [16, 32])
+def test_compose_readouts_small_heads(d):
+    """Read-outs with bf16 inputs at d = 16 and 32 (the dense compose kernel,
+    whose window code reads out itself), against the oracle."""
+    need_gpu()
+    wl = synth.gdn(170 + d, [40, 64, 33, 70], 1, 2, d, torch.bfloat16, alpha_div=32.0, conv_w=4,
+                   seam_w=8)
+    sca, DW = _lib()
+    dw = DW(wl)
+    T, S0 = dw.build()
+    q = _attach_queries(dw, 171 + d)
+    case(f"compose with read-outs, d={d}, bf16")
+    S = dw.compose(T, S0)
+    torch.cuda.synchronize()
+    S_or, o_or = oracle.compose(np64(T), np64(S0), wl=wl, seams=True, q=q)
+    eS = oracle.relF(np64(S), S_or)
+    eo, eo_win = _readout_errs(np64(dw.seams.o), o_or)
+    print(f"  relF S {eS:.3e}, o {eo:.3e} (worst window {eo_win:.3e})")
+    assert eS <= 2e-5 and eo <= 2e-5 and eo_win <= 1e-4
+
+
 def test_compose_readouts_fp32_path():
     """Read-outs on the fp32 compose path (fp32 inputs, windows in fp32
     arithmetic), a window wider than 8 rows: against the oracle."""
