@@ -399,12 +399,11 @@ def main():
     if args.leg in ("rope", "all"):
         log("rotary re-rotation of the cached keys of a 32k-token prompt (16 heads, d=128, bf16)")
         from state_caching_amd import rope_rerotate
-        g6 = torch.Generator(device="cpu").manual_seed(6)
-        n6, h6, d6 = 8 * 4096, 16, 128
-        K6 = torch.randn((n6, h6, d6), generator=g6).to(torch.bfloat16).to(dev)
+        r6 = synth.ROPE_32K
+        n6, h6 = r6["n_tokens"], r6["h"]
+        K6 = synth.rope_keys(r6["seed"], n6, h6, r6["d"]).to(dev)
         K6o = torch.empty_like(K6)
-        st6, ln6 = [4096 * i for i in range(8)], [4096] * 8
-        dl6 = [4096 * i + 517 for i in range(8)]
+        st6, ln6, dl6 = r6["seg_start"], r6["seg_len"], r6["delta"]
 
         def step6(ev):
             if ev: ev["rope"][0].record()

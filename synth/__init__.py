@@ -259,6 +259,20 @@ def random_pairs(seed, n_slots, h, d_k, d_v, tform="dense", rho=0.9):
     return _round(T, torch.float32), _round(S0, torch.float32)
 
 
+def rope_keys(seed, n_tokens, h, d, dtype=torch.bfloat16):
+    """Cached full-attention keys [n_tokens, h, d]: standard normal, drawn by a
+    seeded torch CPU generator, then rounded to dtype."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return torch.randn((n_tokens, h, d), generator=g).to(dtype)
+
+
+ROPE_32K = dict(seed=6, n_tokens=8 * 4096, h=16, d=128,
+                seg_start=[4096 * i for i in range(8)], seg_len=[4096] * 8,
+                delta=[4096 * i + 517 for i in range(8)])
+"""The 32k-token prompt's cached keys (8 segments x 4096, 16 KV heads, d = 128)
+and the shifts that move segment i to start 4096 i + 517 tokens later."""
+
+
 def random_state(seed, h, d_k, d_v):
     rng = np.random.default_rng(seed)
     return _round(rng.standard_normal((h, d_k, d_v)), torch.float32)

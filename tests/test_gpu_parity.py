@@ -647,6 +647,40 @@ def test_rope_keys(dtype, pairing, rot, inplace):
         assert np.array_equal(got[..., rot:], xr[..., rot:])
 
 
+def test_rope_keys_32k_prompt():
+    """The bench's workload in its launch configuration: the 32k-token prompt's
+    keys (8 segments x 4096, 16 heads, d = 128, bf16) moved out of place, every
+    element against the oracle (rounded once to bf16, the bound of
+    test_rope_keys)."""
+    need_gpu()
+    import state_caching_amd as sca
+    r = synth.ROPE_32K
+    x = synth.rope_keys(r["seed"], r["n_tokens"], r["h"], r["d"])
+    xin = x.cuda()
+    out = torch.empty_like(xin)
+    case("rope keys, 32k-token prompt, 16 heads, bf16, out of place")
+    sca.rope_rerotate(xin, r["seg_start"], r["seg_len"], r["delta"], out=out)
+    torch.cuda.synchronize()
+    got = np64(out)
+    del xin, out
+    xr = np64(x)
+    ref = np.empty_like(xr)
+    for s0, n, dl in zip(r["seg_start"], r["seg_len"], r["delta"]):
+        ref[s0:s0 + n] = oracle.rope_rotate(xr[s0:s0 + n], float(dl))
+    rb = np64(torch.from_numpy(ref).to(torch.float32).to(torch.bfloat16))
+    d = r["d"]
+    mag = np.maximum(np.maximum(np.abs(rb), np.abs(got)), 2.0 ** -126)
+    ulp = 2.0 ** (np.floor(np.log2(mag)) - 7)
+    part = (np.arange(d) + d // 2) % d
+    bound = ulp + 2.0 ** -22 * (np.abs(xr) + np.abs(xr[..., part]))
+    diff = np.abs(got - rb)
+    frac = np.mean(diff > 0)
+    print(f"  elements differing from the rounded oracle: {frac:.2e}, "
+          f"max {np.max(diff / bound):.2f} of the bound; relF {oracle.relF(got, ref):.3e}")
+    assert np.all(diff <= bound) and frac < 1e-3
+    assert oracle.relF(got, ref) <= 2e-3
+
+
 @pytest.mark.parametrize("pairing,rot", [(0, 128), (1, 64)])
 def test_rope_state(pairing, rot):
     """A state moved along its key dimension (Eq. (7)) against the oracle."""
