@@ -595,6 +595,17 @@ def test_kda_sampled_4096():
     _check_build(wl, segs=[1], heads=[0, 31], tol=2e-5, label="(sampled units)")
 
 
+def test_kda_32k_prompt_sampled():
+    """The bench's KDA workload in its launch configuration (8 x 4096 tokens, 32
+    value / 16 key heads, d = 128, bf16; all 256 units built in one launch), the
+    first and last segments of two heads against the oracle.  Its gates are
+    fast, so T_C underflows to zero on both sides after 4096 tokens; the slower
+    gates of test_kda_sampled_4096 keep a non-trivial T_C at this length."""
+    need_gpu()
+    wl = synth.workload("kda_gqa_d128_8x4096_bf16")
+    _check_build(wl, segs=[0, 7], heads=[0, 31], tol=2e-5, label="(sampled units)")
+
+
 # ------------------------------------------------------------- rotary re-rotation
 
 @pytest.mark.parametrize("dtype,pairing,rot,inplace", [
