@@ -248,9 +248,7 @@ __device__ __forceinline__ void seam_ops_readout(const SeamArgs &a, const float 
                 for (int c = 0; c < C; ++c) dot[p] += Q[t][c] * K[s][c];
             }
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1)
-#pragma unroll
-            for (int p = 0; p < NQ; ++p) dot[p] += __shfl_xor(dot[p], m);
+        for (int p = 0; p < NQ; ++p) dot[p] = wave_sum(dot[p]);
         if (lane == 0) {
 #pragma unroll
             for (int t = 0, p = 0; t < WM; ++t)
@@ -400,9 +398,7 @@ __global__ void __launch_bounds__(64) seam_ops_kernel(const SeamArgs a, float *o
             for (int c = 0; c < C; ++c) ss[t] += K[t][c] * K[t][c];
         }
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1)
-#pragma unroll
-            for (int t = 0; t < WM; ++t) ss[t] += __shfl_xor(ss[t], m);
+        for (int t = 0; t < WM; ++t) ss[t] = wave_sum(ss[t]);
 #pragma unroll
         for (int t = 0; t < WM; ++t) {
             const float inv = ss[t] > 0.f ? 1.f / sqrtf(ss[t]) : 0.f;
@@ -435,9 +431,7 @@ __global__ void __launch_bounds__(64) seam_ops_kernel(const SeamArgs a, float *o
                 for (int c = 0; c < C; ++c) dot[p] += K[r][c] * K[q][c];
             }
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1)
-#pragma unroll
-            for (int p = 0; p < NP; ++p) dot[p] += __shfl_xor(dot[p], m);
+        for (int p = 0; p < NP; ++p) dot[p] = wave_sum(dot[p]);
         __syncthreads();   // bq visible
         if (lane == 0) {
 #pragma unroll
