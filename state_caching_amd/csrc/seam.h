@@ -367,10 +367,18 @@ __global__ void __launch_bounds__(64) seam_ops_kernel(const SeamArgs a, float *o
             xk_[r] = in ? kx : 0.f;
             xv_[r] = in ? vx : 0.f;
         }
+        // the taps as four independent loads (index clamped into the row, weight 0
+        // past the conv width), so they are in flight together with the rows above
         float wk[4] = {0.f, 0.f, 0.f, 0.f}, wvv[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < Wc; ++j) {
-            wk[j] = a.conv_wk[((int64_t)kh * D + d) * Wc + j];
-            wvv[j] = a.conv_wv[((int64_t)h * D + d) * Wc + j];
+        if (Wc > 0) {   // no weights without a conv (the pointers may be null)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int jj = min(j, Wc - 1);
+                const float xk = a.conv_wk[((int64_t)kh * D + d) * Wc + jj];
+                const float xv = a.conv_wv[((int64_t)h * D + d) * Wc + jj];
+                wk[j] = j < Wc ? xk : 0.f;
+                wvv[j] = j < Wc ? xv : 0.f;
+            }
         }
 #pragma unroll
         for (int t = 0; t < WM; ++t) {
