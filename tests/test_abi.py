@@ -153,6 +153,34 @@ def test_compose_seam_validation(sca):
     assert need > L.hypic_workspace_size(ctypes.byref(d), sca.WS_COMPOSE)
 
 
+def test_compose_workspace_sizes(sca):
+    """Workspace of the 100-segment compose with seams (h_v = 32, d = 128, w = 8),
+    without and with window read-outs, against the layout the header states:
+    window records of (3 wp d + 4) floats, or (5 wp d + 4) with read-outs, then
+    two pools of group pairs, then (read-outs) the rows Y [n-1, h_v, 8, 2d] and
+    the states entering the groups; each array rounded up to 256 bytes."""
+    L = sca.library()
+    n, h, d, w = 100, 32, 128, 8
+    sd = sca.SeamDesc(rule=sca.RULE_DELTA, in_dtype=sca.BF16, w=w, conv_w=4, k_l2norm=1, h_k=h,
+                      h_v=h, d_k=d, d_v=d, n_win=n - 1, xk=16, xv=16, tail_k=16, tail_v=16,
+                      conv_wk=16, conv_wv=16, beta=16, alpha=16)
+    dsc = _compose_desc(sca, order=list(range(n)), h_v=h, n_slots=n, seams=ctypes.pointer(sd))
+    al = lambda b: (b + 255) // 256 * 256
+    wp = (w + 3) // 4 * 4
+    G = -(-n // (256 // h))              # automatic group length: one (group, head) per CU
+    ng = -(-n // G)
+    pool = ng * h * d * d * 4
+    plain = al((3 * wp * d + 4) * (n - 1) * h * 4) + 2 * pool
+    assert L.hypic_workspace_size(ctypes.byref(dsc), sca.WS_COMPOSE) == plain
+    sd.q, sd.o = 16, 16
+    ro = al((5 * wp * d + 4) * (n - 1) * h * 4) + 2 * pool + al((n - 1) * h * 8 * 2 * d * 4) + pool
+    assert L.hypic_workspace_size(ctypes.byref(dsc), sca.WS_COMPOSE) == ro
+    # the fp32 path keeps its windows in the kernel: no workspace either way
+    d32 = _compose_desc(sca, order=list(range(n)), h_v=h, n_slots=n, prec=sca.PREC_FP32,
+                        seams=ctypes.pointer(sd))
+    assert L.hypic_workspace_size(ctypes.byref(d32), sca.WS_COMPOSE) == 0
+
+
 def test_seam_validation(sca):
     L = sca.library()
     sd = sca.SeamDesc(rule=sca.RULE_DELTA, in_dtype=sca.F32, w=65, conv_w=0, k_l2norm=0, h_k=1,

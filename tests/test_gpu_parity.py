@@ -415,7 +415,8 @@ def _readout_errs(o_gpu, o_ref):
     return whole, per
 
 
-@pytest.mark.parametrize("d,G", [(64, 1), (64, 2), (64, 5), (128, 0), (128, 1), (128, 3), (128, 7)])
+@pytest.mark.parametrize("d,G", [(64, 1), (64, 2), (64, 5), (128, 0), (128, 1), (128, 3), (128, 7),
+                                 (128, 64)])
 def test_group_compose_readouts(d, G):
     """Window read-outs o_t = q_t^T S_t inside the two-level compose (ch.2 sec.5:
     the recomputed window tokens produce their outputs from the true prefix
