@@ -503,6 +503,31 @@ def test_compose_readouts_fp32_path():
     assert eS <= 1e-5 and eo <= 1e-5 and eo_win <= 1e-4
 
 
+def test_compose_readouts_twice():
+    """Two read-out composes in a row with different queries and one workspace
+    (the records, Y and the group-start states are rewritten by the second call):
+    each against the oracle."""
+    need_gpu()
+    import state_caching_amd as sca_mod
+    lens = [40, 64, 33, 70, 21, 64, 50, 90, 17, 64, 45, 80, 66, 29, 55, 64, 38, 70]
+    wl = synth.gdn(180, lens, 1, 2, 128, torch.bfloat16, alpha_div=64.0, conv_w=4, seam_w=8)
+    sca, DW = _lib()
+    dw = DW(wl)
+    T, S0 = dw.build()
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    order = list(range(wl.n_seg))
+    for call, seed in enumerate((181, 182)):
+        q = _attach_queries(dw, seed)
+        case(f"compose with read-outs, call {call} of two, one workspace")
+        S = sca_mod.compose(T, S0, order, tform=dw.tform, prec=dw.prec, seams=dw.seams, workspace=ws)
+        torch.cuda.synchronize()
+        S_or, o_or = oracle.compose(np64(T), np64(S0), wl=wl, seams=True, q=q)
+        eS = oracle.relF(np64(S), S_or)
+        eo, eo_win = _readout_errs(np64(dw.seams.o), o_or)
+        print(f"  call {call}: relF S {eS:.3e}, o {eo:.3e} (worst window {eo_win:.3e})")
+        assert eS <= 2e-5 and eo <= 2e-5 and eo_win <= 1e-4
+
+
 def test_group_compose_readouts_across_launches():
     """Read-outs over more positions than one launch holds: windows indexed by
     prompt position, group-start states per launch."""
