@@ -116,12 +116,12 @@ int compose_group_len(const hypic_compose_desc *d, int nb)
 {
     if (compose_readouts(d) && compose_uses_split(d)) {
         // read-outs ride on the group kernel: every launch takes the two-level
-        // path, one group for a short launch
+        // path, with enough (group, head) workgroups to fill the chip once (groups
+        // of one position for a short launch with few heads)
         if (d->group_len >= 1) return std::min(d->group_len, std::max(nb, 1));
-        if (nb < 16) return std::max(nb, 1);
         const int per_cu = d->d_k == 128 ? 1 : 2;
         const int ng = std::max(1, 256 * per_cu / d->h_v);
-        return (nb + ng - 1) / ng;
+        return std::max(1, (nb + ng - 1) / ng);
     }
     if (!compose_uses_split(d) || nb < 2 || d->group_len == 1) return 1;
     if (d->seams && d->seams->w > 8) return 1;   // the group kernel holds windows of up to 8 rows
