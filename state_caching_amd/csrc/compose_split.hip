@@ -203,10 +203,9 @@ __global__ void __launch_bounds__((CsCfg<D, SEAMS>::NT)) compose_split_kernel(co
         put_state(0, Sown);
         int cur = 0;
         auto step = [&](const int j, const int s) __attribute__((always_inline)) {
-            if (a.S_steps) {   // the state entering step j, for the window read-outs
-                float *sp = a.S_steps + ((int64_t)j * a.h_v + h) * D * D + c0 + r16;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sp[(int64_t)(row0 + 4 * g + i) * D] = Sown[i];
+            if (a.S_steps) {   // the state entering step j, transposed ([column][row]), for the read-outs
+                float *sp = a.S_steps + ((int64_t)j * a.h_v + h) * D * D + (int64_t)(c0 + r16) * D + row0 + 4 * g;
+                *reinterpret_cast<float4 *>(sp) = make_float4(Sown[0], Sown[1], Sown[2], Sown[3]);
             }
             lds_barrier();   // S_j complete in buffer cur
             const f4 acc = product(S0b[s], cur);
@@ -379,81 +378,85 @@ static hipError_t launch_ops(const ComposeArgs &a, int n_win, float *ops, hipStr
 // pos (launch-local j = pos - first_pos, group j / G) with state S_g entering
 // its group, Y = A [P | Q] the read-out rows times the group-local prefix pair
 // at the window (written by the group kernel), o = Y_P S_g + Y_Q + C.  One
-// 256-thread workgroup per (group, value head, 64-column block, chunk of 4
-// windows of the group): the block's columns of S_g and the chunk's Y_P rows in
-// LDS (every global load issued before the first LDS store, so they are all in
-// flight together); thread (row set rs, column c) forms rows rs, rs + 4, ... of
-// the chunk for its column, starting from its Y_Q + C.
+// 256-thread workgroup per (group, value head, chunk of 4 windows of the
+// group): the chunk's 32 rows (window, token) times S_g on the matrix cores,
+// fp32 operands split into bf16 hi + lo (three products per term).  A
+// fragments are 8 consecutive entries of a Y_P row, B fragments 8 consecutive
+// rows of one column of S_g, which the fold stores transposed, so both load as
+// whole vectors; wave w owns column tiles w, w + 4, ...
 template <int D>
 __global__ void __launch_bounds__(256) seam_readout_kernel(const ComposeArgs a, const float *ops, const float *Y,
                                                            int G, int j_begin)
 {
-    constexpr int NCB = D / 64, CW = 4, RPT = 8 * CW / 4;   // column blocks, windows per chunk, rows per thread
-    constexpr int SF = D * 16 / 256, YF = 8 * CW * (D / 4) / 256;   // float4 per thread: S_g columns, Y_P rows
-    __shared__ float Ss[D][64];
-    __shared__ float4 Ys[8 * CW][D / 4];
-    const int cb = blockIdx.x % NCB, h = (blockIdx.x / NCB) % a.h_v, gi = blockIdx.x / (NCB * a.h_v);
+    constexpr int CW = 4, RT = 2 * CW / 4, KB = D / 32, CTW = D / 16 / 4;   // row tiles, k blocks, column tiles per wave
+    const int h = blockIdx.x % a.h_v, gi = blockIdx.x / a.h_v;
     const int jlo = gi * G + CW * (int)blockIdx.y, je = min(min(gi * G + G, a.n), jlo + CW);
     const int j0 = max(jlo, j_begin);
     if (j0 >= je) return;   // a chunk with no window
-    const int tid = threadIdx.x, c = tid % 64, rs = tid / 64;
-    const int col = 64 * cb + c;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g = lane >> 4;
     const int w = a.seam.w, wp = winop_wp(w);
     const int nwc = je - j0;
-    //   S_g columns: float4 f = tid + 256 i -> row f / 16, columns 4 (f % 16) ..
-    //   Y_P rows: float4 f -> row r = f / (D/4) (window j0 + r / 8, token r % 8),
-    //   columns 4 (f % (D/4)) ..; rows past the chunk read a clamped window and
-    //   are never stored
-    float4 sv[SF], yv[YF];
-    {
-        const float *Sg = a.S_steps + ((int64_t)gi * a.h_v + h) * D * D + 64 * cb;
+    // row r of the chunk = window j0 + r / 8 (clamped into the chunk), token r % 8
+    auto yrow = [&](int r) {
+        const int v = min(r / 8, nwc - 1);
+        return Y + (((int64_t)(a.first_pos + j0 + v - 1) * a.h_v + h) * 8 + r % 8) * 2 * D;
+    };
+    const float *St = a.S_steps + ((int64_t)gi * a.h_v + h) * D * D;
+    // the sums start from Y_Q + C of this lane's rows and columns (rows past the
+    // chunk or the window read clamped ones and are never stored), fetched first
+    // so that their loads overlap the products
+    f4 acc[RT][CTW];
 #pragma unroll
-        for (int i = 0; i < SF; ++i) {
-            const int f = tid + 256 * i;
-            sv[i] = *reinterpret_cast<const float4 *>(Sg + (int64_t)(f / 16) * D + 4 * (f % 16));
-        }
-    }
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int i = 0; i < YF; ++i) {
-        const int f = tid + 256 * i, r = f / (D / 4), v = min(r / 8, nwc - 1), t = r % 8;
-        const float *yr = Y + (((int64_t)(a.first_pos + j0 + v - 1) * a.h_v + h) * 8 + t) * 2 * D;
-        yv[i] = *reinterpret_cast<const float4 *>(yr + 4 * (f % (D / 4)));
-    }
-    float acc[RPT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = rs + 4 * i, v = min(r / 8, nwc - 1), t = r % 8;
-        const int win = a.first_pos + j0 + v - 1;
-        const float *yr = Y + (((int64_t)win * a.h_v + h) * 8 + t) * 2 * D + D + col;
-        const float *Cr = ops + ((int64_t)win * a.h_v + h) * winop_floats<D>(w, true) + (int64_t)4 * wp * D +
-                          (int64_t)min(t, wp - 1) * D + col;
-        acc[i] = *yr + *Cr;
-    }
-#pragma unroll
-    for (int i = 0; i < SF; ++i) reinterpret_cast<float4 *>(&Ss[0][0])[tid + 256 * i] = sv[i];
-#pragma unroll
-    for (int i = 0; i < YF; ++i) {
-        const int f = tid + 256 * i;
-        Ys[f / (D / 4)][f % (D / 4)] = yv[i];
-    }
-    __syncthreads();   // S_g columns and the chunk's Y_P rows in LDS
-#pragma unroll 2
-    for (int k4 = 0; k4 < D / 4; ++k4) {
-        const float s0 = Ss[4 * k4][c], s1 = Ss[4 * k4 + 1][c], s2 = Ss[4 * k4 + 2][c], s3 = Ss[4 * k4 + 3][c];
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const float4 y = Ys[rs + 4 * i][k4];
-            acc[i] += y.x * s0 + y.y * s1 + y.z * s2 + y.w * s3;
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = rs + 4 * i, v = r / 8, t = r % 8;
-        if (v < nwc && t < w) {
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * rt + 4 * g + i, v = min(r / 8, nwc - 1), t = r % 8;
             const int win = a.first_pos + j0 + v - 1;
-            a.seam.o[(((int64_t)win * w + t) * a.h_v + h) * D + col] = acc[i];
+            const float *yq = Y + (((int64_t)win * a.h_v + h) * 8 + t) * 2 * D + D;
+            const float *Cr = ops + ((int64_t)win * a.h_v + h) * winop_floats<D>(w, true) + (int64_t)4 * wp * D +
+                              (int64_t)min(t, wp - 1) * D;
+#pragma unroll
+            for (int c = 0; c < CTW; ++c) {
+                const int col = 16 * (wv + 4 * c) + r16;
+                acc[rt][c][i] = yq[col] + Cr[col];
+            }
         }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        const int k0 = 32 * kb + 8 * g;
+        b8 ah[RT], al[RT], bh[CTW], bl[CTW];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const float *p = yrow(16 * rt + r16) + k0;
+            const float4 u0 = *reinterpret_cast<const float4 *>(p), u1 = *reinterpret_cast<const float4 *>(p + 4);
+            const float x[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+            split8(x, ah[rt], al[rt]);
+        }
+#pragma unroll
+        for (int c = 0; c < CTW; ++c) {
+            const float *p = St + (int64_t)(16 * (wv + 4 * c) + r16) * D + k0;
+            const float4 u0 = *reinterpret_cast<const float4 *>(p), u1 = *reinterpret_cast<const float4 *>(p + 4);
+            const float x[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+            split8(x, bh[c], bl[c]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int c = 0; c < CTW; ++c) acc[rt][c] = mma3(ah[rt], al[rt], bh[c], bl[c], acc[rt][c]);
     }
+    // lane (g, r16) of tile (rt, c) holds rows 16 rt + 4 g + i, column 16 (wv + 4 c) + r16
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * rt + 4 * g + i, v = r / 8, t = r % 8;
+            if (v < nwc && t < w) {
+                const int win = a.first_pos + j0 + v - 1;
+                float *op = a.seam.o + (((int64_t)win * w + t) * a.h_v + h) * D;
+#pragma unroll
+                for (int c = 0; c < CTW; ++c) op[16 * (wv + 4 * c) + r16] = acc[rt][c][i];
+            }
+        }
 }
 
 hipError_t launch_seam_readout(const ComposeArgs &a, int D, const float *ops, const float *Y, int G,
@@ -464,7 +467,7 @@ hipError_t launch_seam_readout(const ComposeArgs &a, int D, const float *ops, co
     if (a.n - j_begin <= 0) return hipSuccess;
     if (a.seam.w > 8 || G < 1 || !a.S_steps || !a.seam.o) return hipErrorInvalidValue;
     const int ng = (a.n + G - 1) / G;
-    const dim3 grid((unsigned)(ng * a.h_v * (D / 64)), (unsigned)((G + 3) / 4));
+    const dim3 grid((unsigned)(ng * a.h_v), (unsigned)((G + 3) / 4));
     if (D == 128) hipLaunchKernelGGL((seam_readout_kernel<128>), grid, dim3(256), 0, st, a, ops, Y, G, j_begin);
     else if (D == 64) hipLaunchKernelGGL((seam_readout_kernel<64>), grid, dim3(256), 0, st, a, ops, Y, G, j_begin);
     else return hipErrorInvalidValue;
