@@ -72,6 +72,7 @@ class _Lib:
     def __init__(self, path):
         lib = ctypes.CDLL(path)
         lib.orc_threads.restype = ctypes.c_int
+        lib.orc_set_threads.argtypes = [ctypes.c_int]
         lib.orc_recur_batch.argtypes = [ctypes.c_int] * 5 + [
             _d, _l, ctypes.c_long,  # k
             _d, _l, ctypes.c_long,  # v
@@ -104,6 +105,11 @@ def lib(path: str | None = None) -> _Lib:
 
 def threads() -> int:
     return int(lib().lib.orc_threads())
+
+
+def set_threads(n: int) -> None:
+    """Worker threads of the batched calls (OpenMP; 1 runs them serially)."""
+    lib().lib.orc_set_threads(int(n))
 
 
 def _f64(x) -> np.ndarray:

@@ -53,6 +53,16 @@ int orc_threads(void)
 #endif
 }
 
+/* Worker threads of the batched calls (the CPU baseline times 1 and all). */
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* One token: S <- T_t S + u_t, S is dk x dv.  v == NULL means u_t = 0
  * (the transition-only run).  p is scratch of length dv. */
 static void orc_step(int rule, int gate, int dk, int dv,

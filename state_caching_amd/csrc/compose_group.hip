@@ -20,8 +20,7 @@
 // so X never leaves the registers until the group ends.  T of the next position
 // is streamed through the T half's registers and split into the other LDS
 // buffer while the current product runs (one barrier per position); the S
-// half streams S0 the same way into its registers.  (A variant with 64 columns
-// per wave, one wave per SIMD, is kept for comparison: HY_CG_NN = 4.)  The window operators
+// half streams S0 the same way into its registers.  The window operators
 // (W = M diag(b) K, K, U^T, gw; w <= 8) come from the per-(window, head)
 // records that seam_ops_kernel writes.
 #include <type_traits>
@@ -32,8 +31,8 @@
 
 namespace hy {
 
-// NN 16-column tiles of X per wave: 4 (d/32 waves, one per SIMD at d = 128) or
-// 2 (d/16 waves, two per SIMD)
+// NN 16-column tiles of X per wave; the library instantiates NN = 2 (d/16
+// waves, two per SIMD at d = 128)
 template <int D, int NN_>
 struct CgCfg {
     static constexpr int NN = NN_;
@@ -433,26 +432,24 @@ static hipError_t launch_cg(const ComposeArgs &a, const float *ops, int G, int n
     return hipGetLastError();
 }
 
-#ifndef HY_CG_NN
-#define HY_CG_NN 2
-#endif
+constexpr int kCgNN = 2;   // 16-column tiles of X per wave
 
 hipError_t launch_compose_group(const ComposeArgs &a, int D, const float *ops, int G, int ng, float *gT,
                                 float *gS, float *Y, hipStream_t st)
 {
     if (G < 1 || ng < 1 || (int64_t)(ng - 1) * G >= a.n || (int64_t)ng * G < a.n) return hipErrorInvalidValue;
-    if (a.has_seams && a.seam.w > CgCfg<128, HY_CG_NN>::WR) return hipErrorInvalidValue;
+    if (a.has_seams && a.seam.w > CgCfg<128, kCgNN>::WR) return hipErrorInvalidValue;
     // the seam variant needs at least one window record in this launch
     const bool seams = a.has_seams && a.first_pos + a.n >= 2;
     // read-out records are laid out with the read-out rows: the kernel must match
     const bool ro = seams && a.seam.q != nullptr;
     if (ro && !Y) return hipErrorInvalidValue;
-    if (D == 128) return ro ? launch_cg<128, true, HY_CG_NN, true>(a, ops, G, ng, gT, gS, Y, st)
-                    : seams ? launch_cg<128, true, HY_CG_NN, false>(a, ops, G, ng, gT, gS, Y, st)
-                            : launch_cg<128, false, HY_CG_NN, false>(a, ops, G, ng, gT, gS, Y, st);
-    if (D == 64) return ro ? launch_cg<64, true, HY_CG_NN, true>(a, ops, G, ng, gT, gS, Y, st)
-                   : seams ? launch_cg<64, true, HY_CG_NN, false>(a, ops, G, ng, gT, gS, Y, st)
-                           : launch_cg<64, false, HY_CG_NN, false>(a, ops, G, ng, gT, gS, Y, st);
+    if (D == 128) return ro ? launch_cg<128, true, kCgNN, true>(a, ops, G, ng, gT, gS, Y, st)
+                    : seams ? launch_cg<128, true, kCgNN, false>(a, ops, G, ng, gT, gS, Y, st)
+                            : launch_cg<128, false, kCgNN, false>(a, ops, G, ng, gT, gS, Y, st);
+    if (D == 64) return ro ? launch_cg<64, true, kCgNN, true>(a, ops, G, ng, gT, gS, Y, st)
+                   : seams ? launch_cg<64, true, kCgNN, false>(a, ops, G, ng, gT, gS, Y, st)
+                           : launch_cg<64, false, kCgNN, false>(a, ops, G, ng, gT, gS, Y, st);
     return hipErrorInvalidValue;
 }
 

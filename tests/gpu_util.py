@@ -33,6 +33,12 @@ def max_relF(gpu: np.ndarray, ref: np.ndarray, unit_axes: int):
     return max(errs) if errs else 0.0
 
 
+def head_relF(gpu: np.ndarray, ref: np.ndarray):
+    """Largest relative Frobenius error over the heads of states [h, d_k, d_v]
+    (every head is its own unit: a pooled error would hide a bad head)."""
+    return max_relF(gpu, ref, 1)
+
+
 def expand_T(T: np.ndarray, tform: int, d: int) -> np.ndarray:
     name = {0: "scalar", 1: "diag", 2: "dense"}[tform]
     return oracle.expand_dense(T, name, d)

@@ -244,6 +244,20 @@ def pin_gdn_bounds(path):
     assert abs(np.trace(T1) - 7.0) < 1e-13
 
 
+def pin_key_scale(path):
+    """The delta transition depends on beta and k only through beta k k^T
+    (ch.2 sec.3, Table 1): keys scaled by r = 2^6 with beta / r^2 give the same
+    T_C, and the writes beta k v^T, hence S_{C|0}, scale by 1/r.  Powers of two
+    keep the scaled inputs exact."""
+    rng = np.random.default_rng(12)
+    k, v, b, g = rand_unit(rng, "delta", "scalar", 40, 8, 5)
+    T, S0, _ = one_unit(path, "delta", "scalar", k, v, b, g)
+    for r in (2.0 ** 6, 2.0 ** -6):
+        Tr, S0r, _ = one_unit(path, "delta", "scalar", k * r, v, b / (r * r), g)
+        assert np.allclose(Tr, T, rtol=0, atol=1e-13 * np.abs(T).max())
+        assert np.allclose(S0r * r, S0, rtol=0, atol=1e-13 * np.abs(S0).max())
+
+
 def pin_kda_reductions(path):
     """Delta rule with a diagonal gate (KDA row of Table 1), against the other
     families and the norm bound:
@@ -449,4 +463,4 @@ def pin_compose_readouts(path):
 
 ALL = [pin_readout, pin_compose_readouts, pin_worked_example, pin_table2, pin_news_22pct, pin_naive_error_identity,
        pin_brute_force, pin_affine, pin_decay_closed_forms, pin_identity_transition,
-       pin_composition_laws, pin_gdn_bounds, pin_kda_reductions, pin_rope, pin_rope_state, pin_conv, pin_l2norm, pin_compose_equals_full]
+       pin_composition_laws, pin_gdn_bounds, pin_key_scale, pin_kda_reductions, pin_rope, pin_rope_state, pin_conv, pin_l2norm, pin_compose_equals_full]

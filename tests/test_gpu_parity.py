@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import TOL, case, expand_T, max_relF, need_gpu, np64
+from gpu_util import TOL, case, expand_T, head_relF, max_relF, need_gpu, np64
 
 pytestmark = pytest.mark.gpu
 
@@ -54,10 +54,10 @@ def test_gdn_d16_fp32_build_compose():
     Tr, Sr = oracle.build_pairs(wl)
     S_or = oracle.compose(Tr, Sr)
     full = oracle.full_recompute(wl)
-    e = oracle.relF(np64(S), S_or)
+    e = head_relF(np64(S), S_or)
     print(f"  compose relF {e:.3e}; oracle compose vs full {oracle.relF(S_or, full):.1e}")
     assert e <= 1e-5
-    assert oracle.relF(np64(S), full) <= 1e-5
+    assert head_relF(np64(S), full) <= 1e-5
 
 
 def test_retnet_fp32_build_compose_naive():
@@ -69,7 +69,7 @@ def test_retnet_fp32_build_compose_naive():
     torch.cuda.synchronize()
     Tr, Sr = oracle.build_pairs(wl)
     S_or = oracle.compose(Tr, Sr)
-    assert oracle.relF(np64(S), S_or) <= 1e-5
+    assert head_relF(np64(S), S_or) <= 1e-5
     naive = oracle.naive_sum(np64(S0))
     err = oracle.relF(naive, S_or)
     print(f"  naive-sum error vs composed state: {err:.4f}")
@@ -88,7 +88,7 @@ def test_gla_bf16_build():
     S = dw.compose(T, S0)
     torch.cuda.synchronize()
     Tr, Sr = oracle.build_pairs(wl)
-    assert oracle.relF(np64(S), oracle.compose(Tr, Sr)) <= 2e-3
+    assert head_relF(np64(S), oracle.compose(Tr, Sr)) <= 2e-3
 
 
 def test_gla_slow_build():
@@ -106,7 +106,7 @@ def test_gdn_gqa_32k_prompt_sampled():
     heads = [3]
     Tr, Sr = oracle.build_pairs(wl, heads=heads)
     S_or = oracle.compose(Tr, Sr)
-    e = oracle.relF(np64(S)[heads], S_or)
+    e = head_relF(np64(S)[heads], S_or)
     print(f"  compose relF (head 3) {e:.3e}")
     assert e <= 2e-3
 
@@ -157,6 +157,71 @@ def test_deltanet_no_decay():
     _check_build(wl)
 
 
+# ------------------------------------------- builds over more than one launch
+
+def _multi_launch_lens(n, seed):
+    """Ragged segment lengths (30..61 tokens) for builds of n > 128 segments, so
+    that a wrong row offset in a later launch reads another segment's rows."""
+    rng = np.random.default_rng(seed)
+    return [int(x) for x in rng.integers(30, 62, size=n)]
+
+
+@pytest.mark.parametrize("kind,d,dtype,conv", [
+    ("delta", 64, torch.bfloat16, 0), ("delta", 64, torch.bfloat16, 4),
+    ("delta", 128, torch.bfloat16, 4), ("delta", 32, torch.float32, 4),
+    ("retnet", 32, torch.float32, 0), ("gla", 64, torch.bfloat16, 0)],
+    ids=["gdn-bf16-d64", "gdn-bf16-d64-conv", "gdn-bf16-d128-conv", "gdn-f32-d32-conv",
+         "retnet-f32-d32", "gla-bf16-d64"])
+def test_build_multi_launch(kind, d, dtype, conv):
+    """A build of 150 segments runs as two launches (128 + 22).  The pairs of
+    the first and last segments of each launch, and of segments inside both,
+    are compared with the oracle's own pairs: a wrong segment table, output
+    offset or packed conv-workspace offset in the second launch fails here.
+    With conv, inner segments have seam windows, so every body starts after its
+    conv history (rows the second launch must read from the right place)."""
+    need_gpu()
+    n = 150
+    lens = _multi_launch_lens(n, 600 + d + conv)
+    if kind == "delta":
+        wl = synth.gdn(601 + d + conv, lens, 1, 2, d, dtype, alpha_div=16.0, conv_w=conv,
+                       seam_w=8 if conv else 0, name=f"gdn-150seg-d{d}-conv{conv}")
+    elif kind == "retnet":
+        wl = synth.retnet(602 + d, lens, 2, d, dtype=dtype, name="retnet-150seg")
+    else:
+        wl = synth.gla(603 + d, lens, 2, d, dtype=dtype, literal=False, name="gla-150seg")
+    _check_build(wl, segs=[0, 1, 77, 126, 127, 128, 129, 148, 149], label="(two launches)")
+
+
+# ------------------------------------------------------ long segments, key scale
+
+def test_gdn_slow_16k_segment():
+    """One 16384-token segment per head (bf16, d = 128, slow decay as the 32k
+    prompt's slow companion, so the gate-free transition product decays only by
+    the erases): T_C and S0 against the oracle at the bf16 contract bound.  The
+    fp16 operands are rounded in every 64-token chunk, so this is where their
+    rounding has the most chunks to accumulate over."""
+    need_gpu()
+    wl = synth.gdn(610, [16384], 1, 2, 128, torch.bfloat16, alpha_div=4096.0, name="gdn-slow-16k")
+    _check_build(wl, label="(16384-token segment)")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("log2r", [-4, 0, 4])
+def test_delta_key_scale(d, log2r):
+    """Keys of norm r = 2^log2r with write strengths beta / r^2 (bf16 inputs,
+    fp16 matrix-core operands): every transition I - beta' k' k'^T equals the
+    one of the unit-norm keys, and the writes scale by 1/r.  Against the oracle
+    at the contract bound, for keys far from unit norm in both directions."""
+    need_gpu()
+    import dataclasses
+    base = synth.gdn(620 + d, [200, 130, 64], 1, 2, d, torch.bfloat16, alpha_div=32.0)
+    r = 2.0 ** log2r
+    wl = dataclasses.replace(base, k=(base.k.float() * r).to(torch.bfloat16),
+                             beta=(base.beta.float() / (r * r)).to(torch.bfloat16),
+                             name=f"gdn-keys-2^{log2r}")
+    _check_build(wl, label=f"key norm 2^{log2r}")
+
+
 # ---------------------------------------------------------------- compose only
 
 @pytest.mark.parametrize("tform,prec", [("dense", 0), ("dense", 1), ("diag", 0), ("scalar", 0)])
@@ -173,9 +238,9 @@ def test_compose_prebuilt_pairs(tform, prec, d):
     torch.cuda.synchronize()
     Td = expand_T(np64(T), tf, d)
     ref = oracle.compose(Td[order], np64(S0)[order], np64(S_init))
-    e = oracle.relF(np64(S), ref)
+    e = head_relF(np64(S), ref)
     print(f"  relF {e:.3e}")
-    assert e <= (1e-5 if prec == 0 else 2e-5)
+    assert e <= 1e-5   # fp32 pairs: the fp32 contract bound, per head, for both product forms
 
 
 def test_compose_in_place_and_long_chain():
@@ -191,7 +256,7 @@ def test_compose_in_place_and_long_chain():
     sca.compose(T.cuda(), S0.cuda(), order, S_init=S, S_out=S, tform=2, prec=0)
     torch.cuda.synchronize()
     ref = oracle.compose(np64(T)[order], np64(S0)[order], S_ref_init)
-    assert oracle.relF(np64(S), ref) <= 1e-5
+    assert head_relF(np64(S), ref) <= 1e-5
 
 
 def test_compose_empty():
@@ -237,7 +302,7 @@ def test_seam_standalone_outputs(dtype):
                        off_o=u.off_v, ldo=u.ldv)
     Tw, Sw = oracle.build_units(wl.rule, sl.gate_kind, u, d, d, sl.k, sl.v, sl.beta, sl.g)
     tol = 1e-5   # the window runs in fp32 arithmetic for every input dtype
-    errs = (oracle.relF(np64(S), S_ref), oracle.relF(np64(sm.o)[0], o_ref),
+    errs = (head_relF(np64(S), S_ref), oracle.relF(np64(sm.o)[0], o_ref),
             max_relF(np64(sm.T_w)[0], Tw, 1), max_relF(np64(sm.S_w0)[0], Sw, 1))
     print("  seam relF S %.2e o %.2e T_w %.2e S_w0 %.2e" % errs)
     assert max(errs) <= tol
@@ -257,7 +322,7 @@ def test_seam_pipeline_small(dtype):
     Tr, Sr = oracle.build_pairs(wl)
     S_or = oracle.compose(Tr, Sr, wl=wl, seams=True)
     full = oracle.full_recompute(wl)
-    e1, e2 = oracle.relF(np64(S), S_or), oracle.relF(np64(S), full)
+    e1, e2 = head_relF(np64(S), S_or), head_relF(np64(S), full)
     print(f"  compose relF vs oracle {e1:.3e}, vs full recompute {e2:.3e}")
     assert e1 <= TOL[dtype] and e2 <= TOL[dtype]
 
@@ -278,7 +343,7 @@ def test_split_compose_with_seams(d):
     torch.cuda.synchronize()
     S_or = oracle.compose(np64(T), np64(S0), S_init=np64(S_init), wl=wl, seams=True)
     full = oracle.full_recompute(wl, S_init=np64(S_init))
-    e1, e2 = oracle.relF(np64(S), S_or), oracle.relF(np64(S), full)
+    e1, e2 = head_relF(np64(S), S_or), head_relF(np64(S), full)
     print(f"  relF vs oracle compose of the same pairs {e1:.3e}, vs full recompute {e2:.3e}")
     assert e1 <= 2e-5 and e2 <= TOL[torch.bfloat16]
 
@@ -296,7 +361,7 @@ def test_split_compose_seams_across_launches():
     S = dw.compose(T, S0)
     torch.cuda.synchronize()
     S_or = oracle.compose(np64(T), np64(S0), wl=wl, seams=True)
-    e = oracle.relF(np64(S), S_or)
+    e = head_relF(np64(S), S_or)
     print(f"  relF vs oracle compose of the same pairs {e:.3e}")
     assert e <= 2e-5
 
@@ -321,8 +386,8 @@ def test_group_compose_with_seams(d, G):
     torch.cuda.synchronize()
     S_or = oracle.compose(np64(T), np64(S0), S_init=np64(S_init), wl=wl, seams=True)
     full = oracle.full_recompute(wl, S_init=np64(S_init))
-    e1, e2, e3 = (oracle.relF(np64(S), S_or), oracle.relF(np64(S), np64(S_ser)),
-                  oracle.relF(np64(S), full))
+    e1, e2, e3 = (head_relF(np64(S), S_or), head_relF(np64(S), np64(S_ser)),
+                  head_relF(np64(S), full))
     print(f"  relF vs oracle compose {e1:.3e}, vs serial GPU fold {e2:.3e}, vs full recompute {e3:.3e}")
     assert e1 <= 2e-5 and e2 <= 2e-5 and e3 <= TOL[torch.bfloat16]
 
@@ -342,7 +407,7 @@ def test_group_compose_no_seams(d):
         case(f"group compose no seams d={d} G={G}")
         S = sca.compose(T.cuda(), S0.cuda(), order, S_init=S_init.cuda(), group_len=G)
         torch.cuda.synchronize()
-        e = oracle.relF(np64(S), ref)
+        e = head_relF(np64(S), ref)
         print(f"  G={G}: relF vs oracle {e:.3e}")
         assert e <= 2e-5
 
@@ -361,7 +426,7 @@ def test_group_compose_seams_across_launches():
     S = dw.compose(T, S0, group_len=6)
     torch.cuda.synchronize()
     S_or = oracle.compose(np64(T), np64(S0), wl=wl, seams=True)
-    e = oracle.relF(np64(S), S_or)
+    e = head_relF(np64(S), S_or)
     print(f"  relF vs oracle compose of the same pairs {e:.3e}")
     assert e <= 2e-5
 
@@ -384,8 +449,8 @@ def test_gdn_100_segments_seams_slow_group_compose():
     heads = [3, 30]
     Tn, Sn = np64(T)[:, heads], np64(S0)[:, heads]
     S_or = oracle.compose(Tn, Sn, wl=wl, heads=heads, seams=True)
-    e1 = oracle.relF(np64(S)[heads], S_or)
-    e2 = oracle.relF(np64(S), np64(S_ser))
+    e1 = head_relF(np64(S)[heads], S_or)
+    e2 = head_relF(np64(S), np64(S_ser))
     tn = float(np.linalg.norm(np64(T)[-1, heads[0]]))
     print(f"  ||T_C|| (last segment, head {heads[0]}) {tn:.3e}; relF vs oracle compose {e1:.3e}, "
           f"vs serial GPU fold {e2:.3e}")
@@ -409,10 +474,13 @@ def _attach_queries(dw, seed):
 
 
 def _readout_errs(o_gpu, o_ref):
-    """relF over all read-outs, and the largest relF of one window."""
-    whole = oracle.relF(o_gpu, o_ref)
-    per = max(oracle.relF(o_gpu[j], o_ref[j]) for j in range(o_ref.shape[0]))
-    return whole, per
+    """Largest relF of one head's read-outs over all windows, and the largest
+    relF of one (window, head) unit (o is [n_win, w, h, d_v])."""
+    heads = range(o_ref.shape[2])
+    per_head = max(oracle.relF(o_gpu[:, :, h], o_ref[:, :, h]) for h in heads)
+    per = max(oracle.relF(o_gpu[j, :, h], o_ref[j, :, h])
+              for j in range(o_ref.shape[0]) for h in heads)
+    return per_head, per
 
 
 @pytest.mark.parametrize("d,G", [(64, 1), (64, 2), (64, 5), (128, 0), (128, 1), (128, 3), (128, 7),
@@ -435,9 +503,9 @@ def test_group_compose_readouts(d, G):
     S = dw.compose(T, S0, S_init=S_init.cuda(), group_len=G)
     torch.cuda.synchronize()
     S_or, o_or = oracle.compose(np64(T), np64(S0), S_init=np64(S_init), wl=wl, seams=True, q=q)
-    eS = oracle.relF(np64(S), S_or)
+    eS = head_relF(np64(S), S_or)
     eo, eo_win = _readout_errs(np64(dw.seams.o), o_or)
-    print(f"  relF S {eS:.3e}, o {eo:.3e} (worst window {eo_win:.3e})")
+    print(f"  relF S {eS:.3e}, o {eo:.3e} (worst head), {eo_win:.3e} (worst window and head)")
     assert eS <= 2e-5 and eo <= 2e-5 and eo_win <= 1e-4
 
 
@@ -456,9 +524,9 @@ def test_compose_readouts_short_chain(n):
     S = dw.compose(T, S0)
     torch.cuda.synchronize()
     S_or, o_or = oracle.compose(np64(T), np64(S0), wl=wl, seams=True, q=q)
-    eS = oracle.relF(np64(S), S_or)
+    eS = head_relF(np64(S), S_or)
     eo, eo_win = _readout_errs(np64(dw.seams.o), o_or)
-    print(f"  relF S {eS:.3e}, o {eo:.3e} (worst window {eo_win:.3e})")
+    print(f"  relF S {eS:.3e}, o {eo:.3e} (worst head), {eo_win:.3e} (worst window and head)")
     assert eS <= 2e-5 and eo <= 2e-5 and eo_win <= 1e-4
 
 
@@ -477,9 +545,9 @@ def test_compose_readouts_small_heads(d):
     S = dw.compose(T, S0)
     torch.cuda.synchronize()
     S_or, o_or = oracle.compose(np64(T), np64(S0), wl=wl, seams=True, q=q)
-    eS = oracle.relF(np64(S), S_or)
+    eS = head_relF(np64(S), S_or)
     eo, eo_win = _readout_errs(np64(dw.seams.o), o_or)
-    print(f"  relF S {eS:.3e}, o {eo:.3e} (worst window {eo_win:.3e})")
+    print(f"  relF S {eS:.3e}, o {eo:.3e} (worst head), {eo_win:.3e} (worst window and head)")
     assert eS <= 2e-5 and eo <= 2e-5 and eo_win <= 1e-4
 
 
@@ -497,9 +565,9 @@ def test_compose_readouts_fp32_path():
     S = dw.compose(T, S0)
     torch.cuda.synchronize()
     S_or, o_or = oracle.compose(np64(T), np64(S0), wl=wl, seams=True, q=q)
-    eS = oracle.relF(np64(S), S_or)
+    eS = head_relF(np64(S), S_or)
     eo, eo_win = _readout_errs(np64(dw.seams.o), o_or)
-    print(f"  relF S {eS:.3e}, o {eo:.3e} (worst window {eo_win:.3e})")
+    print(f"  relF S {eS:.3e}, o {eo:.3e} (worst head), {eo_win:.3e} (worst window and head)")
     assert eS <= 1e-5 and eo <= 1e-5 and eo_win <= 1e-4
 
 
@@ -522,9 +590,9 @@ def test_compose_readouts_twice():
         S = sca_mod.compose(T, S0, order, tform=dw.tform, prec=dw.prec, seams=dw.seams, workspace=ws)
         torch.cuda.synchronize()
         S_or, o_or = oracle.compose(np64(T), np64(S0), wl=wl, seams=True, q=q)
-        eS = oracle.relF(np64(S), S_or)
+        eS = head_relF(np64(S), S_or)
         eo, eo_win = _readout_errs(np64(dw.seams.o), o_or)
-        print(f"  call {call}: relF S {eS:.3e}, o {eo:.3e} (worst window {eo_win:.3e})")
+        print(f"  call {call}: relF S {eS:.3e}, o {eo:.3e} (worst head), {eo_win:.3e} (worst window and head)")
         assert eS <= 2e-5 and eo <= 2e-5 and eo_win <= 1e-4
 
 
@@ -542,9 +610,9 @@ def test_group_compose_readouts_across_launches():
     S = dw.compose(T, S0, group_len=6)
     torch.cuda.synchronize()
     S_or, o_or = oracle.compose(np64(T), np64(S0), wl=wl, seams=True, q=q)
-    eS = oracle.relF(np64(S), S_or)
+    eS = head_relF(np64(S), S_or)
     eo, eo_win = _readout_errs(np64(dw.seams.o), o_or)
-    print(f"  relF S {eS:.3e}, o {eo:.3e} (worst window {eo_win:.3e})")
+    print(f"  relF S {eS:.3e}, o {eo:.3e} (worst head), {eo_win:.3e} (worst window and head)")
     assert eS <= 2e-5 and eo <= 2e-5 and eo_win <= 1e-4
 
 
@@ -567,7 +635,7 @@ def test_gdn_100_segments_readouts_slow():
     _, o_or = oracle.compose(np64(T)[:, heads], np64(S0)[:, heads], wl=wl, heads=heads,
                              seams=True, q=q)
     eo, eo_win = _readout_errs(np64(dw.seams.o)[:, :, heads], o_or)
-    eS = oracle.relF(np64(S), np64(S_plain))
+    eS = head_relF(np64(S), np64(S_plain))
     print(f"  relF o (heads {heads}) {eo:.3e} (worst window {eo_win:.3e}); S vs compose without "
           f"read-outs {eS:.3e}")
     assert eo <= 2e-5 and eo_win <= 1e-4 and eS <= 1e-6
@@ -590,7 +658,7 @@ def test_kda_build_compose(d, dtype):
     S = dw.compose(T, S0, S_init=S_init.cuda())
     torch.cuda.synchronize()
     full = oracle.full_recompute(wl, S_init=np64(S_init))
-    e = oracle.relF(np64(S), full)
+    e = head_relF(np64(S), full)
     print(f"  compose relF vs full recompute {e:.3e}")
     assert e <= TOL[dtype]
 
@@ -771,6 +839,6 @@ def test_gdn_100_segments_seams_sampled():
     heads = [9]
     Tr, Sr = oracle.build_pairs(wl, heads=heads)
     S_or = oracle.compose(Tr, Sr, wl=wl, heads=heads, seams=True)
-    e = oracle.relF(np64(S)[heads], S_or)
+    e = head_relF(np64(S)[heads], S_or)
     print(f"  compose relF (head 9) {e:.3e}")
     assert e <= 2e-3
