@@ -36,7 +36,8 @@
  *     host arrays read before the call returns.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream) and never synchronise.  The library never allocates or frees
- *     device memory; scratch is the caller's workspace (hypic_workspace_size).
+ *     device memory; scratch is the caller's workspace (hypic_workspace_size),
+ *     except for hypic_compose_noalloc, which uses a static device array.
  *   - Argument errors are returned synchronously as negative hypic_status and
  *     nothing is launched.  Launch failures return HYPIC_E_HIP.  A device fault
  *     surfaces at the caller's next synchronisation.
@@ -67,7 +68,9 @@ typedef enum {
     HYPIC_E_UNSUPPORTED = -2,  /* valid request this build does not implement    */
     HYPIC_E_WORKSPACE = -3,    /* workspace missing or smaller than required     */
     HYPIC_E_HIP = -4,          /* a HIP runtime call or kernel launch failed     */
-    HYPIC_E_DEVICE = -5        /* current device is not a gfx950 GPU             */
+    HYPIC_E_DEVICE = -5,       /* current device is not a gfx950 GPU             */
+    HYPIC_E_TOO_LARGE = -6     /* hypic_compose_noalloc: the request needs more
+                                  scratch than HYPIC_NOALLOC_SCRATCH_BYTES        */
 } hypic_status;
 
 typedef enum { HYPIC_F32 = 0, HYPIC_BF16 = 1 } hypic_dtype;
@@ -282,6 +285,30 @@ typedef struct {
 
 hypic_status hypic_compose(const hypic_compose_desc *d, void *ws, size_t ws_bytes,
                            void *stream);
+
+/*
+ * hypic_compose_noalloc -- hypic_compose for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same descriptor, same kernels and the same result
+ * bit for bit as hypic_compose; the workspace is a static device array inside
+ * the library instead of the caller's buffer, so the call allocates nothing.
+ *
+ *   - The array holds HYPIC_NOALLOC_SCRATCH_BYTES (64 MiB) on every GPU the
+ *     library runs on, from the first kernel launch on that GPU until the
+ *     process ends.  A request whose hypic_workspace_size(d, HYPIC_WS_COMPOSE)
+ *     exceeds it returns HYPIC_E_TOO_LARGE and launches nothing.  (For
+ *     example, 100 positions with w = 8 seams at h_v = 32, d = 128 need 73 MB:
+ *     split such a prompt into two calls, or use hypic_compose.)
+ *   - Every call on one GPU uses that GPU's one array.  Calls that overlap on
+ *     one GPU (two streams, or two host threads without ordering) race on it:
+ *     the caller orders them.  Each call writes every scratch byte it reads
+ *     before reading it, so nothing needs to start at zero and leftovers of an
+ *     earlier call are harmless.
+ * Errors: those of hypic_compose, with HYPIC_E_TOO_LARGE in place of
+ * HYPIC_E_WORKSPACE.
+ */
+#define HYPIC_NOALLOC_SCRATCH_BYTES (64u << 20)
+hypic_status hypic_compose_noalloc(const hypic_compose_desc *d, void *stream);
 
 #define HYPIC_WS_BUILD 0
 #define HYPIC_WS_COMPOSE 1

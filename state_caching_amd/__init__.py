@@ -23,7 +23,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhypic.so")
 
-OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP, E_DEVICE = 0, -1, -2, -3, -4, -5
+OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP, E_DEVICE, E_TOO_LARGE = 0, -1, -2, -3, -4, -5, -6
 F32, BF16 = 0, 1
 RULE_DECAY, RULE_DELTA = 0, 1
 GATE_HEAD_CONST, GATE_SCALAR, GATE_DIAG = 0, 1, 2
@@ -31,6 +31,7 @@ T_SCALAR, T_DIAG, T_DENSE = 0, 1, 2
 PREC_FP32, PREC_SPLIT = 0, 1
 WS_BUILD, WS_COMPOSE = 0, 1
 MAX_SEG_PER_LAUNCH = 128
+NOALLOC_SCRATCH_BYTES = 64 << 20   # static scratch of hypic_compose_noalloc
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -88,6 +89,8 @@ def _lib():
         lib.hypic_segment_build.restype = ctypes.c_int
         lib.hypic_compose.argtypes = [ctypes.POINTER(ComposeDesc), _vp, ctypes.c_size_t, _vp]
         lib.hypic_compose.restype = ctypes.c_int
+        lib.hypic_compose_noalloc.argtypes = [ctypes.POINTER(ComposeDesc), _vp]
+        lib.hypic_compose_noalloc.restype = ctypes.c_int
         lib.hypic_seam_advance.argtypes = [ctypes.POINTER(SeamDesc), _vp, _vp]
         lib.hypic_seam_advance.restype = ctypes.c_int
         lib.hypic_rope_rerotate.argtypes = [ctypes.POINTER(RopeDesc), _vp]
@@ -265,14 +268,9 @@ class Seams:
                         q=_ptr(self.q), o=_ptr(self.o), T_w=_ptr(self.T_w), S_w0=_ptr(self.S_w0))
 
 
-def compose(T_pool: torch.Tensor, S0_pool: torch.Tensor, order: Sequence[int],
-            S_init: Optional[torch.Tensor] = None, tform: int = T_DENSE, prec: int = PREC_SPLIT,
-            seams: Optional[Seams] = None, S_out: Optional[torch.Tensor] = None,
-            workspace: Optional[torch.Tensor] = None, stream=None, group_len: int = 0):
-    """S = fold_i (S <- T[order[i]] S + S0[order[i]]), seams before positions 1..
-
-    group_len: 0 automatic, 1 serial fold, G >= 2 fold groups of G positions
-    in parallel, then the group pairs in order (dense split compose only)."""
+def _compose_desc(T_pool, S0_pool, order, S_init, tform, prec, seams, S_out, group_len):
+    """ComposeDesc for the pools and order (checked against each other), plus the
+    ctypes objects it points to (kept alive by the caller)."""
     n_slots, h_v, d_k, d_v = S0_pool.shape
     if tuple(T_pool.shape) != t_shape(tform, n_slots, h_v, d_k):
         raise ValueError("T_pool shape does not match the transition form")
@@ -283,8 +281,6 @@ def compose(T_pool: torch.Tensor, S0_pool: torch.Tensor, order: Sequence[int],
             raise ValueError("states must be [h_v, d_k, d_v]")
     if seams is not None and seams.xk.shape[0] != max(0, len(order) - 1):
         raise ValueError("compose needs one seam window per inner segment")
-    if S_out is None:
-        S_out = torch.empty((h_v, d_k, d_v), dtype=torch.float32, device=S0_pool.device)
     n = len(order)
     ordr = (ctypes.c_int32 * max(1, n))(*[int(x) for x in order])
     sd = seams.desc() if seams is not None else None
@@ -292,6 +288,32 @@ def compose(T_pool: torch.Tensor, S0_pool: torch.Tensor, order: Sequence[int],
                     order=ctypes.cast(ordr, _pi32), T_pool=_ptr(T_pool), S0_pool=_ptr(S0_pool),
                     S_init=_ptr(S_init), S_out=_ptr(S_out),
                     seams=ctypes.pointer(sd) if sd is not None else None, group_len=int(group_len))
+    return d, (ordr, sd)
+
+
+def compose_noalloc(T_pool: torch.Tensor, S0_pool: torch.Tensor, order: Sequence[int],
+                    S_out: torch.Tensor, S_init: Optional[torch.Tensor] = None, tform: int = T_DENSE,
+                    prec: int = PREC_SPLIT, seams: Optional[Seams] = None, stream=None,
+                    group_len: int = 0):
+    """compose() through hypic_compose_noalloc: the library's static scratch
+    instead of a workspace, nothing allocated (S_out is the caller's)."""
+    d, keep = _compose_desc(T_pool, S0_pool, order, S_init, tform, prec, seams, S_out, group_len)
+    _check(_lib().hypic_compose_noalloc(ctypes.byref(d), _stream(stream)), "hypic_compose_noalloc")
+    return S_out
+
+
+def compose(T_pool: torch.Tensor, S0_pool: torch.Tensor, order: Sequence[int],
+            S_init: Optional[torch.Tensor] = None, tform: int = T_DENSE, prec: int = PREC_SPLIT,
+            seams: Optional[Seams] = None, S_out: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None, stream=None, group_len: int = 0):
+    """S = fold_i (S <- T[order[i]] S + S0[order[i]]), seams before positions 1..
+
+    group_len: 0 automatic, 1 serial fold, G >= 2 fold groups of G positions
+    in parallel, then the group pairs in order (dense split compose only)."""
+    n_slots, h_v, d_k, d_v = S0_pool.shape
+    if S_out is None:
+        S_out = torch.empty((h_v, d_k, d_v), dtype=torch.float32, device=S0_pool.device)
+    d, keep = _compose_desc(T_pool, S0_pool, order, S_init, tform, prec, seams, S_out, group_len)
     L = _lib()
     need = L.hypic_workspace_size(ctypes.byref(d), WS_COMPOSE)
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):

@@ -36,6 +36,36 @@ hypic_status device_check()
 
 hypic_status from_hip(hipError_t e) { return e == hipSuccess ? HYPIC_OK : HYPIC_E_HIP; }
 
+}  // namespace
+
+// Workspace of hypic_compose_noalloc: a file-scope device array, one copy per
+// GPU, allocated when the code object is loaded and held until the process
+// ends.  Host code never uses its name as an address: each device's copy is
+// looked up once with hipGetSymbolAddress and the looked-up pointer is what the
+// kernels receive.
+__device__ __align__(256) unsigned char scratch[HYPIC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of this device's copy of `scratch` (looked up on the first call
+// on each device, with that device current).
+hypic_status scratch_address(void **out)
+{
+    static std::mutex mu;
+    static void *addr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return HYPIC_E_HIP;
+    if (dev < 0 || dev >= 64) return HYPIC_E_DEVICE;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return HYPIC_E_HIP;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return HYPIC_OK;
+}
+
 bool build_needs_prep(const hypic_build_desc *d) { return d->conv_w > 0 || d->k_l2norm; }
 
 int64_t build_rows(const hypic_build_desc *d)
@@ -200,6 +230,7 @@ const char *hypic_status_string(hypic_status s)
     case HYPIC_E_WORKSPACE: return "workspace missing or too small";
     case HYPIC_E_HIP: return "HIP runtime error";
     case HYPIC_E_DEVICE: return "device is not gfx950";
+    case HYPIC_E_TOO_LARGE: return "request needs more scratch than the allocation-free call holds";
     default: return "unknown status";
     }
 }
@@ -324,7 +355,13 @@ hypic_status hypic_segment_build(const hypic_build_desc *d, void *ws, size_t ws_
     return HYPIC_OK;
 }
 
-hypic_status hypic_compose(const hypic_compose_desc *d, void *ws, size_t ws_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Argument checks of a compose (nothing launched); in_kind receives the
+// element kind of the seam windows' inputs.
+hypic_status validate_compose(const hypic_compose_desc *d, int *in_kind_out)
 {
     if (!d) return HYPIC_E_INVALID;
     if (d->tform < HYPIC_T_SCALAR || d->tform > HYPIC_T_DENSE) return HYPIC_E_INVALID;
@@ -350,11 +387,16 @@ hypic_status hypic_compose(const hypic_compose_desc *d, void *ws, size_t ws_byte
         if (compose_readouts(d) && compose_uses_split(d) && d->seams->w > 8) return HYPIC_E_UNSUPPORTED;
         in_kind = d->seams->in_dtype == HYPIC_BF16 ? IN_BF16 : IN_F32;
     }
-    const size_t need = compose_ws_bytes(d);
-    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return HYPIC_E_WORKSPACE;
-    hypic_status st = device_check();
-    if (st != HYPIC_OK) return st;
-    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    *in_kind_out = in_kind;
+    return HYPIC_OK;
+}
+
+// The launches of a validated compose on a workspace of at least
+// compose_ws_bytes(d) bytes.
+hypic_status run_compose(const hypic_compose_desc *d, int in_kind, void *ws, hipStream_t hs)
+{
+    const int D = d->d_k;
+    hypic_status st = HYPIC_OK;
     ComposeArgs a;
     memset(&a, 0, sizeof(a));
     a.T_pool = d->T_pool; a.S0_pool = d->S0_pool;
@@ -412,6 +454,33 @@ hypic_status hypic_compose(const hypic_compose_desc *d, void *ws, size_t ws_byte
         if (st != HYPIC_OK) return st;
     }
     return HYPIC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hypic_status hypic_compose(const hypic_compose_desc *d, void *ws, size_t ws_bytes, void *stream)
+{
+    int in_kind = IN_F32;
+    hypic_status st = validate_compose(d, &in_kind);
+    if (st != HYPIC_OK) return st;
+    const size_t need = compose_ws_bytes(d);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return HYPIC_E_WORKSPACE;
+    if ((st = device_check()) != HYPIC_OK) return st;
+    return run_compose(d, in_kind, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
+hypic_status hypic_compose_noalloc(const hypic_compose_desc *d, void *stream)
+{
+    int in_kind = IN_F32;
+    hypic_status st = validate_compose(d, &in_kind);
+    if (st != HYPIC_OK) return st;
+    if (compose_ws_bytes(d) > (size_t)HYPIC_NOALLOC_SCRATCH_BYTES) return HYPIC_E_TOO_LARGE;
+    if ((st = device_check()) != HYPIC_OK) return st;
+    void *ws = nullptr;
+    if ((st = scratch_address(&ws)) != HYPIC_OK) return st;
+    return run_compose(d, in_kind, ws, reinterpret_cast<hipStream_t>(stream));
 }
 
 hypic_status hypic_rope_rerotate(const hypic_rope_desc *d, void *stream)

@@ -241,3 +241,26 @@ def test_rope_state_validation(sca):
     assert L.hypic_rope_rerotate_state(2, 64, 64, 64, 3, 10000.0, 5, p, p, None) == -1   # pairing
     assert L.hypic_rope_rerotate_state(2, 64, 64, 64, 0, -1.0, 5, p, p, None) == -1     # base
     assert L.hypic_rope_rerotate_state(2, 64, 64, 64, 0, 10000.0, 5, None, p, None) == -1
+
+
+def test_compose_noalloc_validation(sca):
+    """The allocation-free compose checks its arguments like hypic_compose and
+    refuses, before touching a device, a request whose workspace exceeds its
+    static scratch: the 100-segment prompt with w = 8 seams at h_v = 32,
+    d = 128 needs 73 MB of the 64 MiB, so it returns HYPIC_E_TOO_LARGE; the
+    same request at h_v = 16 fits and gets past that check."""
+    L = sca.library()
+    assert L.hypic_compose_noalloc(None, None) == -1
+    d = _compose_desc(sca, tform=5)
+    assert L.hypic_compose_noalloc(ctypes.byref(d), None) == -1
+    n, d_ = 100, 128
+    for h, fits in ((32, False), (16, True)):
+        sd = sca.SeamDesc(rule=sca.RULE_DELTA, in_dtype=sca.BF16, w=8, conv_w=4, k_l2norm=1, h_k=h,
+                          h_v=h, d_k=d_, d_v=d_, n_win=n - 1, xk=16, xv=16, tail_k=16, tail_v=16,
+                          conv_wk=16, conv_wv=16, beta=16, alpha=16)
+        dsc = _compose_desc(sca, order=list(range(n)), h_v=h, n_slots=n, seams=ctypes.pointer(sd))
+        need = L.hypic_workspace_size(ctypes.byref(dsc), sca.WS_COMPOSE)
+        assert (need <= sca.NOALLOC_SCRATCH_BYTES) == fits
+        if not fits:
+            assert L.hypic_compose_noalloc(ctypes.byref(dsc), None) == -6
+            assert b"scratch" in L.hypic_status_string(-6)
