@@ -50,7 +50,16 @@
  *     Precision: fp32 inputs are computed with fp32 matrix products (relative
  *     Frobenius error ~1e-6); bf16 inputs use fp16 matrix-core operands with
  *     fp32 accumulation and power-of-two block scaling (~3e-4 on S, <=1.5e-3 on
- *     dense T_C for 4096-token segments).
+ *     dense T_C for 4096-token segments).  Gated-delta segments longer than
+ *     4096 tokens are built with fp32 products whatever the input dtype (the
+ *     fp16 rounding of every 64-token chunk would add up past 2e-3 on T_C).
+ *   - Delta rule keys enter the matrix products as given: they are meant to be
+ *     L2-normalised (k_l2norm = 1, or by the caller), with b_t |k_t|^2 <= 2 so
+ *     that no transition expands.  With bf16 inputs the keys, b and the solved
+ *     pseudo-keys are fp16 operands: key entries must stay below 2^15 in
+ *     magnitude (larger ones overflow to non-finite pairs), and nonzero entries
+ *     below 2^-14 lose relative precision.  Keys of norm 2^-4 .. 2^4 with
+ *     b scaled by the inverse square are tested at the bf16 bound.
  */
 #ifndef HYPIC_H
 #define HYPIC_H

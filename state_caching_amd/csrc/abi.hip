@@ -68,6 +68,13 @@ hypic_status scratch_address(void **out)
 
 bool build_needs_prep(const hypic_build_desc *d) { return d->conv_w > 0 || d->k_l2norm; }
 
+// Longest gated-delta segment (tokens) built on fp16 matrix-core operands.  Their
+// rounding enters once per 64-token chunk, so the error of the transition
+// product grows with the chunk count: about 1.4e-3 relative at 4096 tokens and
+// 3.3e-3 at 16384 on slowly decaying gates, against the 2e-3 bound for bf16
+// inputs.  Longer segments are built with fp32 products (about 1e-6).
+constexpr int64_t kF16MaxLen = 4096;
+
 int64_t build_rows(const hypic_build_desc *d)
 {
     int64_t n = 0;
@@ -265,9 +272,11 @@ hypic_status hypic_segment_build(const hypic_build_desc *d, void *ws, size_t ws_
     const int D = d->d_k;
     const int in_kind = d->in_dtype == HYPIC_BF16 ? IN_BF16 : IN_F32;
     const bool prep = build_needs_prep(d);
-    // the fp16-operand build (bf16 inputs, d >= 64) takes fp16 keys from the conv
     const bool kda = d->rule == HYPIC_RULE_DELTA && d->gate_kind == HYPIC_GATE_DIAG;
-    const bool khalf = prep && d->in_dtype == HYPIC_BF16 && D >= 64 && d->rule == HYPIC_RULE_DELTA && !kda;
+    // gated-delta segments with bf16 inputs and d >= 64 take the fp16-operand
+    // build, up to kF16MaxLen tokens; longer ones the fp32-operand build
+    const bool f16_family = d->rule == HYPIC_RULE_DELTA && !kda && d->in_dtype == HYPIC_BF16 && D >= 64;
+    auto long_seg = [&](int s) { return f16_family && d->seg_len[s] > kF16MaxLen; };
     float *wk = nullptr, *wvv = nullptr, *wvs = nullptr;
     if (prep) {
         const int64_t rows = build_rows(d);
@@ -279,8 +288,14 @@ hypic_status hypic_segment_build(const hypic_build_desc *d, void *ws, size_t ws_
         wvs = wvv + ((size_t)rows * d->h_v * D / 2);
     }
     int64_t packed = 0;
-    for (int s0 = 0; s0 < d->n_seg; s0 += kMaxSeg) {
-        const int nb = std::min(kMaxSeg, d->n_seg - s0);
+    // launches over runs of consecutive segments of one operand class, at most
+    // kMaxSeg each (outputs of a launch stay contiguous)
+    for (int s0 = 0, nb = 0; s0 < d->n_seg; s0 += nb) {
+        const bool lng = long_seg(s0);
+        nb = 1;
+        while (nb < kMaxSeg && s0 + nb < d->n_seg && long_seg(s0 + nb) == lng) ++nb;
+        // the fp16-operand build takes fp16 keys and scaled fp16 values from the conv
+        const bool khalf = prep && f16_family && !lng;
         const size_t tsz = d->rule == HYPIC_RULE_DELTA ? (size_t)D * D
                          : (d->gate_kind == HYPIC_GATE_DIAG ? (size_t)D : 1);
         float *T_out = d->T_out + (size_t)s0 * d->h_v * tsz;
@@ -335,7 +350,7 @@ hypic_status hypic_segment_build(const hypic_build_desc *d, void *ws, size_t ws_
             }
             const int kv_kind = khalf ? IN_F16K : (prep ? IN_F32 : in_kind);
             st = kda ? from_hip(launch_build_kda(a, D, kv_kind, in_kind, nb * d->h_v, hs))
-                     : from_hip(launch_build_delta(a, D, kv_kind, in_kind, d->in_dtype == HYPIC_BF16,
+                     : from_hip(launch_build_delta(a, D, kv_kind, in_kind, d->in_dtype == HYPIC_BF16 && !lng,
                                                    nb * d->h_v, hs));
         } else {
             DecayArgs a;

@@ -72,35 +72,30 @@ build_decay_kernel(const DecayArgs a)
         ldg = a.h_v;
     }
 
-    // prefetch registers: keys and log2-gates of (d, part), values 8 columns x 2 rows
-    float kq[TP], lq[TP];
+    // prefetch registers (raw input words): keys and gates of (d, part), values
+    // 8 columns x VPASS rows.  Rows are loaded clamped into the segment and masked
+    // when used, so the loads carry no branches and the compiler waits for them
+    // only where the values are consumed, a chunk later.
+    TIN kr[TP], gr[TP];
     constexpr int CPR = NC / 8;
     const int vrow = tid / CPR, vcol = 8 * (tid % CPR);
     constexpr int VROWS = C::NT / CPR;          // rows per pass
     constexpr int VPASS = 64 / VROWS;
-    float vr[VPASS][8];
+    typename Raw8<TIN>::type vraw[VPASS];
+    const unsigned ldk32 = (unsigned)ldk, ldv32 = (unsigned)ldv, ldg32 = (unsigned)ldg;
     auto fetch = [&](int c) {
-        const int t0 = 64 * c + part * TP;
+        const int last = len - 1 - 64 * c;      // >= 0 for every chunk of the segment
+        const TIN *kc = kp + (int64_t)(64 * c) * ldk + d;
 #pragma unroll
-        for (int j = 0; j < TP; ++j) {
-            const int t = t0 + j;
-            if (t < len) {
-                kq[j] = ld1(kp + (int64_t)t * ldk + d);
-                lq[j] = gp ? log2f(ld1(gp + (int64_t)t * ldg)) : l2c;
-            } else {
-                kq[j] = 0.f;
-                lq[j] = 0.f;
-            }
+        for (int j = 0; j < TP; ++j) kr[j] = kc[__umul24(min(part * TP + j, last), ldk32)];
+        if (gp) {
+            const TIN *gc = gp + (int64_t)(64 * c) * ldg;
+#pragma unroll
+            for (int j = 0; j < TP; ++j) gr[j] = gc[__umul24(min(part * TP + j, last), ldg32)];
         }
+        const TIN *vc = vp + (int64_t)(64 * c) * ldv + vcol;
 #pragma unroll
-        for (int p = 0; p < VPASS; ++p) {
-            const int t = 64 * c + vrow + VROWS * p;
-            if (t < len) ld8(vp + (int64_t)t * ldv + vcol, vr[p]);
-            else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vr[p][e] = 0.f;
-            }
-        }
+        for (int p = 0; p < VPASS; ++p) ld_raw8(vc + __umul24(min(vrow + VROWS * p, last), ldv32), vraw[p]);
     };
 
     f4 S[MT];
@@ -112,19 +107,26 @@ build_decay_kernel(const DecayArgs a)
 
     for (int c = 0; c < nch; ++c) {
         lds_barrier();
-        // local suffix sums of this part
+        // log2-gates of this part (rows past the segment end: gate 1, key 0), and
+        // their local suffix sums
         float run = 0.f;
         float sfx[TP];
 #pragma unroll
         for (int j = TP - 1; j >= 0; --j) {
+            const bool in = 64 * c + part * TP + j < len;
+            const float lq = in ? (gp ? log2f(to_f32(gr[j])) : l2c) : 0.f;
             sfx[j] = run;
-            run += lq[j];
+            run += lq;
         }
         sm.part_tot[part][d] = run;
 #pragma unroll
-        for (int p = 0; p < VPASS; ++p)
+        for (int p = 0; p < VPASS; ++p) {
+            mask_raw8(vraw[p], 64 * c + vrow + VROWS * p < len);
+            float vr[8];
+            widen8(vraw[p], vr);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sm.VT[vcol + e][vrow + VROWS * p] = (AT)vr[p][e];
+            for (int e = 0; e < 8; ++e) sm.VT[vcol + e][vrow + VROWS * p] = (AT)vr[e];
+        }
         lds_barrier();
         float off = 0.f, tot = 0.f;
 #pragma unroll
@@ -142,7 +144,8 @@ build_decay_kernel(const DecayArgs a)
         }
 #pragma unroll
         for (int j = 0; j < TP; ++j) {
-            const float kh_ = kq[j] * exp2f(sfx[j] + off);
+            const bool in = 64 * c + part * TP + j < len;
+            const float kh_ = (in ? to_f32(kr[j]) : 0.f) * exp2f(sfx[j] + off);
             const int t = part * TP + j;
             if constexpr (SPLIT) {
                 __bf16 hi, lo;

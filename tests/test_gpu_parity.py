@@ -198,11 +198,31 @@ def test_gdn_slow_16k_segment():
     """One 16384-token segment per head (bf16, d = 128, slow decay as the 32k
     prompt's slow companion, so the gate-free transition product decays only by
     the erases): T_C and S0 against the oracle at the bf16 contract bound.  The
-    fp16 operands are rounded in every 64-token chunk, so this is where their
-    rounding has the most chunks to accumulate over."""
+    fp16 operands' rounding would add up over 256 chunks past the bound (3.3e-3
+    on T_C); segments longer than 4096 tokens take the fp32-operand build."""
     need_gpu()
     wl = synth.gdn(610, [16384], 1, 2, 128, torch.bfloat16, alpha_div=4096.0, name="gdn-slow-16k")
     _check_build(wl, label="(16384-token segment)")
+
+
+@pytest.mark.parametrize("conv", [0, 4])
+def test_gdn_mixed_segment_lengths(conv):
+    """A build whose segments alternate between the fp16-operand class (up to
+    4096 tokens) and the fp32-operand class (longer), with and without conv:
+    each run of one class is its own launch, with its own conv workspace
+    layout.  Every pair against the oracle; the long ones at the fp32 path's
+    precision."""
+    need_gpu()
+    lens = [4096, 4105, 300, 5008, 64, 4108]   # bodies (after 8-token windows) 4096, 4097, ...: both classes
+    wl = synth.gdn(611 + conv, lens, 1, 2, 128, torch.bfloat16, alpha_div=512.0, conv_w=conv,
+                   seam_w=8 if conv else 0, name=f"gdn-mixed-lengths-conv{conv}")
+    dw, T, S0 = _check_build(wl, label="(mixed operand classes)")
+    long_segs = [j for j, (s, e) in enumerate(wl.body_ranges()) if e - s > 4096]
+    Tr, Sr = oracle.build_pairs(wl, segs=long_segs)
+    eT = max_relF(expand_T(np64(T), dw.tform, 128)[long_segs], Tr, 2)
+    eS = max_relF(np64(S0)[long_segs], Sr, 2)
+    print(f"  segments over 4096 tokens: max relF T {eT:.3e}  S {eS:.3e}")
+    assert eT <= 2e-5 and eS <= 2e-5
 
 
 @pytest.mark.parametrize("d", [64, 128])
