@@ -385,6 +385,52 @@ def compose(T, S0, S_init=None, wl=None, heads=None, seams=False, path=None, q=N
     return S, o
 
 
+def _with_window_rows(wl, win):
+    """A float64 copy of workload wl whose seam-window rows carry the given
+    inputs: win["k"] [n_win, w, h_k, d_k] and win["v"] [n_win, w, h_v, d_v]
+    (raw rows when the workload has a conv), win["beta"], win["alpha"]
+    [n_win, w, h_v].  Every other row is the workload's own."""
+    import dataclasses
+    import torch
+    k = torch.as_tensor(_f64(wl.k)).clone()
+    v = torch.as_tensor(_f64(wl.v)).clone()
+    beta = torch.as_tensor(_f64(wl.beta)).clone()
+    gate = torch.as_tensor(_f64(wl.gate)).clone()
+    for j, (s, e) in enumerate(wl.window_ranges()):
+        k[s:e] = torch.as_tensor(_f64(win["k"][j]))
+        v[s:e] = torch.as_tensor(_f64(win["v"][j]))
+        beta[s:e] = torch.as_tensor(_f64(win["beta"][j]))
+        gate[s:e] = torch.as_tensor(_f64(win["alpha"][j]))
+    return dataclasses.replace(wl, k=k, v=v, beta=beta, gate=gate)
+
+
+def compose_layers(wls, T, S0, q0, project, path=None):
+    """A stack of gated-delta layers over one prompt (ch.2 sec.5, Figs. 7-8):
+    the seam-window tokens are recomputed layer by layer, and what a window
+    token reads out at layer l is what its inputs at layer l+1 are made from.
+
+    wls[l]: layer l's workload (its cached bodies; layer 0's window rows too);
+    T[l], S0[l]: layer l's cached pairs (dense, all heads); q0: layer 0's
+    window queries [n_win, w, h_k, d_k].  project(l, o) maps layer l's
+    read-outs o [n_win, w, h_v, d_v] to layer l+1's window inputs: a dict with
+    "k", "v", "beta", "alpha" (see _with_window_rows) and "q".  Each layer is
+    compose(..., seams=True, q=...) token by token over its windows.
+    Returns [(S_l, o_l)] per layer.
+    """
+    out = []
+    win = None
+    for l, wl in enumerate(wls):
+        q = q0
+        if win is not None:
+            wl = _with_window_rows(wl, win)
+            q = win["q"]
+        S, o = compose(T[l], S0[l], wl=wl, seams=True, path=path, q=q)
+        out.append((S, o))
+        if l + 1 < len(wls):
+            win = project(l, o)
+    return out
+
+
 def full_recompute(wl, S_init=None, heads=None, path=None):
     """Recur over the whole concatenation from S_init (zero by default)."""
     heads = list(range(wl.h_v)) if heads is None else list(heads)

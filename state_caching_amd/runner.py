@@ -76,3 +76,46 @@ class DeviceWorkload:
                        prec=self.prec if prec is None else prec,
                        seams=self.seams if seams else None, S_out=S_out, stream=stream,
                        group_len=group_len)
+
+
+def compose_layers(layers, project, S_init=None, stream=None):
+    """Compose a stack of layers bottom to top, each with its seam windows
+    recomputed and read out (HYPIC reading notes ch.2 sec.5, Figs. 7-8: a
+    recomputed window token's output at one layer is what its inputs at the
+    next layer are made from, so the layers run in order).
+
+    layers[l] = (T, S0, order, seams, tform, prec): layer l's cached pairs and
+    Seams, whose tails and conv weights are that layer's own; layer 0's
+    window rows and queries are in its Seams.  project(l, o) receives layer
+    l's read-outs o [n_win, w, h_v, d_v] (fp32, device) and returns layer
+    l+1's window inputs as a dict of device tensors shaped like the Seams
+    fields "xk", "xv", "beta", "alpha", "q" (the caller's model: projections,
+    norms, activations).  Host-side sequencing only: every layer's compose
+    runs in the library.  S_init: None (zero prefix state at every layer) or
+    one state [h_v, d_k, d_v] per layer.  Returns [(S_l, o_l)] per layer.
+    """
+    if S_init is not None and len(S_init) != len(layers):
+        raise ValueError("S_init needs one state per layer")
+    out = []
+    nxt = None
+    for l, (T, S0, order, seams, tform, prec) in enumerate(layers):
+        if seams is None:
+            raise ValueError("every layer needs its seam windows")
+        if nxt is not None:
+            for name in ("xk", "xv", "beta", "alpha", "q"):
+                ref = getattr(seams, name) if name != "q" else seams.xk
+                t = nxt[name]
+                if t.device != S0.device:
+                    raise ValueError(f"layer {l}: window input {name} is on another device")
+                setattr(seams, name, t.to(ref.dtype).contiguous())
+        elif seams.q is None:
+            raise ValueError("layer 0 needs its window queries")
+        n_win, w = seams.xk.shape[0], seams.xk.shape[1]
+        h_v, d_v = S0.shape[1], S0.shape[3]
+        seams.o = torch.empty((n_win, w, h_v, d_v), dtype=torch.float32, device=S0.device)
+        S = compose(T, S0, list(order), S_init=None if S_init is None else S_init[l], tform=tform,
+                    prec=prec, seams=seams, stream=stream)
+        out.append((S, seams.o))
+        if l + 1 < len(layers):
+            nxt = project(l, seams.o)
+    return out

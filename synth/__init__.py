@@ -273,6 +273,29 @@ ROPE_32K = dict(seed=6, n_tokens=8 * 4096, h=16, d=128,
 and the shifts that move segment i to start 4096 i + 517 tokens later."""
 
 
+def layer_projection(seed, h_k, h_v, d):
+    """Weights of a synthetic layer-to-layer map for seam windows: a window
+    token's read-out of one layer, flattened to x [h_v * d], gives the next
+    layer's raw key and value rows x Wk [h_k * d], x Wv [h_v * d], its final
+    query x Wq [h_k * d] (L2-normalised per head by the user of these
+    weights), and the logits of its write strength x wb [h_v] and gate
+    x wa [h_v].  Entries N(0, 1 / (h_v d)); float32 values held as float64."""
+    rng = np.random.default_rng(seed)
+    n = h_v * d
+    sd = 1.0 / np.sqrt(n)
+    out = {}
+    for name, m in (("Wk", h_k * d), ("Wv", h_v * d), ("Wq", h_k * d), ("wb", h_v), ("wa", h_v)):
+        out[name] = _round(rng.standard_normal((n, m)) * sd, torch.float32).double().numpy()
+    return out
+
+
+def window_queries(seed, n_win, w, h_k, d):
+    """Final queries of seam-window tokens [n_win, w, h_k, d]: N(0,1) rows,
+    L2-normalised, float32."""
+    rng = np.random.default_rng(seed)
+    return _round(_unit_rows(rng.standard_normal((n_win, w, h_k, d))), torch.float32)
+
+
 def random_state(seed, h, d_k, d_v):
     rng = np.random.default_rng(seed)
     return _round(rng.standard_normal((h, d_k, d_v)), torch.float32)

@@ -461,6 +461,45 @@ def pin_compose_readouts(path):
         assert oracle.relF(S, S_full) < 1e-12
 
 
-ALL = [pin_readout, pin_compose_readouts, pin_worked_example, pin_table2, pin_news_22pct, pin_naive_error_identity,
+def pin_compose_layers(path):
+    """A stack of three layers whose seam-window inputs are projections of the
+    layer below's window read-outs (ch.2 sec.5, Figs. 7-8) equals, layer by
+    layer, the full token recurrence over the whole prompt with those window
+    rows substituted: read-outs at the window tokens and the end state, GQA
+    heads included (no conv, so the cached bodies never read the windows)."""
+    import synth
+    import torch
+    from stack_util import project_np
+    h_k, h_v, d, w = 1, 2, 8, 4
+    lens = [20, 17, 23, 15]
+    wls = [synth.gdn(30 + l, lens, h_k, h_v, d, torch.float32, alpha_div=8.0, seam_w=w)
+           for l in range(3)]
+    P = [synth.layer_projection(40 + l, h_k, h_v, d) for l in range(2)]
+    proj = project_np(P, h_k, h_v, d, norm_k=True)
+    wins = wls[0].window_ranges()
+    q0 = synth.window_queries(50, len(wins), w, h_k, d).double().numpy()
+    pairs = [oracle.build_pairs(wl, path=path) for wl in wls]
+    got = oracle.compose_layers(wls, [p[0] for p in pairs], [p[1] for p in pairs], q0, proj,
+                                path=path)
+    win, q = None, q0
+    for l, wl in enumerate(wls):
+        wl_l = wl if win is None else oracle._with_window_rows(wl, win)
+        q_all = np.zeros((wl.n_tokens, h_k, d))
+        for j, (s, e) in enumerate(wins):
+            q_all[s:e] = q[j]
+        S_full, o_full = oracle.recur_range(wl_l, 0, wl.n_tokens, np.zeros((h_v, d, d)), path=path,
+                                            q=q_all)
+        o_win = np.stack([o_full[s:e] for s, e in wins])
+        S, o = got[l]
+        assert oracle.relF(S, S_full) < 1e-12, l
+        assert oracle.relF(o, o_win) < 1e-12, l
+        if l + 1 < len(wls):
+            win = proj(l, o_win)
+            q = win["q"]
+    # the layers differ: the upper layers' windows do not see layer 0's rows
+    assert oracle.relF(got[1][1], got[0][1]) > 0.1
+
+
+ALL = [pin_readout, pin_compose_readouts, pin_compose_layers, pin_worked_example, pin_table2, pin_news_22pct, pin_naive_error_identity,
        pin_brute_force, pin_affine, pin_decay_closed_forms, pin_identity_transition,
        pin_composition_laws, pin_gdn_bounds, pin_key_scale, pin_kda_reductions, pin_rope, pin_rope_state, pin_conv, pin_l2norm, pin_compose_equals_full]

@@ -862,3 +862,40 @@ def test_gdn_100_segments_seams_sampled():
     e = head_relF(np64(S)[heads], S_or)
     print(f"  compose relF (head 9) {e:.3e}")
     assert e <= 2e-3
+
+
+@pytest.mark.parametrize("conv_w", [0, 4])
+def test_multilayer_seam_stack(conv_w):
+    """Three layers composed bottom to top (ch.2 sec.5, Figs. 7-8): each layer's
+    seam-window inputs (raw keys and values, write strengths, gates, queries)
+    are seeded projections of the layer below's window read-outs.  The device
+    runs one compose with read-outs per layer on its own pairs; the oracle runs
+    every layer token by token over its windows from its own pairs and its own
+    read-outs.  Every layer's read-outs and end state per head against it."""
+    need_gpu()
+    sca, DW = _lib()
+    from state_caching_amd.runner import compose_layers
+    from stack_util import project_np, project_torch
+    h_k, h_v, d, w, n_layers = 2, 4, 32, 8, 3
+    lens = [48, 40, 56, 36, 44]
+    wls = [synth.gdn(700 + 10 * conv_w + l, lens, h_k, h_v, d, torch.float32, alpha_div=8.0,
+                     conv_w=conv_w, seam_w=w) for l in range(n_layers)]
+    P = [synth.layer_projection(720 + l, h_k, h_v, d) for l in range(n_layers - 1)]
+    q0 = synth.window_queries(730 + conv_w, len(lens) - 1, w, h_k, d)
+    layers = []
+    for wl in wls:
+        dw = DW(wl)
+        T, S0 = dw.build()
+        layers.append((T, S0, range(wl.n_seg), dw.seams, dw.tform, dw.prec))
+    layers[0][3].q = q0.cuda()
+    case(f"multi-layer seam stack: {n_layers} layers, conv_w={conv_w}, fp32, d={d}")
+    got = compose_layers(layers, project_torch(P, h_k, h_v, d, norm_k=conv_w == 0, device="cuda"))
+    torch.cuda.synchronize()
+    pairs = [oracle.build_pairs(wl) for wl in wls]
+    ref = oracle.compose_layers(wls, [p[0] for p in pairs], [p[1] for p in pairs],
+                                np64(q0), project_np(P, h_k, h_v, d, norm_k=conv_w == 0))
+    for l in range(n_layers):
+        eS = head_relF(np64(got[l][0]), ref[l][0])
+        eo, eo_win = _readout_errs(np64(got[l][1]), ref[l][1])
+        print(f"  layer {l}: relF S {eS:.3e}, o {eo:.3e} (worst head), {eo_win:.3e} (worst window and head)")
+        assert eS <= 1e-5 and eo <= 1e-5 and eo_win <= 1e-4, l
