@@ -150,14 +150,21 @@ hypic_status hypic_segment_build(const hypic_build_desc *d, void *ws, size_t ws_
 /*
  * Seam windows (ch.2 secs.5-6).  Window i holds the first w tokens of an inner
  * segment and the conv_w-1 raw rows that end the previous segment (its cached
- * tail conv state).  Only the gated-delta family (rule DELTA, scalar gate).
+ * tail conv state).  The delta rule only (rule DELTA): the gated delta rule
+ * with one gate per token and head (gate_diag 0), or the delta rule with a
+ * gate per key channel, KDA (gate_diag 1; ch.2 sec.3, Table 1:
+ * T_t = (I - b_t k_t k_t^T) diag(g_t)).  Per-channel windows are applied token
+ * by token in fp32 (in hypic_compose on the serial dense path) and have no
+ * window pair (T_w, S_w0 must be NULL).
  *
  *   xk     [n_win, w, h_k, d_k]  raw (conv_w > 0) or final keys, in_dtype
  *   xv     [n_win, w, h_v, d_v]  raw or final values, in_dtype
  *   tail_k [n_win, conv_w-1, h_k, d_k], tail_v [n_win, conv_w-1, h_v, d_v]
  *          (conv_w > 1 only), in_dtype
  *   conv_wk [h_k*d_k, conv_w], conv_wv [h_v*d_v, conv_w] fp32 (conv_w > 0)
- *   beta, alpha [n_win, w, h_v] in_dtype
+ *   beta   [n_win, w, h_v] in_dtype
+ *   alpha  [n_win, w, h_v] (gate_diag 0) or [n_win, w, h_v, d_k] (gate_diag 1),
+ *          in_dtype, values in (0, 1]
  *   q      optional [n_win, w, h_k, d_k] final queries (in_dtype);
  *   o      optional [n_win, w, h_v, d_v] fp32 read-outs o_t = q_t^T S_t with the
  *          post-update state (Eq. (2)); q and o are both set or both NULL.
@@ -175,6 +182,7 @@ typedef struct {
     const void *beta, *alpha;
     const void *q;
     float *o, *T_w, *S_w0;
+    int32_t gate_diag;          /* 0: alpha per token and head; 1: per key channel (KDA) */
 } hypic_seam_desc;
 
 /*

@@ -54,7 +54,7 @@ class SeamDesc(ctypes.Structure):
                 ("n_win", _i32),
                 ("xk", _vp), ("xv", _vp), ("tail_k", _vp), ("tail_v", _vp),
                 ("conv_wk", _vp), ("conv_wv", _vp), ("beta", _vp), ("alpha", _vp),
-                ("q", _vp), ("o", _vp), ("T_w", _vp), ("S_w0", _vp)]
+                ("q", _vp), ("o", _vp), ("T_w", _vp), ("S_w0", _vp), ("gate_diag", _i32)]
 
 
 class RopeDesc(ctypes.Structure):
@@ -219,11 +219,11 @@ def segment_build(rule: int, gate_kind: int, k: torch.Tensor, v: torch.Tensor,
 
 @dataclass
 class Seams:
-    """Seam windows of the gated-delta family (see hypic.h for layouts)."""
+    """Seam windows of the delta-rule family (see hypic.h for layouts)."""
     xk: torch.Tensor                       # [n_win, w, h_k, d]
     xv: torch.Tensor                       # [n_win, w, h_v, d]
     beta: torch.Tensor                     # [n_win, w, h_v]
-    alpha: torch.Tensor                    # [n_win, w, h_v]
+    alpha: torch.Tensor                    # [n_win, w, h_v], or [n_win, w, h_v, d] (KDA)
     tail_k: Optional[torch.Tensor] = None  # [n_win, W-1, h_k, d]
     tail_v: Optional[torch.Tensor] = None  # [n_win, W-1, h_v, d]
     conv_wk: Optional[torch.Tensor] = None  # [h_k*d, W] fp32
@@ -240,9 +240,11 @@ class Seams:
         h_v = self.xv.shape[2]
         if tuple(self.xv.shape) != (n_win, w, h_v, d):
             raise ValueError("xv must be [n_win, w, h_v, d]")
-        for name in ("beta", "alpha"):
-            if tuple(getattr(self, name).shape) != (n_win, w, h_v):
-                raise ValueError(f"{name} must be [n_win, w, h_v]")
+        if tuple(self.beta.shape) != (n_win, w, h_v):
+            raise ValueError("beta must be [n_win, w, h_v]")
+        gate_diag = self.alpha.dim() == 4
+        if tuple(self.alpha.shape) not in ((n_win, w, h_v), (n_win, w, h_v, d)):
+            raise ValueError("alpha must be [n_win, w, h_v] or [n_win, w, h_v, d]")
         if self.conv_w > 1:
             if self.tail_k is None or tuple(self.tail_k.shape) != (n_win, self.conv_w - 1, h_k, d):
                 raise ValueError("tail_k must be [n_win, conv_w-1, h_k, d]")
@@ -265,7 +267,8 @@ class Seams:
                         xk=_ptr(self.xk), xv=_ptr(self.xv), tail_k=_ptr(self.tail_k),
                         tail_v=_ptr(self.tail_v), conv_wk=_ptr(self.conv_wk),
                         conv_wv=_ptr(self.conv_wv), beta=_ptr(self.beta), alpha=_ptr(self.alpha),
-                        q=_ptr(self.q), o=_ptr(self.o), T_w=_ptr(self.T_w), S_w0=_ptr(self.S_w0))
+                        q=_ptr(self.q), o=_ptr(self.o), T_w=_ptr(self.T_w), S_w0=_ptr(self.S_w0),
+                        gate_diag=1 if gate_diag else 0)
 
 
 def _compose_desc(T_pool, S0_pool, order, S_init, tform, prec, seams, S_out, group_len):

@@ -133,14 +133,16 @@ hypic_status validate_seams(const hypic_seam_desc *s, int h_v, int D, int max_w)
     if (s->conv_w > 0 && (!s->conv_wk || !s->conv_wv)) return HYPIC_E_INVALID;
     if (s->conv_w > 1 && (!s->tail_k || !s->tail_v)) return HYPIC_E_INVALID;
     if ((s->q == nullptr) != (s->o == nullptr)) return HYPIC_E_INVALID;
+    if (s->gate_diag != 0 && s->gate_diag != 1) return HYPIC_E_INVALID;
     return HYPIC_OK;
 }
 
 // dense split compose for d in {64, 128} takes the pipelined kernel
+// (windows with per-channel gates run token by token in the serial dense kernel)
 bool compose_uses_split(const hypic_compose_desc *d)
 {
     return d->tform == HYPIC_T_DENSE && d->prec == HYPIC_PREC_SPLIT &&
-           (d->d_k == 64 || d->d_k == 128);
+           (d->d_k == 64 || d->d_k == 128) && !(d->seams && d->seams->gate_diag);
 }
 
 // Group length of the two-level compose for a launch of nb positions (1: the
@@ -219,6 +221,7 @@ SeamArgs seam_args(const hypic_seam_desc *s)
     a.beta = s->beta; a.alpha = s->alpha; a.q = s->q;
     a.o = s->o; a.T_w = s->T_w; a.S_w0 = s->S_w0;
     a.w = s->w; a.conv_w = s->conv_w; a.k_l2norm = s->k_l2norm; a.h_k = s->h_k; a.h_v = s->h_v;
+    a.gate_diag = s->gate_diag;
     return a;
 }
 
@@ -559,6 +562,7 @@ hypic_status hypic_seam_advance(const hypic_seam_desc *d, float *S_inout, void *
     if (d->h_v <= 0) return HYPIC_E_INVALID;
     hypic_status st = validate_seams(d, d->h_v, d->d_k, 64);
     if (st != HYPIC_OK) return st;
+    if (d->gate_diag && (d->T_w || d->S_w0)) return HYPIC_E_UNSUPPORTED;
     if (d->n_win < 0) return HYPIC_E_INVALID;
     if (d->n_win == 0) return HYPIC_OK;
     st = device_check();

@@ -93,8 +93,12 @@ compose_dense_kernel(const ComposeArgs a)
         if constexpr (SEAMS) {
             const int pos = a.first_pos + j;
             if (a.has_seams && pos >= 1) {
-                seam_prep<D, 16, TIN>(sm.win, a.seam, pos - 1, h, c0);
-                seam_apply<D, 16, TIN>(sm.win, &sm.ST[cur][0][0], LD, a.seam, pos - 1, h, c0);
+                if (a.seam.gate_diag) {
+                    seam_apply_diag<D, 16, TIN>(sm.win, &sm.ST[cur][0][0], LD, a.seam, pos - 1, h, c0);
+                } else {
+                    seam_prep<D, 16, TIN>(sm.win, a.seam, pos - 1, h, c0);
+                    seam_apply<D, 16, TIN>(sm.win, &sm.ST[cur][0][0], LD, a.seam, pos - 1, h, c0);
+                }
             }
         }
         // S_next = T S + S0 for this wave's rows
@@ -191,6 +195,10 @@ __global__ void __launch_bounds__(256) seam_kernel(const ComposeArgs a, float *S
     const SeamArgs &sa = a.seam;
     for (int win = 0; win < n_win; ++win) {
         lds_barrier();
+        if (sa.gate_diag) {   // per-channel gates: token by token (no window pair)
+            seam_apply_diag<D, 64, TIN>(ws, &ST[0][0], D + 4, sa, win, h, c0);
+            continue;
+        }
         seam_prep<D, 64, TIN>(ws, sa, win, h, c0);
         // window pair: T_w[:, cols of this block] and S_w0[:, cols]
         if (sa.T_w) {

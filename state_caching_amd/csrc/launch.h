@@ -70,6 +70,7 @@ struct SeamArgs {
     const void *beta, *alpha, *q;
     float *o, *T_w, *S_w0;
     int w, conv_w, k_l2norm, h_k, h_v;
+    int gate_diag;              // alpha per key channel [n_win, w, h_v, D] (KDA windows)
 };
 
 // Dense / diagonal / scalar composition over a prompt's segments.

@@ -46,10 +46,11 @@ __device__ __forceinline__ float win_row(const TIN *x, const TIN *tail, int t, i
     return ld1(tail + (int64_t)(Wc - 1 + t) * row_stride + col);
 }
 
-// Window prep: everything that does not depend on the state (value columns
-// [c0, c0 + NC) of head h).
+// The window's keys (after conv and, if asked, L2 normalisation) into ws.K and
+// its value columns [c0, c0 + NC) of head h (after conv) into ws.V.  Ends with
+// a barrier.
 template <int D, int WMAX, typename TIN, int NC = 16>
-__device__ void seam_prep(WinSmem<D, WMAX, NC> &ws, const SeamArgs &a, int win, int h, int c0)
+__device__ void seam_stage_kv(WinSmem<D, WMAX, NC> &ws, const SeamArgs &a, int win, int h, int c0)
 {
     const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wv = tid >> 6, nwv = nt >> 6;
     const int w = a.w, Wc = a.conv_w;
@@ -86,6 +87,27 @@ __device__ void seam_prep(WinSmem<D, WMAX, NC> &ws, const SeamArgs &a, int win, 
         }
         ws.V[t][cc] = y;
     }
+    lds_barrier();
+    if (a.k_l2norm) {
+        for (int t = wv; t < w; t += nwv) {
+            float ss = 0.f;
+            for (int d = lane; d < D; d += 64) ss += ws.K[t][d] * ws.K[t][d];
+            ss = wave_sum(ss);
+            const float inv = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
+            for (int d = lane; d < D; d += 64) ws.K[t][d] *= inv;
+        }
+        lds_barrier();
+    }
+}
+
+// Window prep (scalar gates): everything that does not depend on the state
+// (value columns [c0, c0 + NC) of head h).
+template <int D, int WMAX, typename TIN, int NC = 16>
+__device__ void seam_prep(WinSmem<D, WMAX, NC> &ws, const SeamArgs &a, int win, int h, int c0)
+{
+    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wv = tid >> 6;
+    const int w = a.w;
+    seam_stage_kv<D, WMAX, TIN, NC>(ws, a, win, h, c0);
     if (wv == 0) {   // gates: inclusive prefix and exclusive suffix of log2 a over the window
         const TIN *bp = reinterpret_cast<const TIN *>(a.beta) + (int64_t)win * w * a.h_v + h;
         const TIN *ap = reinterpret_cast<const TIN *>(a.alpha) + (int64_t)win * w * a.h_v + h;
@@ -105,16 +127,6 @@ __device__ void seam_prep(WinSmem<D, WMAX, NC> &ws, const SeamArgs &a, int win, 
         if (lane == 0) ws.gw = scale_pow2(1.f, tot);
     }
     lds_barrier();
-    if (a.k_l2norm) {
-        for (int t = wv; t < w; t += nwv) {
-            float ss = 0.f;
-            for (int d = lane; d < D; d += 64) ss += ws.K[t][d] * ws.K[t][d];
-            ss = wave_sum(ss);
-            const float inv = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
-            for (int d = lane; d < D; d += 64) ws.K[t][d] *= inv;
-        }
-        lds_barrier();
-    }
     // G (strictly lower, scaled by b_r)
     for (int idx = tid; idx < w * w; idx += nt) {
         const int r = idx / w, c = idx % w;
@@ -202,6 +214,58 @@ __device__ void seam_apply(WinSmem<D, WMAX, 16> &ws, float *ST, int ldst, const 
         float acc = gw * ST[cc * ldst + d];
         for (int t = 0; t < w; ++t) acc += ws.K[t][d] * ws.E[t][cc];
         ST[cc * ldst + d] = acc;
+    }
+    lds_barrier();
+}
+
+// Window with a gate per key channel (the delta rule with a diagonal gate,
+// KDA: T_t = (I - b_t k_t k_t^T) diag(g_t), u_t = b_t k_t v_t^T; ch.2 sec.3
+// Table 1), applied token by token to the state block ST[16][ldst] (in
+// place): S <- diag(g_t) S, then S <- S + b_t k_t (v_t^T - k_t^T S); with
+// read-outs also o_t = q_t^T S after the token.  Each wave owns whole columns
+// of the block, so the token loop needs no barrier.  fp32 throughout.
+template <int D, int WMAX, typename TIN>
+__device__ void seam_apply_diag(WinSmem<D, WMAX, 16> &ws, float *ST, int ldst, const SeamArgs &a,
+                                int win, int h, int c0)
+{
+    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wv = tid >> 6, nwv = nt >> 6;
+    const int w = a.w;
+    seam_stage_kv<D, WMAX, TIN, 16>(ws, a, win, h, c0);
+    // gates g_t[d] (into the W rows, unused on this path) and write strengths
+    const TIN *ap = reinterpret_cast<const TIN *>(a.alpha) + ((int64_t)win * w * a.h_v + h) * D;
+    for (int idx = tid; idx < w * D; idx += nt) {
+        const int t = idx / D, d = idx % D;
+        ws.W[t][d] = ld1(ap + (int64_t)t * a.h_v * D + d);
+    }
+    if (tid < w) ws.beta[tid] = ld1(reinterpret_cast<const TIN *>(a.beta) + ((int64_t)win * w + tid) * a.h_v + h);
+    lds_barrier();
+    const int kh = h / (a.h_v / a.h_k);
+    const int64_t ldk = (int64_t)a.h_k * D;
+    const TIN *qp = a.q ? reinterpret_cast<const TIN *>(a.q) + (int64_t)win * w * ldk + (int64_t)kh * D : nullptr;
+    float *op = a.o ? a.o + (int64_t)win * w * a.h_v * D + (int64_t)h * D + c0 : nullptr;
+    for (int t = 0; t < w; ++t) {
+        const float bt = ws.beta[t];
+        for (int cc = wv; cc < 16; cc += nwv) {
+            float *col = ST + cc * ldst;
+            float x = 0.f;
+            for (int d = lane; d < D; d += 64) {
+                const float sv = col[d] * ws.W[t][d];
+                col[d] = sv;
+                x += ws.K[t][d] * sv;
+            }
+            x = wave_sum(x);
+            const float coef = bt * (ws.V[t][cc] - x);
+            float o = 0.f;
+            for (int d = lane; d < D; d += 64) {
+                const float sv = col[d] + coef * ws.K[t][d];
+                col[d] = sv;
+                if (qp) o += ld1(qp + (int64_t)t * ldk + d) * sv;
+            }
+            if (qp) {
+                o = wave_sum(o);
+                if (lane == 0) op[(int64_t)t * a.h_v * D + cc] = o;
+            }
+        }
     }
     lds_barrier();
 }

@@ -149,7 +149,7 @@ def gdn(seed, seg_len, h_k, h_v, d, dtype, alpha_div=1.0, name="gdn",
                     seam_w=seam_w, seed=seed)
 
 
-def kda(seed, seg_len, h_k, h_v, d, dtype, gate_div=1.0, name="kda", conv_w=0):
+def kda(seed, seg_len, h_k, h_v, d, dtype, gate_div=1.0, name="kda", conv_w=0, seam_w=0):
     """Delta rule with a diagonal gate (KDA row of Table 1).
 
     k ~ N(0,1) L2-normalised per (token, key head) (raw N(0,1) when conv_w>0),
@@ -172,7 +172,8 @@ def kda(seed, seg_len, h_k, h_v, d, dtype, gate_div=1.0, name="kda", conv_w=0):
     return Workload(name=name, rule=RULE_DELTA, gate_kind=GATE_DIAG, dtype=dtype,
                     h_k=h_k, h_v=h_v, d_k=d, d_v=d, seg_len=list(seg_len),
                     k=_round(k, dtype), v=_round(v, dtype), beta=_round(beta, dtype),
-                    gate=_round(g, dtype), conv_w=conv_w, conv_wk=wk, conv_wv=wv, seed=seed)
+                    gate=_round(g, dtype), conv_w=conv_w, conv_wk=wk, conv_wv=wv, seam_w=seam_w,
+                    seed=seed)
 
 
 def retnet(seed, seg_len, h, d, dtype=torch.float32, name="retnet", gammas=None):

@@ -403,6 +403,17 @@ def pin_compose_equals_full(path):
             assert err < 1e-12, (seam_w, err)
         else:
             assert err > 1e-4, (seam_w, err)
+    # per-channel gates (KDA windows), GQA, read-outs at the window tokens
+    wl = synth.kda(17, [30, 26, 35, 22], 1, 2, 8, torch.float32, gate_div=16.0, conv_w=4, seam_w=6)
+    q_all = np.random.default_rng(18).standard_normal((wl.n_tokens, 1, 8))
+    wins = wl.window_ranges()
+    T, S0 = oracle.build_pairs(wl, path=path)
+    S, o = oracle.compose(T, S0, wl=wl, seams=True, path=path,
+                          q=np.stack([q_all[s:e] for s, e in wins]))
+    F, o_full = oracle.recur_range(wl, 0, wl.n_tokens, np.zeros((2, 8, 8)), path=path, q=q_all)
+    assert oracle.relF(S, F) < 1e-12
+    for j, (s, e) in enumerate(wins):
+        assert oracle.relF(o[j], o_full[s:e]) < 1e-12, j
     wl = synth.gdn(12, [33, 50, 21, 64], 1, 2, 8, torch.float32, alpha_div=16.0)
     S_init = np.random.default_rng(13).standard_normal((2, 8, 8))
     T, S0 = oracle.build_pairs(wl, path=path)

@@ -190,6 +190,27 @@ def test_seam_validation(sca):
     assert L.hypic_seam_advance(ctypes.byref(sd), None, None) == -1
     sd.q = 16                                                            # q without o
     assert L.hypic_seam_advance(ctypes.byref(sd), 16, None) == -1
+    sd.q = None
+    sd.gate_diag = 2                                                     # neither gate form
+    assert L.hypic_seam_advance(ctypes.byref(sd), 16, None) == -1
+    sd.gate_diag = 1                                                     # KDA windows have no pair
+    sd.T_w = 16
+    assert L.hypic_seam_advance(ctypes.byref(sd), 16, None) == -2
+
+
+def test_kda_seams_take_serial_compose(sca):
+    """Per-channel window gates need no workspace: the compose runs them token
+    by token in the serial dense kernel (the split path's window records hold
+    scalar-gate operators only)."""
+    L = sca.library()
+    n, h, d, w = 100, 32, 128, 8
+    sd = sca.SeamDesc(rule=sca.RULE_DELTA, in_dtype=sca.BF16, w=w, conv_w=4, k_l2norm=1, h_k=h,
+                      h_v=h, d_k=d, d_v=d, n_win=n - 1, xk=16, xv=16, tail_k=16, tail_v=16,
+                      conv_wk=16, conv_wv=16, beta=16, alpha=16)
+    dsc = _compose_desc(sca, order=list(range(n)), h_v=h, n_slots=n, seams=ctypes.pointer(sd))
+    assert L.hypic_workspace_size(ctypes.byref(dsc), sca.WS_COMPOSE) > 0
+    sd.gate_diag = 1
+    assert L.hypic_workspace_size(ctypes.byref(dsc), sca.WS_COMPOSE) == 0
 
 
 def test_binding_rejects_out_of_range_rows(sca):

@@ -899,3 +899,68 @@ def test_multilayer_seam_stack(conv_w):
         eo, eo_win = _readout_errs(np64(got[l][1]), ref[l][1])
         print(f"  layer {l}: relF S {eS:.3e}, o {eo:.3e} (worst head), {eo_win:.3e} (worst window and head)")
         assert eS <= 1e-5 and eo <= 1e-5 and eo_win <= 1e-4, l
+
+
+@pytest.mark.parametrize("d,conv_w,dtype", [(64, 4, torch.bfloat16), (128, 4, torch.bfloat16),
+                                            (128, 0, torch.bfloat16), (32, 4, torch.float32),
+                                            (16, 0, torch.float32)],
+                         ids=["bf16-64-conv", "bf16-128-conv", "bf16-128", "f32-32-conv", "f32-16"])
+def test_kda_seams_compose(d, conv_w, dtype):
+    """KDA prompts on the reuse path (ch.2 sec.3 Table 1, KDA row; ch.2 sec.5):
+    pairs built on the device, composed with per-channel-gate seam windows that
+    read out at every window token, GQA, ragged segments: the end state per head
+    and the read-outs against the oracle's composition of its own pairs."""
+    need_gpu()
+    lens = [40, 57, 33, 70, 21, 64, 45]
+    wl = synth.kda(740 + d + conv_w, lens, 1, 2, d, dtype, gate_div=16.0, conv_w=conv_w, seam_w=8)
+    sca, DW = _lib()
+    dw = DW(wl)
+    T, S0 = dw.build()
+    S_init = synth.random_state(741 + d, 2, d, d)
+    q = _attach_queries(dw, 742 + d + conv_w)
+    case(f"KDA compose with seams and read-outs d={d} conv_w={conv_w} {dtype}")
+    S = dw.compose(T, S0, S_init=S_init.cuda())
+    torch.cuda.synchronize()
+    Tr, S0r = oracle.build_pairs(wl)
+    S_or, o_or = oracle.compose(Tr, S0r, S_init=np64(S_init), wl=wl, seams=True, q=q)
+    eS = head_relF(np64(S), S_or)
+    eo, eo_win = _readout_errs(np64(dw.seams.o), o_or)
+    print(f"  relF S {eS:.3e}, o {eo:.3e} (worst head), {eo_win:.3e} (worst window and head)")
+    tol = 1e-5 if dtype == torch.float32 else 2e-3
+    assert eS <= tol and eo <= tol and eo_win <= 1e-4
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_kda_seam_standalone(dtype):
+    """hypic_seam_advance over one KDA window (per-channel gates) with read-outs,
+    from a random state, against the oracle's token recurrence; a window pair
+    is not available for per-channel gates and is refused."""
+    need_gpu()
+    sca, DW = _lib()
+    d, h = 64, 2
+    wl = synth.kda(750, [40, 30], 1, h, d, dtype, gate_div=8.0, conv_w=4, seam_w=8)
+    dw = DW(wl)
+    rng = np.random.default_rng(751)
+    S_init = synth.random_state(752, h, d, d)
+    q = synth._round(rng.standard_normal((1, 8, 1, d)) / np.sqrt(d), dtype)
+    sm = dw.seams
+    sm.q = q.cuda()
+    sm.o = torch.zeros((1, 8, h, d), dtype=torch.float32, device="cuda")
+    S = S_init.clone().cuda()
+    case(f"KDA seam standalone {dtype}")
+    sca.seam_advance(S, sm)
+    torch.cuda.synchronize()
+    s, e = wl.window_ranges()[0]
+    sl = oracle.Slice(wl, s, e)
+    u = sl.units()
+    S_ref = np64(S_init).copy()
+    o_ref = np.zeros((8, h, d))
+    oracle.recur_units(wl.rule, sl.gate_kind, u, d, d, sl.k, sl.v, sl.beta, sl.g, S_ref,
+                       q=np.ascontiguousarray(np64(q)[0]), o=o_ref, off_q=u.off_k, ldq=u.ldk,
+                       off_o=u.off_v, ldo=u.ldv)
+    errs = (head_relF(np64(S), S_ref), oracle.relF(np64(sm.o)[0], o_ref))
+    print("  KDA seam relF S %.2e o %.2e" % errs)
+    assert max(errs) <= 1e-5   # fp32 window arithmetic for every input dtype
+    sm.T_w = torch.zeros((1, h, d, d), dtype=torch.float32, device="cuda")
+    with pytest.raises(sca.HypicError):
+        sca.seam_advance(S, sm)
