@@ -44,6 +44,7 @@ PEAK_MFMA_F32 = 157.3      # TFLOP/s, MI355X dense fp32 matrix cores
 CSRC = os.path.join(ROOT, "state_caching_amd", "csrc")
 KERNEL_SOURCES = {
     "build_delta_f16_kernel": ["build_delta_f16.hip", "common.h", "launch.h"],
+    "build_gdn_kernel": ["build_gdn.hip", "common.h", "launch.h"],
     "seam_ops_kernel": ["seam.h", "compose_split.hip", "common.h", "launch.h"],
     "compose_split_kernel": ["compose_split.hip", "seam.h", "common.h", "launch.h"],
     "compose_group_kernel": ["compose_group.hip", "seam.h", "common.h", "launch.h"],
@@ -338,10 +339,10 @@ def build_leg(args, torch, dev, out):
                                "inputs, fp32 pairs: build all (segment, head) pairs then compose",
                    "segments": wl3.n_seg, "seg_len": 4096, "h_v": wl3.h_v, "h_k": wl3.h_k,
                    "d": 128, "in_dtype": "bf16"},
-        "roofline": {"bound": "mfma", "kernel": "build_delta_f16_kernel<128,bf16,bf16,bf16>",
+        "roofline": {"bound": "mfma", "kernel": "build_gdn_kernel<bf16,bf16,bf16>",
                      "achieved": ach, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
                      "frac": ach / PEAK_MFMA_F16,
-                     "traffic": counter_traffic(["build_delta_f16_kernel"], "gdn_32k_prompt"),
+                     "traffic": counter_traffic(["build_gdn_kernel"], "gdn_32k_prompt"),
                      "kernel_ms": kb, "kernel_ms_min_max": [kb_all[0], kb_all[-1]],
                      "timing": "median of 20 HIP-event-timed calls, 512 MB cache flush before each",
                      "kernel_ms_in_step_loop": sum(per["build"]) / len(per["build"]),

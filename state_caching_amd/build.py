@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libhypic.so")
-SOURCES = ["abi.hip", "build_delta.hip", "build_delta_f16.hip", "build_decay.hip", "build_kda.hip", "compose.hip", "compose_split.hip", "compose_group.hip", "conv.hip", "rope.hip"]
+SOURCES = ["abi.hip", "build_delta.hip", "build_delta_f16.hip", "build_gdn.hip", "build_decay.hip", "build_kda.hip", "compose.hip", "compose_split.hip", "compose_group.hip", "conv.hip", "rope.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -477,14 +477,15 @@ static hipError_t launch_one(const DeltaArgs &a, int n_units, hipStream_t st)
     return hipGetLastError();
 }
 
-// bf16 inputs use the fp16-operand pipelined kernel (build_delta_f16.hip) for
-// d >= 64.  Below that a 64-token chunk erases most of the key space, so
+// bf16 inputs use the fp16-operand pipelined kernels: build_gdn.hip at d = 128,
+// build_delta_f16.hip at d = 64.  Below that a 64-token chunk erases most of the key space, so
 // Tbar - K^T (W Tbar) cancels heavily and fp16 rounding of W, Tbar and E is
 // amplified: small heads, like fp32 inputs, use fp32 products here.
 template <int D>
 static hipError_t launch_d(const DeltaArgs &a, int kv_kind, int g_kind, bool f16, int n_units,
                            hipStream_t st)
 {
+    if (f16 && D == 128) return launch_build_gdn(a, kv_kind, g_kind, n_units, st);
     if (f16 && D >= 64) return launch_build_delta_f16(a, D, kv_kind, g_kind, n_units, st);
     if (kv_kind == IN_BF16 && g_kind == IN_BF16) return launch_one<D, false, bf16_t, bf16_t>(a, n_units, st);
     if (kv_kind == IN_F32 && g_kind == IN_BF16) return launch_one<D, false, float, bf16_t>(a, n_units, st);

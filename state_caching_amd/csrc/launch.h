@@ -111,6 +111,8 @@ hipError_t launch_build_delta(const DeltaArgs &a, int D, int kv_kind, int g_kind
                               int n_units, hipStream_t st);
 hipError_t launch_build_delta_f16(const DeltaArgs &a, int D, int kv_kind, int g_kind, int n_units,
                                   hipStream_t st);
+// d = 128 with bf16 inputs (or their conv workspace): build_gdn.hip
+hipError_t launch_build_gdn(const DeltaArgs &a, int kv_kind, int g_kind, int n_units, hipStream_t st);
 // delta rule with a diagonal gate (KDA): alpha is the gate [N, h_v, D]
 hipError_t launch_build_kda(const DeltaArgs &a, int D, int kv_kind, int g_kind, int n_units, hipStream_t st);
 hipError_t launch_build_decay(const DecayArgs &a, int D, int in_kind, int n_units,

@@ -10,8 +10,8 @@ source to assembly and walks the control-flow graph of each kernel: on every
 path from a matrix-core instruction to an instruction that reads any of its
 destination registers there must be at least MIN_WAIT[opcode] wait states
 (one per instruction, n + 1 per s_nop n): the spacing the compiler itself
-keeps on straight-line code, 8 after the 4-pass 16x16x32 half-precision
-products and 10 after the 8-pass 16x16x4 fp32 product.  A matrix-core opcode
+keeps on straight-line code, 8 after the 16x16x32 and 16x16x16
+half-precision products and 10 after the 8-pass 16x16x4 fp32 product.  A matrix-core opcode
 without a figure here fails the test, so a new one gets a deliberate entry.
 """
 from __future__ import annotations
@@ -28,6 +28,7 @@ from state_caching_amd import build as hb
 MIN_WAIT = {
     "v_mfma_f32_16x16x32_bf16": 8,
     "v_mfma_f32_16x16x32_f16": 8,
+    "v_mfma_f32_16x16x16_f16": 8,
     "v_mfma_f32_16x16x4_f32": 10,
 }
 _REG = re.compile(r"\b([av])\[(\d+):(\d+)\]|\b([av])(\d+)\b")
