@@ -25,7 +25,7 @@
 //                    of S (fp32 in matrix-core accumulators): P (one half of its
 //                    columns at a time; the value term scaled from the raw rows
 //                    here), the block substitution for E, and X += K^T E
-//   prep waves 4-7   chunk j: the raw value rows go from memory straight into LDS;
+//   prep waves 4-7   chunk j: the raw value rows (prefetched into registers) to LDS;
 //                    gates; 16 key rows per wave converted to fp16.  Chunk j-1:
 //                    the transposed key copy; the Gram tiles below the diagonal
 //                    (negated; waves 5-7) and, on wave 4, all four diagonal
@@ -210,8 +210,12 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
         const TG *ap = reinterpret_cast<const TG *>(a.alpha) + a.gtok0[s] * a.h_v + h;
         constexpr bool VSC = std::is_same<TV, _Float16>::value;   // conv workspace: a power of two per row
         const float *vsp = VSC ? a.vscale + a.tok0[s] * a.h_v + h : nullptr;
-        // register prefetch of the next chunk's key rows and gates, double-buffered
+        // register prefetch of the next chunk's key rows, value rows and gates,
+        // double-buffered.  The value rows pass through registers rather than a direct
+        // memory-to-LDS load: the compiler orders every later LDS read of the wave
+        // behind such a load, which would expose the prefetch's memory latency.
         typename Raw8<TK>::type kraw[2][4];
+        uint4 vraw[2][4];
         TG braw[2], araw[2];
         float vrs[2];
         auto fetch = [&](int c, auto pc) {
@@ -227,19 +231,14 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
             araw[P] = ap[gc + go];
             if constexpr (VSC) vrs[P] = vsp[gc + go];
             else vrs[P] = 1.f;
-        };
-        // the raw value rows 16 pw .. 16 pw + 15 of chunk c, memory to LDS slot c % 3:
-        // load i fills rows 16 pw + 4i + g, lane r16 the piece at position r16 (rows past
-        // the segment end repeat its last row; their factor is 0)
-        auto load_v = [&](int c) {
-            const int sl = c % 3, last = len - 1 - 64 * c;
+            // raw value rows 16 pw + 4i + g, the 16-byte piece r16 ^ 2 (t & 7) of row t
+            // (rows past the segment end repeat its last row; their factor is 0)
             const unsigned char *vc = vb + (int64_t)(64 * c) * ldv_b;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * pw + 4 * i + g;
                 const uint32_t off = (uint32_t)min(t, last) * ldv_b + 16 * (r16 ^ (2 * (t & 7)));
-                __builtin_amdgcn_global_load_lds(vc + off, (__attribute__((address_space(3))) void *)&sm.Vr[sl][16 * pw + 4 * i][0],
-                                                 16, 0, 0);
+                vraw[P][i] = *reinterpret_cast<const uint4 *>(vc + off);
             }
         };
 
@@ -258,6 +257,10 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
             sm.beta[sl][lane] = br;
             sm.fac[sl][lane] = gin ? exp2f(sfx) * vrs[P] : 0.f;
             sm.gb[sl] = exp2f(lane_f(sfx + l2, 0));
+            // value rows into slot sl: row 16 pw + 4i + g, piece position r16
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<uint4 *>(&sm.Vr[sl][16 * pw + 4 * i + g][8 * r16]) = vraw[P][i];
             if constexpr (decltype(tail)::value) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) mask_raw8(kraw[P][q], 64 * c + row0 + q < len);
@@ -370,9 +373,9 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
         const std::integral_constant<int, 0> p0;
         const std::integral_constant<int, 1> p1;
         if (nch > 0) fetch(0, p0);
-        // iteration j: V rows of chunk j to LDS and the prefetch of chunk j + 1 first (in
-        // flight for the whole step), then chunk j's gates and keys, then chunk j-1's
-        // transposed keys, Gram tiles and inverses; every load has landed before the barrier
+        // iteration j: the prefetch of chunk j + 1 first (in flight across the barrier,
+        // waited for where the next step first uses it), then chunk j's gates, keys and
+        // value rows, then chunk j-1's transposed keys, Gram tiles and inverses
         auto iter = [&](int j, auto pc) {
             constexpr int P = decltype(pc)::value;
             lds_barrier();
@@ -380,10 +383,11 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
             // so no later wait covers the loads issued below
 #pragma unroll
             for (int q = 0; q < 4; ++q) claim(kraw[P][q]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) claim(vraw[P][i]);
             claim(braw[P]);
             claim(araw[P]);
             claim(vrs[P]);
-            if (j < nch) load_v(j);
             if (j + 1 < nch) fetch(j + 1, std::integral_constant<int, P ^ 1>());
             if (j < nch - 1) stage(j, pc, full);
             else if (j == nch - 1) stage(j, pc, tail);
@@ -395,7 +399,6 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
                     store_kt(j - 1);
                 }
             }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         };
         for (int j = 0; j < nch + 2; j += 2) {
             iter(j, p0);
