@@ -279,7 +279,10 @@ hypic_status hypic_segment_build(const hypic_build_desc *d, void *ws, size_t ws_
     // gated-delta segments with bf16 inputs and d >= 64 take the fp16-operand
     // build, up to kF16MaxLen tokens; longer ones the fp32-operand build
     const bool f16_family = d->rule == HYPIC_RULE_DELTA && !kda && d->in_dtype == HYPIC_BF16 && D >= 64;
-    auto long_seg = [&](int s) { return f16_family && d->seg_len[s] > kF16MaxLen; };
+    // KDA segments with bf16 inputs (no conv) and d >= 64 take the fp16-operand
+    // state products under the same length limit
+    const bool kda_f16 = kda && d->in_dtype == HYPIC_BF16 && D >= 64 && !prep;
+    auto long_seg = [&](int s) { return (f16_family || kda_f16) && d->seg_len[s] > kF16MaxLen; };
     float *wk = nullptr, *wvv = nullptr, *wvs = nullptr;
     if (prep) {
         const int64_t rows = build_rows(d);
@@ -352,7 +355,7 @@ hypic_status hypic_segment_build(const hypic_build_desc *d, void *ws, size_t ws_
                 a.ldk = (int64_t)d->h_k * D; a.ldv = (int64_t)d->h_v * D;
             }
             const int kv_kind = khalf ? IN_F16K : (prep ? IN_F32 : in_kind);
-            st = kda ? from_hip(launch_build_kda(a, D, kv_kind, in_kind, nb * d->h_v, hs))
+            st = kda ? from_hip(launch_build_kda(a, D, kv_kind, in_kind, kda_f16 && !lng, nb * d->h_v, hs))
                      : from_hip(launch_build_delta(a, D, kv_kind, in_kind, d->in_dtype == HYPIC_BF16 && !lng,
                                                    nb * d->h_v, hs));
         } else {

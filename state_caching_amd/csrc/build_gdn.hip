@@ -436,9 +436,12 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
             float target = (float)pow2_exponent(xm) + sig[n];
             if (xm == 0.f) target = isS ? (float)ev : sig[n];
             if (isS && target < (float)ev - 4.f) target = (float)ev - 4.f;
-            const float f = exp2f(sig[n] - target);
+            // an integer shift, exact, and finite however far the tile has decayed
+            const int sh = (int)(sig[n] - target);
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) X[mt][n] *= f;
+            for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) X[mt][n][i] = ldexpf(X[mt][n][i], sh);
             sig[n] = target;
         };
         // chunk c, before its products: the chunk gate on S

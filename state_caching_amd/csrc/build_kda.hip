@@ -329,6 +329,415 @@ __global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_kernel(const DeltaA
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 inputs, d >= 64: the same chunk algebra with the two state products on
+// fp16 matrix-core operands (16x16x32, fp32 accumulation):
+//   E = [0 | U] - W X     (A = W, token rows with keys permuted inside each
+//                          32-key block; B = -X from the state's accumulators)
+//   X <- Gam_b X + Kh^T E (A = Kh^T, key rows with tokens permuted the same way;
+//                          B = E from its accumulators)
+// The state's column tiles are carried in power-of-two units (renormalised every
+// 4 chunks, the S tiles also when a chunk's values run more than 2^4 ahead), so
+// every fp16 operand stays in range.  W = M diag(b) (Gam K) and U = M diag(b) V
+// take fp16 operands too (A = M diag(b) rounded once per chunk; the value
+// columns scaled by a power of two per tile and chunk); the Gram and the
+// inverse stay fp32.
+template <int D>
+struct KdaHSmem {
+    using C = KdaCfg<D>;
+    static constexpr int LDW = D + 8;         // W row stride (halves)
+    static constexpr int LDK = 64 + 8;        // Kh^T row stride (halves)
+    float KT[D][C::LDT];     // keys (dim-major); then Gam k
+    float CL[D][C::LDT];     // cumulative log2 gates (dim-major)
+    uint16_t VT[D][LDK];     // raw bf16 values (dim-major)
+    union {
+        float Gm[64][C::LDG];        // b_r L_rs for s < r, else 0
+        _Float16 Wh[64][LDW];        // then W (token rows, keys permuted)
+    };
+    float Mm[64][C::LDG];    // M = (I + Gm)^-1
+    _Float16 Mb[64][LDK];    // M diag(b) in fp16 (token rows, columns permuted)
+    _Float16 Kh[D][LDK];     // Kh^T (key rows, tokens permuted)
+    float beta[64];
+    float clb[D];
+    float gamb[D];
+};
+
+// position of index k inside its block of 32 in the permuted operand order: lane
+// group g's 8 elements are k = 4g + (e & 3) + 16 (e >> 2), e = 0..7
+__device__ __forceinline__ int kda_perm(int k)
+{
+    return (k & ~31) + 8 * ((k & 15) >> 2) + 4 * ((k >> 4) & 1) + (k & 3);
+}
+
+template <int D, typename TG>
+__global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_f16_kernel(const DeltaArgs a)
+{
+    using C = KdaCfg<D>;
+    using SM = KdaHSmem<D>;
+    constexpr int MT = C::MT, NW = C::NW, KB = D / 32, LDW = SM::LDW, LDK = SM::LDK;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    SM &sm = *reinterpret_cast<SM *>(smem_raw);
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int unit = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int s = unit / a.h_v, h = unit % a.h_v;
+    const int kh = h / (a.h_v / a.h_k);
+    const int len = a.len[s];
+    const bf16_t *kp = reinterpret_cast<const bf16_t *>(a.k) + a.tok0[s] * a.ldk + (int64_t)kh * D;
+    const bf16_t *vp = reinterpret_cast<const bf16_t *>(a.v) + a.tok0[s] * a.ldv + (int64_t)h * D;
+    const TG *bp = reinterpret_cast<const TG *>(a.beta) + a.gtok0[s] * a.h_v + h;
+    const TG *gp = reinterpret_cast<const TG *>(a.alpha) + (a.gtok0[s] * a.h_v + h) * (int64_t)D;
+    const int64_t ldg = (int64_t)a.h_v * D;
+
+    for (int idx = tid; idx < 64 * 64; idx += C::NT) {
+        const int r = idx >> 6, c = idx & 63;
+        if ((c >> 4) > (r >> 4)) sm.Mm[r][c] = 0.f;
+    }
+
+    // X = [T | S] in power-of-two units: X[mt][jn] holds rows 16 mt .., column tile 2w + jn
+    f4 X[MT][2];
+    float sig[2] = {0.f, 0.f};
+    int svq = 0;   // value exponent of the last chunk (S tile waves)
+#pragma unroll
+    for (int jn = 0; jn < 2; ++jn) {
+        const int n = 2 * w + jn;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                X[mt][jn][i] = (n < MT && 16 * mt + 4 * g + i == 16 * n + r16) ? 1.f : 0.f;
+    }
+    // Xhat <- Xhat 2^(sig - target): the unit follows the tile's largest entry,
+    // never below 2^(ev - 4) for S (keeps the value term of E within fp16 range)
+    auto renorm = [&](int jn, bool isS, int ev) {
+        float xm = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xm = fmaxf(xm, fabsf(X[mt][jn][i]));
+        xm = wave_max(xm);
+        float target = (float)pow2_exponent(xm) + sig[jn];
+        if (xm == 0.f) target = isS ? (float)ev : sig[jn];
+        if (isS && target < (float)ev - 4.f) target = (float)ev - 4.f;
+        // an integer shift, exact, and finite however far the tile has decayed
+        const int sh = (int)(sig[jn] - target);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) X[mt][jn][i] = ldexpf(X[mt][jn][i], sh);
+        sig[jn] = target;
+    };
+
+    constexpr int CPR = D / 8;
+    const int prow = tid / CPR, pcol = 8 * (tid % CPR);
+    constexpr int NPASS = 64 * CPR / C::NT;   // rows per thread per chunk
+    typename Raw8<bf16_t>::type kraw[NPASS], vraw[NPASS];
+    typename Raw8<TG>::type graw[NPASS];
+    float br = 0.f;
+    constexpr int PROWS = C::NT / CPR;
+    auto fetch = [&](int c) {
+        const int t0 = 64 * c;
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const int t = t0 + prow + PROWS * p;
+            if (t < len) {
+                ld_raw8(kp + (int64_t)t * a.ldk + pcol, kraw[p]);
+                ld_raw8(vp + (int64_t)t * a.ldv + pcol, vraw[p]);
+                ld_raw8(gp + (int64_t)t * ldg + pcol, graw[p]);
+            } else {
+                zero_raw8(kraw[p]);
+                zero_raw8(vraw[p]);
+                zero_raw8(graw[p]);
+            }
+        }
+        if (w == 0) {
+            const int t = t0 + lane;
+            br = t < len ? ld1(bp + (int64_t)t * a.h_v) : 0.f;
+        }
+    };
+
+    const int nch = (len + 63) / 64;
+    if (nch > 0) fetch(0);
+
+    for (int c = 0; c < nch; ++c) {
+        lds_barrier();   // readers of the previous chunk are done
+
+        // ---- stage keys, values, log2 gates (dim-major), betas -------------------
+        {
+            float kr[NPASS][8], vr[NPASS][8], gr[NPASS][8];
+#pragma unroll
+            for (int p = 0; p < NPASS; ++p) {
+                widen8(kraw[p], kr[p]);
+                widen8(vraw[p], vr[p]);
+                widen8(graw[p], gr[p]);
+            }
+#pragma unroll
+            for (int p = 0; p < NPASS; ++p) {
+                const int t = prow + PROWS * p;
+                const bool in = 64 * c + t < len;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sm.KT[pcol + e][t] = kr[p][e];
+                    sm.VT[pcol + e][kda_perm(t)] = (uint16_t)(__float_as_uint(vr[p][e]) >> 16);
+                    sm.CL[pcol + e][t] = in ? fmaxf(log2f(gr[p][e]), -126.f) : 0.f;
+                }
+            }
+            if (w == 0) sm.beta[lane] = br;
+        }
+        if (c + 1 < nch) fetch(c + 1);
+        lds_barrier();
+
+        // ---- cumulative log2 gates over the chunk, per channel
+        for (int d = w; d < D; d += NW) {
+            const float cl = wave_prefix_incl(sm.CL[d][lane]);
+            sm.CL[d][lane] = cl;
+            if (lane == 63) {
+                sm.clb[d] = cl;
+                sm.gamb[d] = exp2f(cl);
+            }
+        }
+        lds_barrier();
+
+        // ---- decay-aware Gram: b_r sum_d k_r k_s 2^(cl_r - cl_s), s < r ------------
+        for (int q = w; q < 10; q += NW) {
+            const int ti = kKdaTi[q], tj = kKdaTj[q];
+            const int ref = ti == tj ? 16 * ti + 8 : 16 * tj + 15;
+            f4 acc = zero4();
+#pragma unroll 4
+            for (int ks = 0; ks < D / 4; ++ks) {
+                const int k = g * (D / 4) + ks;
+                const float cr = sm.CL[k][ref];
+                const float A = sm.KT[k][16 * ti + r16] * exp2f(sm.CL[k][16 * ti + r16] - cr);
+                const float B = sm.KT[k][16 * tj + r16] * exp2f(cr - sm.CL[k][16 * tj + r16]);
+                acc = mma(A, B, acc);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 16 * ti + 4 * g + i, cc = 16 * tj + r16;
+                sm.Gm[rr][cc] = (cc < rr) ? sm.beta[rr] * acc[i] : 0.f;
+            }
+        }
+        lds_barrier();
+
+        // ---- M = (I + Gm)^-1: diagonal 16x16 blocks by forward substitution ----
+        if (w == 0) {
+            const int o = 16 * (lane >> 4), cc = lane & 15;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+                for (int q = 0; q < r; ++q) acc -= sm.Gm[o + r][o + q] * x[q];
+                x[r] = acc;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.Mm[o + r][o + cc] = x[r];
+        }
+        lds_barrier();
+        for (int p = w; p < 2; p += NW) {
+            const int o0 = 32 * p, o1 = 32 * p + 16;
+            f4 y = zero4();
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int k = 4 * g + ks;
+                y = mma(sm.Gm[o1 + r16][o0 + k], sm.Mm[o0 + k][o0 + r16], y);
+            }
+            f4 m = zero4();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) m = mma(sm.Mm[o1 + r16][o1 + 4 * g + i], y[i], m);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.Mm[o1 + 4 * g + i][o0 + r16] = -m[i];
+        }
+        lds_barrier();
+        for (int tj = w; tj < 2; tj += NW) {
+            f4 y2 = zero4(), y3 = zero4();
+            for (int tk = tj; tk < 2; ++tk) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const int k = 4 * g + ks;
+                    const float bm = sm.Mm[16 * tk + k][16 * tj + r16];
+                    y2 = mma(sm.Gm[32 + r16][16 * tk + k], bm, y2);
+                    y3 = mma(sm.Gm[48 + r16][16 * tk + k], bm, y3);
+                }
+            }
+            f4 m2 = zero4(), m3 = zero4();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                m2 = mma(sm.Mm[32 + r16][32 + 4 * g + i], y2[i], m2);
+                m3 = mma(sm.Mm[48 + r16][32 + 4 * g + i], y2[i], m3);
+                m3 = mma(sm.Mm[48 + r16][48 + 4 * g + i], y3[i], m3);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sm.Mm[32 + 4 * g + i][16 * tj + r16] = -m2[i];
+                sm.Mm[48 + 4 * g + i][16 * tj + r16] = -m3[i];
+            }
+        }
+
+        // ---- decayed keys: KT <- Gam k (fp32), Kh^T = (Gam_b / Gam) k (fp16, tokens permuted)
+        for (int idx = tid; idx < D * 64; idx += C::NT) {
+            const int d = idx >> 6, t = idx & 63;
+            const float kv = sm.KT[d][t], cl = sm.CL[d][t];
+            sm.KT[d][t] = kv * exp2f(cl);
+            sm.Kh[d][kda_perm(t)] = (_Float16)(kv * exp2f(sm.clb[d] - cl));
+        }
+        lds_barrier();   // M complete; the last reads of Gm are above
+        // ---- Mb = M diag(b) in fp16, columns permuted (the A operand of W and U)
+        for (int idx = tid; idx < 64 * 64; idx += C::NT) {
+            const int r = idx >> 6, t = idx & 63;
+            sm.Mb[r][kda_perm(t)] = (_Float16)(sm.Mm[r][t] * sm.beta[t]);
+        }
+        lds_barrier();
+
+        // ---- W = M diag(b) Kt, stored fp16 by token rows, keys permuted: wave w forms
+        //      key columns 16w .. 16w + 15; A = M diag(b) (fp16, the chunk's Mb),
+        //      B = Kt (rows 32 sb + 4g + (e & 3) + 16 (e >> 2) of key 16w + r16)
+        {
+            const int td = w;
+            f4 acc[4];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) acc[ti] = zero4();
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                const float4 b0 = *reinterpret_cast<const float4 *>(&sm.KT[16 * td + r16][32 * sb + 4 * g]);
+                const float4 b1 = *reinterpret_cast<const float4 *>(&sm.KT[16 * td + r16][32 * sb + 16 + 4 * g]);
+                const h8 B = h8{(_Float16)b0.x, (_Float16)b0.y, (_Float16)b0.z, (_Float16)b0.w,
+                                (_Float16)b1.x, (_Float16)b1.y, (_Float16)b1.z, (_Float16)b1.w};
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) {
+                    const h8 A = *reinterpret_cast<const h8 *>(&sm.Mb[16 * ti + r16][32 * sb + 8 * g]);
+                    acc[ti] = mma(A, B, acc[ti]);
+                }
+            }
+            const int kpos = kda_perm(16 * td + r16);
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.Wh[16 * ti + 4 * g + i][kpos] = (_Float16)acc[ti][i];
+        }
+        lds_barrier();
+
+        // ---- state update of this wave's two column tiles ----------------------
+#pragma unroll
+        for (int jn = 0; jn < 2; ++jn) {
+            const int n = 2 * w + jn;
+            const bool isS = n >= MT;
+            f4 E[4];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) E[ti] = zero4();
+            if (isS) {
+                // U = M diag(b) V for the value columns of this tile: B = the raw values of
+                // column 16 (n - MT) + r16 (tokens permuted as stored) divided by 2^ev, ev the
+                // exponent of the tile's largest value in the chunk
+                const int cc = 16 * (n - MT);
+                float vb[2][8];
+                float am = 0.f;
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+                    const uint4 raw = *reinterpret_cast<const uint4 *>(&sm.VT[cc + r16][32 * sb + 8 * g]);
+                    const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        vb[sb][2 * q] = __uint_as_float(wv[q] << 16);
+                        vb[sb][2 * q + 1] = __uint_as_float(wv[q] & 0xffff0000u);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(vb[sb][e]));
+                }
+                const int ev = pow2_exponent(wave_max(am));
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+                    h8 B;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) B[e] = (_Float16)ldexpf(vb[sb][e], -ev);
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti) {
+                        const h8 A = *reinterpret_cast<const h8 *>(&sm.Mb[16 * ti + r16][32 * sb + 8 * g]);
+                        E[ti] = mma(A, B, E[ti]);
+                    }
+                }
+                // the S unit: the chunk's value scale on the first chunk (S is zero),
+                // renormalised when the values run more than 2^4 ahead of it
+                float vmax = 0.f;
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) vmax = fmaxf(vmax, fabsf(E[ti][i]));
+                svq = pow2_exponent(wave_max(vmax)) + ev;
+                if (c == 0) sig[jn] = (float)svq;
+                else if ((float)svq > sig[jn] + 4.f) renorm(jn, true, svq);
+                const int isg = (int)sig[jn] - ev;
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) E[ti][i] = ldexpf(E[ti][i], -isg);
+            }
+            // E -= W Xhat (Xhat before the chunk)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                h8 B;   // -Xhat, keys 32 kb + 4g + (e & 3) + 16 (e >> 2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    B[i] = (_Float16)(-X[2 * kb][jn][i]);
+                    B[4 + i] = (_Float16)(-X[2 * kb + 1][jn][i]);
+                }
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) {
+                    const h8 A = *reinterpret_cast<const h8 *>(&sm.Wh[16 * ti + r16][32 * kb + 8 * g]);
+                    E[ti] = mma(A, B, E[ti]);
+                }
+            }
+            h4 Eh[4];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) Eh[ti] = h4{(_Float16)E[ti][0], (_Float16)E[ti][1], (_Float16)E[ti][2], (_Float16)E[ti][3]};
+            // Xhat <- Gam_b Xhat + Kh^T E
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const float4 gq = *reinterpret_cast<const float4 *>(&sm.gamb[16 * mt + 4 * g]);
+                X[mt][jn] *= f4{gq.x, gq.y, gq.z, gq.w};
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb) {
+                    const h8 A = *reinterpret_cast<const h8 *>(&sm.Kh[16 * mt + r16][32 * jb + 8 * g]);
+                    const h8 Bv = h8{Eh[2 * jb][0], Eh[2 * jb][1], Eh[2 * jb][2], Eh[2 * jb][3],
+                                     Eh[2 * jb + 1][0], Eh[2 * jb + 1][1], Eh[2 * jb + 1][2], Eh[2 * jb + 1][3]};
+                    X[mt][jn] = mma(A, Bv, X[mt][jn]);
+                }
+            }
+        }
+        // periodic renormalisation of each tile every 4 chunks, the two tiles two chunks apart
+        if ((c & 3) == 1) renorm(0, 2 * w >= MT, svq);
+        else if ((c & 3) == 3) renorm(1, 2 * w + 1 >= MT, svq);
+    }
+
+    float *Tu = a.T_out + (int64_t)unit * D * D;
+    float *Su = a.S0_out + (int64_t)unit * D * D;
+#pragma unroll
+    for (int jn = 0; jn < 2; ++jn) {
+        const int n = 2 * w + jn;
+        const bool isS = n >= MT;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * mt + 4 * g + i;
+                const float val = ldexpf(X[mt][jn][i], (int)sig[jn]);
+                if (isS) Su[row * D + 16 * (n - MT) + r16] = val;
+                else     Tu[row * D + 16 * n + r16] = val;
+            }
+    }
+}
+
+template <int D, typename TG>
+static hipError_t launch_kda_f16_one(const DeltaArgs &a, int n_units, hipStream_t st)
+{
+    const size_t smem = sizeof(KdaHSmem<D>);
+    static std::atomic<uint64_t> lds_set{0};
+    if (hipError_t e = allow_dyn_lds(&build_kda_f16_kernel<D, TG>, smem, lds_set); e != hipSuccess) return e;
+    hipLaunchKernelGGL((build_kda_f16_kernel<D, TG>), dim3(n_units), dim3(KdaCfg<D>::NT), smem, st, a);
+    return hipGetLastError();
+}
+
 template <int D, typename TKV, typename TG>
 static hipError_t launch_kda_one(const DeltaArgs &a, int n_units, hipStream_t st)
 {
@@ -340,21 +749,25 @@ static hipError_t launch_kda_one(const DeltaArgs &a, int n_units, hipStream_t st
 }
 
 template <int D>
-static hipError_t launch_kda_d(const DeltaArgs &a, int kv_kind, int g_kind, int n_units, hipStream_t st)
+static hipError_t launch_kda_d(const DeltaArgs &a, int kv_kind, int g_kind, bool f16, int n_units, hipStream_t st)
 {
+    if constexpr (D >= 64) {
+        if (f16 && kv_kind == IN_BF16 && g_kind == IN_BF16) return launch_kda_f16_one<D, bf16_t>(a, n_units, st);
+    }
     if (kv_kind == IN_BF16 && g_kind == IN_BF16) return launch_kda_one<D, bf16_t, bf16_t>(a, n_units, st);
     if (kv_kind == IN_F32 && g_kind == IN_BF16) return launch_kda_one<D, float, bf16_t>(a, n_units, st);
     if (kv_kind == IN_F32 && g_kind == IN_F32) return launch_kda_one<D, float, float>(a, n_units, st);
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_build_kda(const DeltaArgs &a, int D, int kv_kind, int g_kind, int n_units, hipStream_t st)
+hipError_t launch_build_kda(const DeltaArgs &a, int D, int kv_kind, int g_kind, bool f16, int n_units,
+                            hipStream_t st)
 {
     switch (D) {
-    case 16: return launch_kda_d<16>(a, kv_kind, g_kind, n_units, st);
-    case 32: return launch_kda_d<32>(a, kv_kind, g_kind, n_units, st);
-    case 64: return launch_kda_d<64>(a, kv_kind, g_kind, n_units, st);
-    case 128: return launch_kda_d<128>(a, kv_kind, g_kind, n_units, st);
+    case 16: return launch_kda_d<16>(a, kv_kind, g_kind, false, n_units, st);
+    case 32: return launch_kda_d<32>(a, kv_kind, g_kind, false, n_units, st);
+    case 64: return launch_kda_d<64>(a, kv_kind, g_kind, f16, n_units, st);
+    case 128: return launch_kda_d<128>(a, kv_kind, g_kind, f16, n_units, st);
     default: return hipErrorInvalidValue;
     }
 }

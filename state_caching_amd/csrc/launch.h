@@ -114,7 +114,9 @@ hipError_t launch_build_delta_f16(const DeltaArgs &a, int D, int kv_kind, int g_
 // d = 128 with bf16 inputs (or their conv workspace): build_gdn.hip
 hipError_t launch_build_gdn(const DeltaArgs &a, int kv_kind, int g_kind, int n_units, hipStream_t st);
 // delta rule with a diagonal gate (KDA): alpha is the gate [N, h_v, D]
-hipError_t launch_build_kda(const DeltaArgs &a, int D, int kv_kind, int g_kind, int n_units, hipStream_t st);
+// f16: bf16 inputs at d >= 64 take the fp16-operand state products
+hipError_t launch_build_kda(const DeltaArgs &a, int D, int kv_kind, int g_kind, bool f16, int n_units,
+                            hipStream_t st);
 hipError_t launch_build_decay(const DecayArgs &a, int D, int in_kind, int n_units,
                               hipStream_t st);
 hipError_t launch_conv(const ConvArgs &a, int D, int in_kind, bool out_f16, int64_t total_rows,

@@ -672,7 +672,10 @@ def test_kda_build_compose(d, dtype):
     need_gpu()
     lens = [0, 1, 63, 65, 130, 200]
     wl = synth.kda(400 + d, lens, 2, 4, d, dtype, gate_div=32.0, name=f"kda-d{d}")
-    dw, T, S0 = _check_build(wl, tol=1e-5 if dtype == torch.float32 else 2e-5)
+    # bf16 inputs at d >= 64 take fp16 state products: the contract's bf16 bound;
+    # below that the fp32-product kernel holds its own much tighter figure
+    tol = 1e-5 if dtype == torch.float32 else (TOL[dtype] if d >= 64 else 2e-5)
+    dw, T, S0 = _check_build(wl, tol=tol)
     S_init = synth.random_state(401 + d, 4, d, d)
     case(f"compose kda d={d}")
     S = dw.compose(T, S0, S_init=S_init.cuda())
@@ -706,7 +709,7 @@ def test_kda_sampled_4096():
     need_gpu()
     wl = synth.kda(430, [4096, 4096], 16, 32, 128, torch.bfloat16, gate_div=256.0,
                    name="kda-gqa-2x4096")
-    _check_build(wl, segs=[1], heads=[0, 31], tol=2e-5, label="(sampled units)")
+    _check_build(wl, segs=[1], heads=[0, 31], label="(sampled units)")
 
 
 def test_kda_32k_prompt_sampled():
@@ -717,7 +720,7 @@ def test_kda_32k_prompt_sampled():
     gates of test_kda_sampled_4096 keep a non-trivial T_C at this length."""
     need_gpu()
     wl = synth.workload("kda_gqa_d128_8x4096_bf16")
-    _check_build(wl, segs=[0, 7], heads=[0, 31], tol=2e-5, label="(sampled units)")
+    _check_build(wl, segs=[0, 7], heads=[0, 31], label="(sampled units)")
 
 
 # ------------------------------------------------------------- rotary re-rotation
@@ -927,7 +930,10 @@ def test_kda_seams_compose(d, conv_w, dtype):
     eo, eo_win = _readout_errs(np64(dw.seams.o), o_or)
     print(f"  relF S {eS:.3e}, o {eo:.3e} (worst head), {eo_win:.3e} (worst window and head)")
     tol = 1e-5 if dtype == torch.float32 else 2e-3
-    assert eS <= tol and eo <= tol and eo_win <= 1e-4
+    # a single window's read-out: 1e-4 where the pairs come from fp32 products, the
+    # bf16 bound where the build took fp16 state products (bf16, no conv, d >= 64)
+    win_tol = 2e-3 if (dtype == torch.bfloat16 and conv_w == 0 and d >= 64) else 1e-4
+    assert eS <= tol and eo <= tol and eo_win <= win_tol
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
