@@ -49,6 +49,7 @@ KERNEL_SOURCES = {
     "compose_split_kernel": ["compose_split.hip", "seam.h", "common.h", "launch.h"],
     "compose_group_kernel": ["compose_group.hip", "seam.h", "common.h", "launch.h"],
     "build_kda_kernel": ["build_kda.hip", "common.h", "launch.h"],
+    "build_kda_f16_kernel": ["build_kda.hip", "common.h", "launch.h"],
     "rope_keys_kernel": ["rope.hip", "common.h", "launch.h"],
     "seam_readout_kernel": ["compose_split.hip", "seam.h", "common.h", "launch.h"],
     "build_decay_kernel": ["build_decay.hip", "common.h", "launch.h"],
@@ -586,10 +587,11 @@ def main():
                                   "8 segments x 4096, 32 value heads over 16 key heads, d = 128, bf16 "
                                   "inputs, fp32 pairs",
                       "ms_per_build": k5, "tokens_per_s": wl5.n_tokens / (k5 * 1e-3),
-                      "roofline": {"bound": "mfma", "kernel": "build_kda_kernel<128,bf16,bf16> (fp32 products)",
-                                   "achieved": ach5, "peak": PEAK_MFMA_F32, "unit": "TFLOP/s",
-                                   "frac": ach5 / PEAK_MFMA_F32,
-                                   "traffic": counter_traffic(["build_kda_kernel"], "kda_32k_prompt"),
+                      "roofline": {"bound": "mfma",
+                                   "kernel": "build_kda_f16_kernel<128,bf16> (fp16 state, W and U products)",
+                                   "achieved": ach5, "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
+                                   "frac": ach5 / PEAK_MFMA_F16,
+                                   "traffic": counter_traffic(["build_kda_f16_kernel"], "kda_32k_prompt"),
                                    "algorithmic_flop": fl5}}
         del dw5, T5, S05
         torch.cuda.empty_cache()
