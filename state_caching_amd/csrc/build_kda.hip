@@ -351,7 +351,8 @@ struct KdaHSmem {
     float CL[D][C::LDT];     // cumulative log2 gates (dim-major)
     uint16_t VT[D][LDK];     // raw bf16 values (dim-major)
     union {
-        float Gm[64][C::LDG];        // b_r L_rs for s < r, else 0
+        float bp[8][D];              // log2-gate totals of the chunk's 8-token blocks (staging)
+        float Gm[64][C::LDG];        // then b_r L_rs for s < r, else 0
         _Float16 Wh[64][LDW];        // then W (token rows, keys permuted)
     };
     float Mm[64][C::LDG];    // M = (I + Gm)^-1
@@ -429,33 +430,31 @@ __global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_f16_kernel(const De
         sig[jn] = target;
     };
 
-    constexpr int CPR = D / 8;
-    const int prow = tid / CPR, pcol = 8 * (tid % CPR);
-    constexpr int NPASS = 64 * CPR / C::NT;   // rows per thread per chunk
-    typename Raw8<bf16_t>::type kraw[NPASS], vraw[NPASS];
-    typename Raw8<TG>::type graw[NPASS];
+    // staging role: thread (dp, blk) owns key dims 2 dp, 2 dp + 1 of the 8 tokens
+    // 8 blk .. 8 blk + 7 of a chunk; a wave's loads are whole rows
+    static_assert(std::is_same<TG, bf16_t>::value, "bf16 gates");
+    constexpr int LPR = D / 2;                 // lanes per row
+    constexpr int NB = C::NT / LPR;            // token blocks per chunk
+    static_assert(NB == 8, "8 blocks of 8 tokens");
+    const int dp = tid % LPR, blk = tid / LPR;
+    uint32_t kraw[8], vraw[8], graw[8];
     float br = 0.f;
-    constexpr int PROWS = C::NT / CPR;
     auto fetch = [&](int c) {
-        const int t0 = 64 * c;
+        const int t0 = 64 * c + 8 * blk, last = len - 1;
 #pragma unroll
-        for (int p = 0; p < NPASS; ++p) {
-            const int t = t0 + prow + PROWS * p;
-            if (t < len) {
-                ld_raw8(kp + (int64_t)t * a.ldk + pcol, kraw[p]);
-                ld_raw8(vp + (int64_t)t * a.ldv + pcol, vraw[p]);
-                ld_raw8(gp + (int64_t)t * ldg + pcol, graw[p]);
-            } else {
-                zero_raw8(kraw[p]);
-                zero_raw8(vraw[p]);
-                zero_raw8(graw[p]);
-            }
+        for (int i = 0; i < 8; ++i) {
+            const int64_t t = min(t0 + i, last);
+            kraw[i] = *reinterpret_cast<const uint32_t *>(kp + t * a.ldk + 2 * dp);
+            vraw[i] = *reinterpret_cast<const uint32_t *>(vp + t * a.ldv + 2 * dp);
+            graw[i] = *reinterpret_cast<const uint32_t *>(gp + t * ldg + 2 * dp);
         }
         if (w == 0) {
-            const int t = t0 + lane;
+            const int t = 64 * c + lane;
             br = t < len ? ld1(bp + (int64_t)t * a.h_v) : 0.f;
         }
     };
+    auto lo16 = [](uint32_t x) { return __uint_as_float(x << 16); };
+    auto hi16 = [](uint32_t x) { return __uint_as_float(x & 0xffff0000u); };
 
     const int nch = (len + 63) / 64;
     if (nch > 0) fetch(0);
@@ -463,38 +462,66 @@ __global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_f16_kernel(const De
     for (int c = 0; c < nch; ++c) {
         lds_barrier();   // readers of the previous chunk are done
 
-        // ---- stage keys, values, log2 gates (dim-major), betas -------------------
+        // ---- stage keys, values (dim-major) and the in-block cumulative log2 gates;
+        //      the block totals go to LDS for the cross-block offsets
+        float cp[8][2];
         {
-            float kr[NPASS][8], vr[NPASS][8], gr[NPASS][8];
+            float kf[8][2];
+            uint32_t vw[8];
 #pragma unroll
-            for (int p = 0; p < NPASS; ++p) {
-                widen8(kraw[p], kr[p]);
-                widen8(vraw[p], vr[p]);
-                widen8(graw[p], gr[p]);
+            for (int i = 0; i < 8; ++i) {
+                const bool in = 64 * c + 8 * blk + i < len;
+                kf[i][0] = in ? lo16(kraw[i]) : 0.f;
+                kf[i][1] = in ? hi16(kraw[i]) : 0.f;
+                vw[i] = in ? vraw[i] : 0u;
+                const float l0 = in ? fmaxf(log2f(lo16(graw[i])), -126.f) : 0.f;
+                const float l1 = in ? fmaxf(log2f(hi16(graw[i])), -126.f) : 0.f;
+                cp[i][0] = i ? cp[i - 1][0] + l0 : l0;
+                cp[i][1] = i ? cp[i - 1][1] + l1 : l1;
             }
+            *reinterpret_cast<float2 *>(&sm.bp[blk][2 * dp]) = make_float2(cp[7][0], cp[7][1]);
+            // tokens 8 blk + i sit at kda_perm positions pb + i (i < 4) and pb + 8 + i - 4
+            const int pb = 32 * (blk >> 2) + 16 * (blk & 1) + 4 * ((blk >> 1) & 1);
 #pragma unroll
-            for (int p = 0; p < NPASS; ++p) {
-                const int t = prow + PROWS * p;
-                const bool in = 64 * c + t < len;
+            for (int e = 0; e < 2; ++e) {
+                float *kt = &sm.KT[2 * dp + e][8 * blk];
+                *reinterpret_cast<float4 *>(kt) = make_float4(kf[0][e], kf[1][e], kf[2][e], kf[3][e]);
+                *reinterpret_cast<float4 *>(kt + 4) = make_float4(kf[4][e], kf[5][e], kf[6][e], kf[7][e]);
+                uint32_t vv[4];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    sm.KT[pcol + e][t] = kr[p][e];
-                    sm.VT[pcol + e][kda_perm(t)] = (uint16_t)(__float_as_uint(vr[p][e]) >> 16);
-                    sm.CL[pcol + e][t] = in ? fmaxf(log2f(gr[p][e]), -126.f) : 0.f;
-                }
+                for (int q = 0; q < 4; ++q)
+                    vv[q] = e ? ((vw[2 * q] >> 16) | (vw[2 * q + 1] & 0xffff0000u))
+                              : ((vw[2 * q] & 0xffffu) | (vw[2 * q + 1] << 16));
+                *reinterpret_cast<uint2 *>(&sm.VT[2 * dp + e][pb]) = make_uint2(vv[0], vv[1]);
+                *reinterpret_cast<uint2 *>(&sm.VT[2 * dp + e][pb + 8]) = make_uint2(vv[2], vv[3]);
             }
             if (w == 0) sm.beta[lane] = br;
         }
         if (c + 1 < nch) fetch(c + 1);
         lds_barrier();
 
-        // ---- cumulative log2 gates over the chunk, per channel
-        for (int d = w; d < D; d += NW) {
-            const float cl = wave_prefix_incl(sm.CL[d][lane]);
-            sm.CL[d][lane] = cl;
-            if (lane == 63) {
-                sm.clb[d] = cl;
-                sm.gamb[d] = exp2f(cl);
+        // ---- cumulative log2 gates over the chunk: the block's own prefix plus the
+        //      totals of the earlier blocks; the chunk total per channel
+        {
+            float off0 = 0.f, off1 = 0.f;
+#pragma unroll
+            for (int b = 0; b < NB - 1; ++b) {
+                const float2 q = *reinterpret_cast<const float2 *>(&sm.bp[b][2 * dp]);
+                if (b < blk) { off0 += q.x; off1 += q.y; }
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float off = e ? off1 : off0;
+                float *cl = &sm.CL[2 * dp + e][8 * blk];
+                *reinterpret_cast<float4 *>(cl) = make_float4(off + cp[0][e], off + cp[1][e], off + cp[2][e], off + cp[3][e]);
+                *reinterpret_cast<float4 *>(cl + 4) = make_float4(off + cp[4][e], off + cp[5][e], off + cp[6][e], off + cp[7][e]);
+            }
+            if (blk == NB - 1) {
+                // the last block's last token carries the chunk total
+                sm.clb[2 * dp] = off0 + cp[7][0];
+                sm.clb[2 * dp + 1] = off1 + cp[7][1];
+                sm.gamb[2 * dp] = exp2f(off0 + cp[7][0]);
+                sm.gamb[2 * dp + 1] = exp2f(off1 + cp[7][1]);
             }
         }
         lds_barrier();
