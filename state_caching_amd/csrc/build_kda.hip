@@ -431,7 +431,10 @@ __global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_f16_kernel(const De
     };
 
     // staging role: thread (dp, blk) owns key dims 2 dp, 2 dp + 1 of the 8 tokens
-    // 8 blk .. 8 blk + 7 of a chunk; a wave's loads are whole rows
+    // 8 blk .. 8 blk + 7 of a chunk; a wave's loads are whole rows.
+    // log2 and exp2 below are the hardware instructions: log-gates are clamped at
+    // -126 anyway, and a decay factor below 2^-126 flushes to zero (its term is
+    // below the fp32 range of the chunk's own contributions)
     static_assert(std::is_same<TG, bf16_t>::value, "bf16 gates");
     constexpr int LPR = D / 2;                 // lanes per row
     constexpr int NB = C::NT / LPR;            // token blocks per chunk
@@ -474,8 +477,8 @@ __global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_f16_kernel(const De
                 kf[i][0] = in ? lo16(kraw[i]) : 0.f;
                 kf[i][1] = in ? hi16(kraw[i]) : 0.f;
                 vw[i] = in ? vraw[i] : 0u;
-                const float l0 = in ? fmaxf(log2f(lo16(graw[i])), -126.f) : 0.f;
-                const float l1 = in ? fmaxf(log2f(hi16(graw[i])), -126.f) : 0.f;
+                const float l0 = in ? fmaxf(__builtin_amdgcn_logf(lo16(graw[i])), -126.f) : 0.f;
+                const float l1 = in ? fmaxf(__builtin_amdgcn_logf(hi16(graw[i])), -126.f) : 0.f;
                 cp[i][0] = i ? cp[i - 1][0] + l0 : l0;
                 cp[i][1] = i ? cp[i - 1][1] + l1 : l1;
             }
@@ -520,8 +523,8 @@ __global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_f16_kernel(const De
                 // the last block's last token carries the chunk total
                 sm.clb[2 * dp] = off0 + cp[7][0];
                 sm.clb[2 * dp + 1] = off1 + cp[7][1];
-                sm.gamb[2 * dp] = exp2f(off0 + cp[7][0]);
-                sm.gamb[2 * dp + 1] = exp2f(off1 + cp[7][1]);
+                sm.gamb[2 * dp] = __builtin_amdgcn_exp2f(off0 + cp[7][0]);
+                sm.gamb[2 * dp + 1] = __builtin_amdgcn_exp2f(off1 + cp[7][1]);
             }
         }
         lds_barrier();
@@ -535,8 +538,8 @@ __global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_f16_kernel(const De
             for (int ks = 0; ks < D / 4; ++ks) {
                 const int k = g * (D / 4) + ks;
                 const float cr = sm.CL[k][ref];
-                const float A = sm.KT[k][16 * ti + r16] * exp2f(sm.CL[k][16 * ti + r16] - cr);
-                const float B = sm.KT[k][16 * tj + r16] * exp2f(cr - sm.CL[k][16 * tj + r16]);
+                const float A = sm.KT[k][16 * ti + r16] * __builtin_amdgcn_exp2f(sm.CL[k][16 * ti + r16] - cr);
+                const float B = sm.KT[k][16 * tj + r16] * __builtin_amdgcn_exp2f(cr - sm.CL[k][16 * tj + r16]);
                 acc = mma(A, B, acc);
             }
 #pragma unroll
@@ -606,8 +609,8 @@ __global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_f16_kernel(const De
         for (int idx = tid; idx < D * 64; idx += C::NT) {
             const int d = idx >> 6, t = idx & 63;
             const float kv = sm.KT[d][t], cl = sm.CL[d][t];
-            sm.KT[d][t] = kv * exp2f(cl);
-            sm.Kh[d][kda_perm(t)] = (_Float16)(kv * exp2f(sm.clb[d] - cl));
+            sm.KT[d][t] = kv * __builtin_amdgcn_exp2f(cl);
+            sm.Kh[d][kda_perm(t)] = (_Float16)(kv * __builtin_amdgcn_exp2f(sm.clb[d] - cl));
         }
         lds_barrier();   // M complete; the last reads of Gm are above
         // ---- Mb = M diag(b) in fp16, columns permuted (the A operand of W and U)
