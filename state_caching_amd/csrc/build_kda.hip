@@ -605,12 +605,24 @@ __global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_f16_kernel(const De
             }
         }
 
-        // ---- decayed keys: KT <- Gam k (fp32), Kh^T = (Gam_b / Gam) k (fp16, tokens permuted)
-        for (int idx = tid; idx < D * 64; idx += C::NT) {
-            const int d = idx >> 6, t = idx & 63;
-            const float kv = sm.KT[d][t], cl = sm.CL[d][t];
-            sm.KT[d][t] = kv * __builtin_amdgcn_exp2f(cl);
-            sm.Kh[d][kda_perm(t)] = (_Float16)(kv * __builtin_amdgcn_exp2f(sm.clb[d] - cl));
+        // ---- decayed keys: KT <- Gam k (fp32), Kh^T = (Gam_b / Gam) k (fp16, tokens
+        //      permuted), 4 tokens per step (kda_perm keeps runs of 4), by waves 2 ..
+        //      while waves 0 and 1 finish the inverse above
+        if (w >= 2) {
+            for (int u = tid - 128; u < D * 16; u += C::NT - 128) {
+                const int d = u >> 4, t4 = 4 * (u & 15);
+                const float4 kv = *reinterpret_cast<const float4 *>(&sm.KT[d][t4]);
+                const float4 cl = *reinterpret_cast<const float4 *>(&sm.CL[d][t4]);
+                const float cb = sm.clb[d];
+                *reinterpret_cast<float4 *>(&sm.KT[d][t4]) =
+                    make_float4(kv.x * __builtin_amdgcn_exp2f(cl.x), kv.y * __builtin_amdgcn_exp2f(cl.y),
+                                kv.z * __builtin_amdgcn_exp2f(cl.z), kv.w * __builtin_amdgcn_exp2f(cl.w));
+                const h4 kh = h4{(_Float16)(kv.x * __builtin_amdgcn_exp2f(cb - cl.x)),
+                                 (_Float16)(kv.y * __builtin_amdgcn_exp2f(cb - cl.y)),
+                                 (_Float16)(kv.z * __builtin_amdgcn_exp2f(cb - cl.z)),
+                                 (_Float16)(kv.w * __builtin_amdgcn_exp2f(cb - cl.w))};
+                *reinterpret_cast<h4 *>(&sm.Kh[d][kda_perm(t4)]) = kh;
+            }
         }
         lds_barrier();   // M complete; the last reads of Gm are above
         // ---- Mb = M diag(b) in fp16, columns permuted (the A operand of W and U)
