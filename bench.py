@@ -53,6 +53,7 @@ KERNEL_SOURCES = {
     "rope_keys_kernel": ["rope.hip", "common.h", "launch.h"],
     "seam_readout_kernel": ["compose_split.hip", "seam.h", "common.h", "launch.h"],
     "build_decay_kernel": ["build_decay.hip", "common.h", "launch.h"],
+    "build_decay_bf16_kernel": ["build_decay.hip", "common.h", "launch.h"],
 }
 
 
@@ -458,10 +459,10 @@ def decay_leg(args, torch, dev, out):
                               "fp32 pairs (diagonal T_C)",
                   "ms_per_build": k2, "ms_min_max": [k2_all[0], k2_all[-1]],
                   "tokens_per_s": wl2.n_tokens / (k2 * 1e-3),
-                  "roofline": {"bound": "hbm", "kernel": "build_decay_kernel<128,diag,bf16>",
+                  "roofline": {"bound": "hbm", "kernel": "build_decay_bf16_kernel<128,diag>",
                                "achieved": by2 / (k2 * 1e-3) / 1e9, "peak": PEAK_HBM, "unit": "GB/s",
                                "frac": by2 / (k2 * 1e-3) / 1e9 / PEAK_HBM,
-                               "traffic": counter_traffic(["build_decay_kernel"], "gla_8x512"),
+                               "traffic": counter_traffic(["build_decay_bf16_kernel"], "gla_8x512"),
                                "algorithmic_bytes": by2, "algorithmic_flop": fl2}}
     del dw2, T2, S2
     # RetNet, scalar decay per head, and the naive sum
