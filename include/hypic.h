@@ -28,7 +28,7 @@
  *   DELTA + SCALAR     : T_i = a_i(I - b_i k_i k_i^T), u_i = b_i k_i v_i^T
  *                        (GDN; DeltaNet is a_i = 1)                           T_C dense
  *   DELTA + DIAG       : T_i = (I - b_i k_i k_i^T) diag(g_i), u_i = b_i k_i v_i^T
- *                        (KDA; fp32 matrix products for every input dtype)    T_C dense
+ *                        (KDA)                                                T_C dense
  *
  * Conventions shared by every call
  *   - Every data pointer is a DEVICE pointer owned by the caller; arrays are
@@ -48,11 +48,16 @@
  *     return HYPIC_E_UNSUPPORTED.  Pointers must be 16-byte aligned.
  *   - States, transitions and pair pools are fp32.  Inputs are fp32 or bf16.
  *     Precision: fp32 inputs are computed with fp32 matrix products (relative
- *     Frobenius error ~1e-6); bf16 inputs use fp16 matrix-core operands with
- *     fp32 accumulation and power-of-two block scaling (~3e-4 on S, <=1.5e-3 on
- *     dense T_C for 4096-token segments).  Gated-delta segments longer than
- *     4096 tokens are built with fp32 products whatever the input dtype (the
- *     fp16 rounding of every 64-token chunk would add up past 2e-3 on T_C).
+ *     Frobenius error ~1e-6).  bf16 inputs of the delta rule (scalar gate, and
+ *     per-channel gate at d >= 64) use fp16 matrix-core operands with fp32
+ *     accumulation and power-of-two block scaling (~3e-4 on S, <=1.7e-3 on
+ *     dense T_C for 4096-token segments; the per-channel gate's Gram matrix and
+ *     triangular inverse stay fp32); delta-rule segments longer than 4096
+ *     tokens are built with fp32 products whatever the input dtype (the fp16
+ *     rounding of every 64-token chunk would add up past 2e-3 on T_C).  bf16
+ *     inputs of the decay family take bf16 hi + lo key products against the
+ *     exact bf16 values (~1e-5); decay factors below 2^-126 of a chunk's own
+ *     contributions flush to zero.
  *   - Delta rule keys enter the matrix products as given: they are meant to be
  *     L2-normalised (k_l2norm = 1, or by the caller), with b_t |k_t|^2 <= 2 so
  *     that no transition expands.  With bf16 inputs the keys, b and the solved
