@@ -56,7 +56,7 @@
  *     tokens are built with fp32 products whatever the input dtype (the fp16
  *     rounding of every 64-token chunk would add up past 2e-3 on T_C).  bf16
  *     inputs of the decay family take bf16 hi + lo key products against the
- *     exact bf16 values (~1e-5); decay factors below 2^-126 of a chunk's own
+ *     exact bf16 values (<= 5e-6 in the tests); factors below 2^-126 of a chunk's own
  *     contributions flush to zero.
  *   - Delta rule keys enter the matrix products as given: they are meant to be
  *     L2-normalised (k_l2norm = 1, or by the caller), with b_t |k_t|^2 <= 2 so
