@@ -302,28 +302,35 @@ build_decay_bf16_kernel(const DecayArgs a)
     // row, and its tokens are masked), so every fetch is unconditional; the loads
     // are issued in one fixed order on every path (scheduling fences), so the
     // compiler's load-counter waits stay exact across the loop
+    // Addresses: a 64-bit base per chunk plus 32-bit row offsets inside it (a
+    // clamped row lies at most a few chunks behind the base), so segments of any
+    // length stay addressable.
     auto fetch = [&](int c, Buf &b) {
-        const int last = len - 1, t0 = 64 * c + TPB * blk;
+        const int last = len - 1 - 64 * c, t0 = TPB * blk;   // rows relative to the chunk
+        const int64_t cb = (int64_t)(64 * c);
+        const uint16_t *kc = kp + cb * ldk, *vc = vp + cb * ldv + vcol;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < TPB; ++i) {
-            b.k[i] = *reinterpret_cast<const uint32_t *>(kp + (unsigned)min(t0 + i, last) * ldk);
+            b.k[i] = *reinterpret_cast<const uint32_t *>(kc + min(t0 + i, last) * (int)ldk);
             __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (DIAG) {
+            const uint16_t *gc = gp + cb * ldg;
 #pragma unroll
             for (int i = 0; i < TPB; ++i) {
-                b.g[i] = *reinterpret_cast<const uint32_t *>(gp + (unsigned)min(t0 + i, last) * ldg);
+                b.g[i] = *reinterpret_cast<const uint32_t *>(gc + min(t0 + i, last) * (int)ldg);
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else if constexpr (GK == HYPIC_GATE_SCALAR) {
+            const uint16_t *gc = gp + cb * ldg;
 #pragma unroll
             for (int i = 0; i < TPB; ++i) {
-                b.gs[i] = gp[(unsigned)min(t0 + i, last) * ldg];
+                b.gs[i] = gc[min(t0 + i, last) * (int)ldg];
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        b.v = *reinterpret_cast<const db_u4 *>(vp + vcol + (unsigned)min(64 * c + vrow, last) * ldv);
+        b.v = *reinterpret_cast<const db_u4 *>(vc + min(vrow, last) * (int)ldv);
         __builtin_amdgcn_sched_barrier(0);
     };
     auto lo16 = [](uint32_t x) { return __uint_as_float(x << 16); };
