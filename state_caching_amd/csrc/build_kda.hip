@@ -396,13 +396,15 @@ __global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_f16_kernel(const De
         if ((c >> 4) > (r >> 4)) sm.Mm[r][c] = 0.f;
     }
 
-    // X = [T | S] in power-of-two units: X[mt][jn] holds rows 16 mt .., column tile 2w + jn
+    // X = [T | S] in power-of-two units: X[mt][jn] holds rows 16 mt .. of column tile
+    // n = w (jn = 0, a T tile) or MT + w (jn = 1, an S tile): every wave carries one
+    // of each, so the value products of the S tiles spread over all waves
     f4 X[MT][2];
     float sig[2] = {0.f, 0.f};
     int svq = 0;   // value exponent of the last chunk (S tile waves)
 #pragma unroll
     for (int jn = 0; jn < 2; ++jn) {
-        const int n = 2 * w + jn;
+        const int n = jn ? MT + w : w;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -663,7 +665,7 @@ __global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_f16_kernel(const De
         // ---- state update of this wave's two column tiles ----------------------
 #pragma unroll
         for (int jn = 0; jn < 2; ++jn) {
-            const int n = 2 * w + jn;
+            const int n = jn ? MT + w : w;
             const bool isS = n >= MT;
             f4 E[4];
 #pragma unroll
@@ -748,15 +750,15 @@ __global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_f16_kernel(const De
             }
         }
         // periodic renormalisation of each tile every 4 chunks, the two tiles two chunks apart
-        if ((c & 3) == 1) renorm(0, 2 * w >= MT, svq);
-        else if ((c & 3) == 3) renorm(1, 2 * w + 1 >= MT, svq);
+        if ((c & 3) == 1) renorm(0, false, svq);
+        else if ((c & 3) == 3) renorm(1, true, svq);
     }
 
     float *Tu = a.T_out + (int64_t)unit * D * D;
     float *Su = a.S0_out + (int64_t)unit * D * D;
 #pragma unroll
     for (int jn = 0; jn < 2; ++jn) {
-        const int n = 2 * w + jn;
+        const int n = jn ? MT + w : w;
         const bool isS = n >= MT;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
