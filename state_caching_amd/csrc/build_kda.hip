@@ -470,12 +470,15 @@ __global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_f16_kernel(const De
         // ---- stage keys, values (dim-major) and the in-block cumulative log2 gates;
         //      the block totals go to LDS for the cross-block offsets
         float cp[8][2];
-        {
+        // MK: the chunk runs past the segment end (rows beyond it stage as zero keys
+        // and values and gate 1); a full chunk takes no masks
+        auto stage = [&](auto mk) {
+            constexpr bool MK = decltype(mk)::value;
             float kf[8][2];
             uint32_t vw[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const bool in = 64 * c + 8 * blk + i < len;
+                const bool in = !MK || 64 * c + 8 * blk + i < len;
                 kf[i][0] = in ? lo16(kraw[i]) : 0.f;
                 kf[i][1] = in ? hi16(kraw[i]) : 0.f;
                 vw[i] = in ? vraw[i] : 0u;
@@ -501,7 +504,9 @@ __global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_f16_kernel(const De
                 *reinterpret_cast<uint2 *>(&sm.VT[2 * dp + e][pb + 8]) = make_uint2(vv[2], vv[3]);
             }
             if (w == 0) sm.beta[lane] = br;
-        }
+        };
+        if (64 * (c + 1) <= len) stage(std::false_type{});
+        else stage(std::true_type{});
         if (c + 1 < nch) fetch(c + 1);
         lds_barrier();
 
