@@ -139,11 +139,12 @@ def test_decay_shapes_ragged(d, kind, dtype):
     _check_build(wl, label=f"d={d}")
 
 
-def test_mamba2_scalar_gate():
+@pytest.mark.parametrize("d", [64, 128])
+def test_mamba2_scalar_gate(d):
     """Per-token scalar gate with the decay rule (Mamba2 form)."""
     need_gpu()
     import dataclasses
-    base = synth.gdn(50, [100, 77], 2, 2, 64, torch.bfloat16, alpha_div=8.0)
+    base = synth.gdn(50, [100, 77], 2, 2, d, torch.bfloat16, alpha_div=8.0)
     wl = dataclasses.replace(base, rule="decay", beta=None, name="mamba2-like")
     _check_build(wl)
 
