@@ -19,23 +19,30 @@
 // (keys, values, G's lower blocks, the M'_ii) is ready a pipeline step ahead,
 // so one barrier per chunk suffices.
 //
+// The substitution runs over two 32-row blocks: M'_00 and M'_11 are the
+// inverses of the two 32 x 32 diagonal blocks (times diag(b)), each assembled
+// from two 16-row inverses as [[M'_a, 0], [-M'_b G_ba M'_a, M'_b]], and G_10 is
+// the 32 x 32 block of G below the diagonal, so
+//   E_0 = M'_00 P_0,   E_1 = M'_11 (P_1 - G_10 E_0).
+//
 // One workgroup of 8 waves per (segment, value head), two per SIMD: a state
 // wave and a prep wave.  Between two barriers:
-//   state waves 0-3  state(j-2): wave w owns column tiles 2w, 2w + 1 of Tbar and
-//                    of S (fp32 in matrix-core accumulators): P (one half of its
-//                    columns at a time; the value term scaled from the raw rows
-//                    here), the block substitution for E, and X += K^T E
+//   state waves 0-3  state(j-2): wave w owns the 32-column tile w of Tbar and
+//                    of S (fp32 in matrix-core accumulators, 32 x 32 x 16
+//                    products): P (one tile at a time; the value term scaled
+//                    from the raw rows here), the two-block substitution for E,
+//                    and X += K^T E
 //   prep waves 4-7   chunk j: the raw value rows (prefetched into registers) to LDS;
 //                    gates; 16 key rows per wave converted to fp16.  Chunk j-1:
-//                    the transposed key copy; the Gram tiles below the diagonal
-//                    (negated; waves 5-7) and, on wave 4, all four diagonal
-//                    blocks' inverses (one block per lane row, the multipliers
-//                    broadcast across the row by lane moves) and the M'_ii
-// The two key operands reach the matrix cores through 16-byte LDS reads (twice
-// the bandwidth of 8-byte and transposing reads): keys are stored with their
-// order permuted inside each 32-key block so that one read yields the
-// reduction order of the accumulator layout, and the transposed key copy
-// permutes tokens the same way.
+//                    the transposed key copy; the four Gram tiles of G_10
+//                    (negated; waves 5 and 6) and, on wave 4, the four 16-row
+//                    diagonal inverses (one block per lane row, the multipliers
+//                    broadcast across the row by lane moves), the M'_ii and the
+//                    blocks -M'_b G_ba M'_a that join them into 32-row inverses
+// Every matrix-core operand reaches the products through 16-byte LDS reads:
+// keys are stored with their order permuted inside each 16-key block, and the
+// transposed key copy and the M tiles permute tokens the same way, so that one
+// read yields the reduction order of the 32 x 32 accumulator layout.
 // X is kept in power-of-two units per column tile (renormalised every 4
 // chunks, or when a chunk's values run ahead of the S unit), so every fp16
 // operand stays in range.
@@ -50,23 +57,25 @@ namespace {
 constexpr int GD = 128;          // d_k = d_v
 constexpr int GLK = GD + 8;      // Ks row stride (halves)
 constexpr int GLT = 64 + 8;      // KT row stride (halves)
-constexpr int GLP = 72;          // Mx row stride (halves)
+constexpr int GLM = 32 + 8;      // Mx row stride (halves)
 constexpr int GLG = 20;          // Gd row stride (floats)
 
-// Storage order inside a 32-wide block: position 8a + e holds index
-// 4a + (e & 3) + 16 (e >> 2), so the 8 halves at 8a are the accumulator
-// layout's reduction indices 4a + {0..3} and 16 + 4a + {0..3}.
-__device__ __forceinline__ int perm32_index(int pos) { return 4 * ((pos & 31) >> 3) + (pos & 3) + 16 * ((pos >> 2) & 1) + (pos & ~31); }
-// position of the four indices 4b .. 4b + 3 (b = 0..7 inside the block)
-__device__ __forceinline__ int perm32_pos4(int idx) { return (idx & ~31) + 8 * ((idx & 15) >> 2) + 4 * ((idx >> 4) & 1); }
+// Storage order inside a 16-wide block: position 8a + e holds index
+// 4a + (e & 3) + 8 (e >> 2), so the 8 halves at 8a are the reduction indices
+// that lane half a holds in the 32 x 32 accumulator layout, 4a + {0..3} and
+// 8 + 4a + {0..3}.
+__device__ __forceinline__ int perm16_index(int pos) { return (pos & ~15) + 4 * ((pos >> 3) & 1) + (pos & 3) + 8 * ((pos >> 2) & 1); }
+// position of index idx; the four indices 4b .. 4b + 3 stay contiguous
+__device__ __forceinline__ int perm16_pos(int idx) { return (idx & ~15) + 8 * ((idx >> 2) & 1) + 4 * ((idx >> 3) & 1) + (idx & 3); }
 
 struct GdnSmem {
-    _Float16 Ks[3][64][GLK];     // keys, token-major, key order permuted per 32-key block
-    _Float16 KT[2][GD][GLT];     // keys transposed (key-major), token order permuted per 32 tokens
+    _Float16 Ks[3][64][GLK];     // keys, token-major, key order permuted per 16-key block
+    _Float16 KT[2][GD][GLT];     // keys transposed (key-major), token order permuted per 16 tokens
     unsigned short Vr[3][64][GD];   // raw value rows as stored (bf16 or fp16 bits); the 16-byte
                                     // piece p of row t sits at piece position p ^ (2 (t & 7))
-    _Float16 Mx[2][64][GLP];     // per chunk slot: -G_ij in the blocks below the diagonal,
-                                 // M'_ii on the diagonal blocks (upper blocks unused)
+    _Float16 Mx[2][3][32][GLM];  // per chunk slot: M'_00, M'_11 and -G_10 (32 x 32 each, token
+                                 // columns permuted per 16; the upper right 16 x 16 blocks of the
+                                 // two inverses stay zero)
     float Gd[4][16][GLG];        // the four diagonal Gram blocks (inverting wave's scratch)
     float beta[3][64];           // b_t per slot
     float fac[3][64];            // value row factor dec_t (times the row scale of the conv
@@ -89,6 +98,18 @@ __device__ __forceinline__ h4 tr4(const _Float16 *S, int ld, int k0, int x0, int
 }
 __device__ __forceinline__ h8 cat8(h4 lo, h4 hi) { return h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}; }
 __device__ __forceinline__ h4 cvt4(f4 v) { return h4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]}; }
+typedef float f16v __attribute__((ext_vector_type(16)));
+// registers o .. o + 7 of a 32 x 32 accumulator tile as an fp16 operand
+__device__ __forceinline__ h8 cvt8(const f16v &v, int o)
+{
+    h8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (_Float16)v[o + e];
+    return r;
+}
+// 32x32x16 product: lane holds A[l%32][8(l/32) + e], B[8(l/32) + e][l%32]; the
+// result register i is row 8 (i >> 2) + 4 (l/32) + (i & 3), column l%32
+__device__ __forceinline__ f16v mma32(h8 a, h8 b, f16v c) { return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0); }
 // 16x16x16 product: lane holds A[l%16][4(l/16) + e], B[4(l/16) + e][l%16]
 __device__ __forceinline__ f4 mma16(h4 a, h4 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0); }
 // LDS addressing for the per-chunk state loop: one base register per operand
@@ -170,11 +191,6 @@ __device__ __forceinline__ void subst_steps(float (&x)[16], const float (&n)[16]
     if constexpr (Q < 14) subst_steps<Q + 1>(x, n);
 }
 
-// the off-diagonal Gram tiles (row block, column block) of prep wave p = 1..3,
-// two each: index 2 (p - 1) + q into (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
-__device__ __forceinline__ int gram_ti(int idx) { return (0x333221u >> (4 * idx)) & 15; }
-__device__ __forceinline__ int gram_tj(int idx) { return (0x210100u >> (4 * idx)) & 15; }
-
 static_assert(sizeof(GdnSmem) <= 160 * 1024, "the build's LDS exceeds a workgroup's 160 KiB");
 
 }  // namespace
@@ -193,13 +209,25 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
     const int len = a.len[s];
     const int nch = (len + 63) / 64;
 
+    // the upper right 16 x 16 blocks of the two 32-row inverses are never written:
+    // zero all M tiles once (the roles' first barrier orders this)
+    {
+        uint32_t *mz = reinterpret_cast<uint32_t *>(&sm.Mx[0][0][0][0]);
+        for (int i = tid; i < (int)(sizeof(sm.Mx) / 4); i += 512) mz[i] = 0u;
+    }
     // The two roles keep their registers apart: every variable, lambda and loop
     // of a role lives inside its branch.  Both roles meet the same nch + 3 barriers.
     if (w >= 4) {
         // ------------------------------------------------------------ staging
-        // prep lane (g, r16) stages key rows 16 pw + 4g + q (q = 0..3), columns 8 r16 .. 8 r16 + 7
+        // Prep waves 1-3 stage the chunk: wave 1 rows 0-23, wave 2 rows 24-47, wave 3
+        // rows 48-63 and the gates (wave 0 inverts and stages nothing).  Lane (g, r16)
+        // stages key rows rbase + nr g + q (q < nr), columns 8 r16 .. 8 r16 + 7, and value
+        // rows rbase + 4i + g (i < nr).
+        constexpr int MR = 6;
         const int pw = w - 4;
-        const int row0 = 16 * pw + 4 * g;
+        const int nr = pw == 3 ? 4 : MR;
+        const int rbase = pw == 1 ? 0 : pw == 2 ? 24 : 48;
+        const int row0 = rbase + nr * g;
         // uniform row bases of the segment (64-bit) plus per-lane offsets inside a
         // chunk (32-bit: a chunk spans 64 rows)
         const TK *kb = reinterpret_cast<const TK *>(a.k) + a.tok0[s] * a.ldk + (int64_t)kh * GD;
@@ -214,8 +242,8 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
         // double-buffered.  The value rows pass through registers rather than a direct
         // memory-to-LDS load: the compiler orders every later LDS read of the wave
         // behind such a load, which would expose the prefetch's memory latency.
-        typename Raw8<TK>::type kraw[2][4];
-        uint4 vraw[2][4];
+        typename Raw8<TK>::type kraw[2][MR];
+        uint4 vraw[2][MR];
         TG braw[2], araw[2];
         float vrs[2];
         auto fetch = [&](int c, auto pc) {
@@ -223,52 +251,57 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
             const int last = len - 1 - 64 * c;   // >= 0 for every chunk of the segment
             const TK *kc = kb + (int64_t)(64 * c) * a.ldk;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                ld_raw8(kc + (__umul24(min(row0 + q, last), (unsigned)a.ldk) + 8 * r16), kraw[P][q]);
-            const uint32_t go = __umul24(min(lane, last), (unsigned)a.h_v);
-            const int64_t gc = (int64_t)(64 * c) * a.h_v;
-            braw[P] = bp[gc + go];
-            araw[P] = ap[gc + go];
-            if constexpr (VSC) vrs[P] = vsp[gc + go];
-            else vrs[P] = 1.f;
-            // raw value rows 16 pw + 4i + g, the 16-byte piece r16 ^ 2 (t & 7) of row t
+            for (int q = 0; q < MR; ++q)
+                if (q < nr) ld_raw8(kc + (__umul24(min(row0 + q, last), (unsigned)a.ldk) + 8 * r16), kraw[P][q]);
+            if (pw == 3) {   // the gate wave
+                const uint32_t go = __umul24(min(lane, last), (unsigned)a.h_v);
+                const int64_t gc = (int64_t)(64 * c) * a.h_v;
+                braw[P] = bp[gc + go];
+                araw[P] = ap[gc + go];
+                if constexpr (VSC) vrs[P] = vsp[gc + go];
+                else vrs[P] = 1.f;
+            }
+            // raw value rows rbase + 4i + g, the 16-byte piece r16 ^ 2 (t & 7) of row t
             // (rows past the segment end repeat its last row; their factor is 0)
             const unsigned char *vc = vb + (int64_t)(64 * c) * ldv_b;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * pw + 4 * i + g;
+            for (int i = 0; i < MR; ++i) {
+                const int t = rbase + 4 * i + g;
                 const uint32_t off = (uint32_t)min(t, last) * ldv_b + 16 * (r16 ^ (2 * (t & 7)));
-                vraw[P][i] = *reinterpret_cast<const uint4 *>(vc + off);
+                if (i < nr) vraw[P][i] = *reinterpret_cast<const uint4 *>(vc + off);
             }
         };
 
         double cl_lane = 0.0;
-        // chunk c into slot c % 3 from prefetch buffer P: gates (every prep wave computes
-        // all 64 and writes the same values) and this wave's 16 key rows.  TAIL: the
-        // segment's last chunk, whose rows past the end read as zero.
+        // chunk c into slot c % 3 from prefetch buffer P: gates (prep wave 3 alone) and this
+        // wave's 16 key rows.  TAIL: the segment's last chunk, whose rows past the end read
+        // as zero.
         auto stage = [&](int c, auto pc, auto tail) {
             constexpr int P = decltype(pc)::value;
             const int sl = c % 3;
-            const bool gin = 64 * c + lane < len;
-            const float br = gin ? to_f32(braw[P]) : 0.f, ar = gin ? to_f32(araw[P]) : 1.f;
-            const float l2 = log2f(ar);
-            const float sfx = wave_suffix_excl(l2);   // log2 dec_t
-            cl_lane += (double)l2;
-            sm.beta[sl][lane] = br;
-            sm.fac[sl][lane] = gin ? exp2f(sfx) * vrs[P] : 0.f;
-            sm.gb[sl] = exp2f(lane_f(sfx + l2, 0));
-            // value rows into slot sl: row 16 pw + 4i + g, piece position r16
+            if (pw == 3) {
+                const bool gin = 64 * c + lane < len;
+                const float br = gin ? to_f32(braw[P]) : 0.f, ar = gin ? to_f32(araw[P]) : 1.f;
+                const float l2 = log2f(ar);
+                const float sfx = wave_suffix_excl(l2);   // log2 dec_t
+                cl_lane += (double)l2;
+                sm.beta[sl][lane] = br;
+                sm.fac[sl][lane] = gin ? exp2f(sfx) * vrs[P] : 0.f;
+                sm.gb[sl] = exp2f(lane_f(sfx + l2, 0));
+            }
+            // value rows into slot sl: row rbase + 4i + g, piece position r16
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<uint4 *>(&sm.Vr[sl][16 * pw + 4 * i + g][8 * r16]) = vraw[P][i];
+            for (int i = 0; i < MR; ++i)
+                if (i < nr) *reinterpret_cast<uint4 *>(&sm.Vr[sl][rbase + 4 * i + g][8 * r16]) = vraw[P][i];
             if constexpr (decltype(tail)::value) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) mask_raw8(kraw[P][q], 64 * c + row0 + q < len);
+                for (int q = 0; q < MR; ++q) mask_raw8(kraw[P][q], 64 * c + row0 + q < len);
             }
             // keys 8 r16 .. 8 r16 + 7 = two runs of four, stored at their permuted positions
-            const int kpos = perm32_pos4(8 * r16);
+            const int kpos0 = perm16_pos(8 * r16), kpos1 = perm16_pos(8 * r16 + 4);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < MR; ++q) {
+                if (q >= nr) break;
                 float kx[8];
                 widen8(kraw[P][q], kx);
                 h4 k0, k1;
@@ -277,24 +310,25 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
                     k0[e] = (_Float16)kx[e];
                     k1[e] = (_Float16)kx[4 + e];
                 }
-                *reinterpret_cast<h4 *>(&sm.Ks[sl][row0 + q][kpos]) = k0;
-                *reinterpret_cast<h4 *>(&sm.Ks[sl][row0 + q][kpos + 8]) = k1;
+                *reinterpret_cast<h4 *>(&sm.Ks[sl][row0 + q][kpos0]) = k0;
+                *reinterpret_cast<h4 *>(&sm.Ks[sl][row0 + q][kpos1]) = k1;
             }
         };
-        // keys of chunk c transposed into KT slot c & 1, by prep waves 1-3 (key blocks
-        // xb = 3 (p - 1) .. , all 64 tokens): a transposing read gives lane (g, r16)
-        // tokens 16 tb + 4g .. + 3 of stored key column 16 xb + r16, written as one run at
-        // the tokens' permuted position
+        // keys of chunk c transposed into KT slot c & 1, by prep waves 1-3 (16-key blocks
+        // 0-3 on wave 3, 4-5 on wave 1, 6-7 on wave 2; all 64 tokens): a transposing read
+        // gives lane (g, r16) tokens 16 tb + 4g .. + 3 of stored key column 16 xb + r16,
+        // written as one run at the tokens' permuted position
         auto store_kt = [&](int c) {
             const int sl = c % 3, s2 = c & 1;
+            const int nb = pw == 3 ? 4 : 2, xb0 = pw == 3 ? 0 : 2 + 2 * pw;
 #pragma unroll
-            for (int i = 0; i < 3; ++i) {
-                const int xb = 3 * (pw - 1) + i;
-                if (xb < 8) {
+            for (int i = 0; i < 4; ++i) {
+                if (i < nb) {
+                    const int xb = xb0 + i;
 #pragma unroll
                     for (int tb = 0; tb < 4; ++tb) {
                         const h4 v = tr4(&sm.Ks[sl][0][0], GLK, 16 * tb + 4 * g, 16 * xb, lane);
-                        *reinterpret_cast<h4 *>(&sm.KT[s2][perm32_index(16 * xb + r16)][perm32_pos4(16 * tb + 4 * g)]) = v;
+                        *reinterpret_cast<h4 *>(&sm.KT[s2][16 * xb + perm16_index(r16)][16 * tb + perm16_pos(4 * g)]) = v;
                     }
                 }
             }
@@ -313,22 +347,26 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
             }
             return acc;
         };
-        // chunk c, prep waves 1-3: two off-diagonal Gram tiles each, negated, into Mx
+        // chunk c, prep waves 1 and 2: the Gram tiles (1 + pw, 0) and (1 + pw, 1) of the
+        // 16-row blocks, negated, into the -G_10 tile of the chunk's Mx slot
         auto prep_offgram = [&](int c) {
             const int ms = c & 1, sl = c % 3;
+            const int ti = 1 + pw;
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int idx = 2 * (pw - 1) + q, ti = gram_ti(idx), tj = gram_tj(idx);
+            for (int tj = 0; tj < 2; ++tj) {
                 const f4 acc = gram_tile(sl, ti, tj);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sm.Mx[ms][16 * ti + 4 * g + i][16 * tj + r16] = (_Float16)(-acc[i]);
+                for (int i = 0; i < 4; ++i)
+                    sm.Mx[ms][2][16 * (ti - 2) + 4 * g + i][16 * tj + perm16_pos(r16)] = (_Float16)(-acc[i]);
             }
         };
-        // chunk c, prep wave 0: the four diagonal blocks.  Their Gram tiles go through
-        // LDS so that lane row g holds block g with one column per lane (G is
+        // chunk c, prep wave 0: the four 16-row diagonal blocks.  Their Gram tiles go
+        // through LDS so that lane row g holds block g with one column per lane (G is
         // symmetric); the inverse of I + A'_gg (A' = diag(b) strictlower(G)) follows by
         // forward substitution, x_r += (-A'[r][q]) x_q, the multiplier taken from lane
-        // q of the row; M'_gg[r][c] = x_r b_c into the chunk's Mx slot
+        // q of the row; M'_gg[r][c] = x_r b_c into the chunk's Mx slot (blocks 0, 1 form
+        // M'_00, blocks 2, 3 M'_11).  Then the lower left 16 x 16 block of each 32-row
+        // inverse, -M'_b G_ba M'_a for (a, b) = (0, 1) and (2, 3)
         auto prep_diag = [&](int c) {
             const int sl = c % 3, ms = c & 1;
             h8 kf[4][4];   // [block][k block]: rows 16 b + r16 (each is both operands of its tile)
@@ -343,6 +381,16 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) acc = mma(kf[b][kb], kf[b][kb], acc);
                 *reinterpret_cast<float4 *>(&sm.Gd[b][r16][4 * g]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            }
+            // G_ab for (a, b) = (0, 1), (2, 3): lane (g, r16) holds G_ab[4g + i][r16] =
+            // G_ba[r16][4g + i], which is G_ba's operand layout on the left of a product
+            h4 Gba[2];
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                f4 acc = zero4();
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) acc = mma(kf[2 * p][kb], kf[2 * p + 1][kb], acc);
+                Gba[p] = cvt4(acc);
             }
             wave_lds_fence();
             // lane (g, c): G_g[r][c] = Gd[g][c][r], r = 0..15; the rows' write strengths
@@ -364,74 +412,99 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
             for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(n[r]));   // n complete here
             asm volatile("s_nop 1");   // the two wait states before the lane moves read n
             subst_steps<0>(x, n);
+            {
+                const int blk = g >> 1, off = 16 * (g & 1), cpos = off + perm16_pos(r16);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sm.Mx[ms][16 * g + r][16 * g + r16] = (_Float16)(x[r] * bc);
+                for (int r = 0; r < 16; ++r) sm.Mx[ms][blk][off + r][cpos] = (_Float16)(x[r] * bc);
+            }
+            wave_lds_fence();
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                // T = G_ba M'_a: M'_a read transposed, so lane (g, j) holds rows 4g .. 4g + 3
+                // of stored column position j (token perm16_index(j)), and so does T
+                const h4 Ma = tr4(&sm.Mx[ms][p][0][0], GLM, 4 * g, 0, lane);
+                const f4 T = mma16(Gba[p], Ma, zero4());
+                // L = -M'_b T: lane (r16, g) holds M'_b[r16][4g .. 4g + 3] (contiguous, permuted
+                // only in whole runs of four); the result keeps T's column order, so lane
+                // (g, j) writes its rows at column position j
+                const h4 Mb = *reinterpret_cast<const h4 *>(&sm.Mx[ms][p][16 + r16][16 + perm16_pos(4 * g)]);
+                const f4 L = mma16(Mb, cvt4(T), zero4());
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.Mx[ms][p][16 + 4 * g + i][r16] = (_Float16)(-L[i]);
+            }
         };
 
         const std::false_type full;
         const std::true_type tail;
         const std::integral_constant<int, 0> p0;
-        const std::integral_constant<int, 1> p1;
-        if (nch > 0) fetch(0, p0);
-        // iteration j: the prefetch of chunk j + 1 first (in flight across the barrier,
-        // waited for where the next step first uses it), then chunk j's gates, keys and
-        // value rows, then chunk j-1's transposed keys, Gram tiles and inverses
+        if (pw != 0 && nch > 0) fetch(0, p0);
+        // iteration j: chunk j's gates, keys and value rows from the registers, then the
+        // prefetch of chunk j + 1 into them (in flight across the barrier, waited for where
+        // the next step first uses it), then chunk j-1's transposed keys, Gram tiles and
+        // inverses
         auto iter = [&](int j, auto pc) {
             constexpr int P = decltype(pc)::value;
             lds_barrier();
             // this chunk's prefetch landed before the barrier: claim its registers now,
             // so no later wait covers the loads issued below
+            if (pw != 0) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) claim(kraw[P][q]);
+                for (int q = 0; q < MR; ++q) claim(kraw[P][q]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) claim(vraw[P][i]);
-            claim(braw[P]);
-            claim(araw[P]);
-            claim(vrs[P]);
-            if (j + 1 < nch) fetch(j + 1, std::integral_constant<int, P ^ 1>());
-            if (j < nch - 1) stage(j, pc, full);
-            else if (j == nch - 1) stage(j, pc, tail);
+                for (int i = 0; i < MR; ++i) claim(vraw[P][i]);
+            }
+            if (pw == 3) {
+                claim(braw[P]);
+                claim(araw[P]);
+                claim(vrs[P]);
+            }
+            if (pw != 0) {
+                if (j < nch - 1) stage(j, pc, full);
+                else if (j == nch - 1) stage(j, pc, tail);
+            }
+            // the next chunk's prefetch reuses the registers just staged (one buffer:
+            // the loads still have the rest of this step and the barrier to land)
+            if (pw != 0 && j + 1 < nch) fetch(j + 1, pc);
             if (j >= 1 && j <= nch) {
                 if (pw == 0) {
                     prep_diag(j - 1);
                 } else {
-                    prep_offgram(j - 1);
+                    if (pw < 3) prep_offgram(j - 1);
                     store_kt(j - 1);
                 }
             }
         };
-        for (int j = 0; j < nch + 2; j += 2) {
-            iter(j, p0);
-            if (j + 1 < nch + 2) iter(j + 1, p1);
-        }
-        if (w == 4) {   // the prep waves accumulate the log-gates
+        for (int j = 0; j < nch + 2; ++j) iter(j, p0);
+        if (w == 7) {   // the gate wave accumulates the log-gates
             const double tot = wave_sum_f64(cl_lane);
             if (lane == 0) sm.cl_tot = tot;
         }
         lds_barrier();
     } else {
         // ---------------------------------------------------------------- state
-        // column tiles of X = [Tbar | S] held by state wave w: n = 0, 1 the Tbar
-        // tiles 2w, 2w + 1; n = 2, 3 the S tiles 2w, 2w + 1
-        f4 X[8][4];
-        float sig[4] = {0.f, 0.f, 0.f, 0.f};
-        int svq[2] = {0, 0};   // value exponent of the last chunk per S tile
+        // column tiles of X = [Tbar | S] held by state wave w: n = 0 the Tbar tile w,
+        // n = 1 the S tile w (32 columns each), as four 32-row tiles.  Lane (l32, hh),
+        // register i of a tile: row 32 rt + 8 (i >> 2) + 4 hh + (i & 3), column 32 w + l32
+        const int l32 = lane & 31, hh = lane >> 5;
+        f16v X[4][2];
+        float sig[2] = {0.f, 0.f};
+        int svq = 0;   // value exponent of the last chunk (S tile)
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
+        for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int n = 0; n < 4; ++n)
+            for (int n = 0; n < 2; ++n)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    X[mt][n][i] = (n < 2 && 16 * mt + 4 * g + i == 16 * (2 * w + n) + r16) ? 1.f : 0.f;
+                for (int i = 0; i < 16; ++i)
+                    X[rt][n][i] = (n == 0 && 32 * rt + 8 * (i >> 2) + 4 * hh + (i & 3) == 32 * w + l32) ? 1.f : 0.f;
 
         // Xhat <- Xhat 2^(sig - target): the unit follows the tile's largest entry,
         // never below 2^(ev - 4) for S (keeps the value term of P within fp16 range)
         auto renorm = [&](int n, bool isS, int ev) {
             float xm = 0.f;
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
+            for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) xm = fmaxf(xm, fabsf(X[mt][n][i]));
+                for (int i = 0; i < 16; ++i) xm = fmaxf(xm, fabsf(X[rt][n][i]));
             xm = wave_max(xm);
             float target = (float)pow2_exponent(xm) + sig[n];
             if (xm == 0.f) target = isS ? (float)ev : sig[n];
@@ -439,158 +512,162 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
             // an integer shift, exact, and finite however far the tile has decayed
             const int sh = (int)(sig[n] - target);
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
+            for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) X[mt][n][i] = ldexpf(X[mt][n][i], sh);
+                for (int i = 0; i < 16; ++i) X[rt][n][i] = ldexpf(X[rt][n][i], sh);
             sig[n] = target;
         };
-        // chunk c, before its products: the chunk gate on S
         // chunk c, before its products: the chunk gate on S
         auto state_pre = [&](int c) {
             const float gbv = sm.gb[c % 3];
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                X[mt][2] *= gbv;
-                X[mt][3] *= gbv;
-            }
+            for (int rt = 0; rt < 4; ++rt) X[rt][1] *= gbv;
         };
-        h4 Eh[4][2];   // [token block][column tile of the half]
-        // chunk c, column half hf (tiles 2 hf, 2 hf + 1): P = [0 | diag(dec) V 2^-sig] - K Xhat,
-        // E by block forward substitution, E_i = M'_ii (P_i - sum_{j<i} G_ij E_j), kept
-        // as fp16 (accumulator layout: rows 16 i + 4g + e, column r16), then X += K^T E
-        // for the half's tiles (the halves are independent columns of X)
-        auto state_half = [&](int c, auto hfc) {
-            constexpr int hf = decltype(hfc)::value;
+        // chunk c: P = [0 | diag(dec) V 2^-sig] - K Xhat for both tiles (two 32-token
+        // tiles each), E by the two-block substitution E_0 = M'_00 P_0, E_1 = M'_11 (P_1 -
+        // G_10 E_0) (fp16 operands from the accumulators: registers 8m .. 8m + 7 of a
+        // 32-row tile are its rows 16m + {4hh .. 4hh + 3, 8 + 4hh .. 8 + 4hh + 3}, the
+        // stored order of the operands' 16-blocks), then X += K^T E.  Every key and M
+        // fragment read from LDS feeds both tiles, and the two tiles' substitutions
+        // interleave.
+        auto state_chunk = [&](int c) {
             const int sl = c % 3, s2 = c & 1;
-            // bases: K rows (P's A operand, 16 bytes per lane), K^T rows (the update's
-            // A operand, 16 bytes per lane), the Mx rows
-            lds_h *kA = lds_base(&sm.Ks[sl][r16][8 * g]);
-            lds_h *kT = lds_base(&sm.KT[s2][r16][8 * g]);
-            lds_h *mx = lds_base(&sm.Mx[s2][r16][4 * g]);
+            // bases: K rows (P's left operand), K^T rows (the update's left operand), the
+            // Mx rows; 16 bytes per lane each
+            lds_h *kA = lds_base(&sm.Ks[sl][l32][8 * hh]);
+            lds_h *kT = lds_base(&sm.KT[s2][l32][8 * hh]);
+            lds_h *mx = lds_base(&sm.Mx[s2][0][l32][8 * hh]);
             // Software pipeline: every LDS fragment is requested one step before
             // the products that use it (the scheduling fences keep the requests
             // ahead), so a single wave keeps the matrix core fed.
-            h8 Ak[2][4];   // K rows 16 tt + r16, keys 32 kb + 4g + (e & 3) + 16 (e >> 2)
-            auto load_k = [&](int kb, h8 (&dst)[4]) {
+            h8 Ak[2][2];   // [buffer][token tile]: K rows 32 tt + l32, keys of block ks
+            auto load_k = [&](int ks, h8 (&dst)[2]) {
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt) dst[tt] = lds8h(kA + 16 * tt * GLK + 32 * kb);
+                for (int tt = 0; tt < 2; ++tt) dst[tt] = lds8h(kA + 32 * tt * GLK + 16 * ks);
             };
-            h4 Am[10];     // Mx fragments: -G_ij (j < i) and M'_ii, in use order
-            auto load_m = [&]() {
-                int n = 0;
+            h8 Am[2];      // one 32 x 32 tile of Mx (M'_00, M'_11 or -G_10), token blocks m = 0, 1
+            auto load_m = [&](int b) {
 #pragma unroll
-                for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-                    for (int jb = 0; jb <= ib; ++jb) Am[n++] = lds4h(mx + 16 * ib * GLP + 16 * jb);
+                for (int m = 0; m < 2; ++m) Am[m] = lds8h(mx + 32 * b * GLM + 16 * m);
             };
-            h8 At[2][2];   // K^T rows 16 mt + r16, tokens 32 jb + 4g + (e & 3) + 16 (e >> 2)
-            auto load_t = [&](int mt, h8 (&dst)[2]) {
+            h8 At[2][2];   // [buffer][token block of the pair]: K^T rows 32 rt + l32
+            auto load_t = [&](int rt, int kp, h8 (&dst)[2]) {
 #pragma unroll
-                for (int jb = 0; jb < 2; ++jb) dst[jb] = lds8h(kT + 16 * mt * GLT + 32 * jb);
+                for (int q = 0; q < 2; ++q) dst[q] = lds8h(kT + 32 * rt * GLT + 16 * (2 * kp + q));
             };
 
-            f4 P[4][2];    // [token block][column tile of the half]
+            f16v P[2][2];  // [tile][token tile 0-31, 32-63]
             load_k(0, Ak[0]);
-            if constexpr (hf == 0) {
+            P[0][0] = P[0][1] = f16v{};
+            {
+                // value term of the S tile: lane (l32, hh) reads V[32 tt + 8j + 4hh + e][32 w + l32],
+                // e = 0..3, through the transposing load: in lane row G = lane >> 4, lane j reads
+                // 8 bytes of row 32 tt + 8j + 4 (G >> 1) + (j >> 2), piece 4w + 2 (G & 1) +
+                // ((j >> 1) & 1) at its swizzled position, half j & 1
+                const int G = lane >> 4, lj = lane & 15;
+                const int t4 = 4 * (G >> 1) + (lj >> 2);
+                lds_h *vb = lds_base(&sm.Vr[sl][t4][8 * ((4 * w + 2 * (G & 1) + ((lj >> 1) & 1)) ^ (2 * (t4 & 7))) + 4 * (lj & 1)]);
+                lds_h *fb = lds_base(&sm.fac[sl][4 * hh]);
+                float vmax = 0.f;
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt) P[tt][0] = P[tt][1] = zero4();
-            } else {
-                // value term: lane (g, r16) reads V[16 tt + 4g + e][16 (2w + q) + r16], e = 0..3,
-                // through the transposing load (lane j's 8 bytes: row 4g + (j >> 2) of the
-                // block, piece 4w + 2q + ((j >> 1) & 1) at its swizzled position, half j & 1)
-                const int t4 = 4 * g + (r16 >> 2);
-                lds_h *vb[2];
+                for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int q = 0; q < 2; ++q)
-                    vb[q] = lds_base(&sm.Vr[sl][t4][8 * ((4 * w + 2 * q + ((r16 >> 1) & 1)) ^ (2 * (t4 & 7))) + 4 * (r16 & 1)]);
-                lds_h *fb = lds_base(&sm.fac[sl][4 * g]);
-                float vmax[2] = {0.f, 0.f};
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt) {
-                    const f4 f = lds4f(fb + 32 * tt);   // fac[16 tt + 4g + e] (floats: 2 halves each)
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const s4v v = lds_tr4s(vb[q] + 16 * tt * GD);
+                    for (int j = 0; j < 4; ++j) {
+                        const f4 f = lds4f(fb + 2 * (32 * tt + 8 * j));   // fac[32 tt + 8j + 4hh + e]
+                        const s4v v = lds_tr4s(vb + (32 * tt + 8 * j) * GD);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            P[tt][q][e] = raw_f32(v[e], TV()) * f[e];
-                            vmax[q] = fmaxf(vmax[q], fabsf(P[tt][q][e]));
+                            P[1][tt][4 * j + e] = raw_f32(v[e], TV()) * f[e];
+                            vmax = fmaxf(vmax, fabsf(P[1][tt][4 * j + e]));
                         }
                     }
-                }
                 // the S unit: the chunk's value scale on the first chunk (S is zero),
                 // renormalised when the values run more than 2^4 ahead of it
+                svq = pow2_exponent(wave_max_nn(vmax));
+                if (c == 0) sig[1] = (float)svq;
+                else if ((float)svq > sig[1] + 4.f) renorm(1, true, svq);
+                const int isg = (int)sig[1];
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    svq[q] = pow2_exponent(wave_max_nn(vmax[q]));
-                    if (c == 0) sig[2 + q] = (float)svq[q];
-                    else if ((float)svq[q] > sig[2 + q] + 4.f) renorm(2 + q, true, svq[q]);
-                    const int isg = (int)sig[2 + q];
+                for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                    for (int tt = 0; tt < 4; ++tt)
+                    for (int i = 0; i < 16; ++i) P[1][tt][i] = ldexpf(P[1][tt][i], -isg);
+            }
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) P[tt][q][e] = ldexpf(P[tt][q][e], -isg);
+            for (int ks = 0; ks < 8; ++ks) {
+                if (ks < 7) load_k(ks + 1, Ak[(ks + 1) & 1]);
+                else load_m(0);
+                sched_fence();
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    h8 B;   // -Xhat, keys 16 ks + the stored order of the block
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) B[e] = (_Float16)(-X[ks >> 1][n][8 * (ks & 1) + e]);
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) P[n][tt] = mma32(Ak[ks & 1][tt], B, P[n][tt]);
                 }
-            }
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                if (kb < 3) load_k(kb + 1, Ak[(kb + 1) & 1]);
-                else load_m();
-                sched_fence();
-                h8 B[2];   // -Xhat, keys 32 kb + 4g + (e & 3) + 16 (e >> 2)
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        B[q][i] = (_Float16)(-X[2 * kb][2 * hf + q][i]);
-                        B[q][4 + i] = (_Float16)(-X[2 * kb + 1][2 * hf + q][i]);
-                    }
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) P[tt][q] = mma(Ak[kb & 1][tt], B[q], P[tt][q]);
                 sched_fence();
             }
-            load_t(0, At[0]);
-            sched_fence();
+            h8 Eh[2][4];   // [tile] E as fp16, token blocks of 16
             {
-                int n = 0;
+                // each Mx tile is requested while the products before its use run
+                f16v E[2];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int n = 0; n < 2; ++n) {
+                    E[n] = mma32(Am[0], cvt8(P[n][0], 0), f16v{});
+                    E[n] = mma32(Am[1], cvt8(P[n][0], 8), E[n]);
+                }
+                sched_fence();
+                load_m(2);
+                sched_fence();
 #pragma unroll
-                    for (int jb = 0; jb < i; ++jb, ++n)
+                for (int n = 0; n < 2; ++n) {
+                    Eh[n][0] = cvt8(E[n], 0);
+                    Eh[n][1] = cvt8(E[n], 8);
+                    P[n][1] = mma32(Am[0], Eh[n][0], P[n][1]);
+                    P[n][1] = mma32(Am[1], Eh[n][1], P[n][1]);
+                }
+                sched_fence();
+                load_m(1);
+                sched_fence();
 #pragma unroll
-                        for (int q = 0; q < 2; ++q) P[i][q] = mma16(Am[n], Eh[jb][q], P[i][q]);
+                for (int n = 0; n < 2; ++n) {
+                    const h8 Pa = cvt8(P[n][1], 0), Pb = cvt8(P[n][1], 8);
+                    E[n] = mma32(Am[0], Pa, f16v{});
+                    E[n] = mma32(Am[1], Pb, E[n]);
+                }
+                sched_fence();
+                load_t(0, 0, At[0]);
+                sched_fence();
 #pragma unroll
-                    for (int q = 0; q < 2; ++q) Eh[i][q] = cvt4(mma16(Am[n], cvt4(P[i][q]), zero4()));
-                    ++n;
+                for (int n = 0; n < 2; ++n) {
+                    Eh[n][2] = cvt8(E[n], 0);
+                    Eh[n][3] = cvt8(E[n], 8);
                 }
             }
             sched_fence();
-            // X += K^T E for the half's two tiles
+            // X += K^T E for both tiles: row tile rt, token block pairs kp = 0, 1
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                if (mt < 7) load_t(mt + 1, At[(mt + 1) & 1]);
+            for (int st = 0; st < 8; ++st) {
+                const int rt = st >> 1, kp = st & 1;
+                if (st < 7) load_t((st + 1) >> 1, (st + 1) & 1, At[(st + 1) & 1]);
                 sched_fence();
 #pragma unroll
-                for (int jb = 0; jb < 2; ++jb)
+                for (int n = 0; n < 2; ++n)
 #pragma unroll
-                    for (int q = 0; q < 2; ++q)
-                        X[mt][2 * hf + q] = mma(At[mt & 1][jb], cat8(Eh[2 * jb][q], Eh[2 * jb + 1][q]), X[mt][2 * hf + q]);
+                    for (int q = 0; q < 2; ++q) X[rt][n] = mma32(At[st & 1][q], Eh[n][2 * kp + q], X[rt][n]);
                 sched_fence();
             }
         };
-        // periodic renormalisation of the four tiles, every 4 chunks
+        // periodic renormalisation of the two tiles, every 4 chunks
         auto state_post = [&](int c) {
             if ((c & 3) == 3) {
-#pragma unroll
-                for (int n = 0; n < 4; ++n) renorm(n, n >= 2, n >= 2 ? svq[n - 2] : 0);
+                renorm(0, false, 0);
+                renorm(1, true, svq);
             }
         };
         auto state = [&](int c) {
             state_pre(c);
-            state_half(c, std::integral_constant<int, 0>());
-            state_half(c, std::integral_constant<int, 1>());
+            state_chunk(c);
             state_post(c);
         };
 
@@ -602,21 +679,25 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
         const double cl_tot = sm.cl_tot;
         float *Tu = a.T_out + (int64_t)unit * GD * GD;
         float *Su = a.S0_out + (int64_t)unit * GD * GD;
-        int g4 = 4 * g;   // opaque: keeps the row indices from being computed before the loop
-        asm volatile("" : "+v"(g4));
+        int h4r = 4 * hh;   // opaque: keeps the row indices from being computed before the loop
+        asm volatile("" : "+v"(h4r));
+        const int col = 32 * w + l32;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const bool isS = n >= 2;
-            const int col = 16 * (2 * w + (n & 1)) + r16;
+        for (int n = 0; n < 2; ++n) {
+            const bool isS = n == 1;
+            // 2^e split into an integer exponent and a factor in [1, 2) (0 once the tile
+            // has decayed below the float range), the same for the whole tile
             const double e = (double)sig[n] + (isS ? 0.0 : cl_tot);
+            const double fl = floor(e);
+            const int ie = e < -400.0 ? 0 : (int)fl;
+            const float fr = e < -400.0 ? 0.f : exp2f((float)(e - fl));
+            float *dst = isS ? Su : Tu;
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
+            for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * mt + g4 + i;
-                    const float val = scale_pow2(X[mt][n][i], e);
-                    if (isS) Su[row * GD + col] = val;
-                    else     Tu[row * GD + col] = val;
+                for (int i = 0; i < 16; ++i) {
+                    const int row = 32 * rt + 8 * (i >> 2) + h4r + (i & 3);
+                    dst[row * GD + col] = ldexpf(X[rt][n][i] * fr, ie);
                 }
         }
     }

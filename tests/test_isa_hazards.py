@@ -11,7 +11,8 @@ path from a matrix-core instruction to an instruction that reads any of its
 destination registers there must be at least MIN_WAIT[opcode] wait states
 (one per instruction, n + 1 per s_nop n): the spacing the compiler itself
 keeps on straight-line code, 8 after the 16x16x32 and 16x16x16
-half-precision (fp16 and bf16) products and 10 after the 8-pass 16x16x4 fp32 product.  A matrix-core opcode
+half-precision (fp16 and bf16) products, 12 after the 32x32x16 fp16 product and
+10 after the 8-pass 16x16x4 fp32 product.  A matrix-core opcode
 without a figure here fails the test, so a new one gets a deliberate entry.
 """
 from __future__ import annotations
@@ -30,6 +31,7 @@ MIN_WAIT = {
     "v_mfma_f32_16x16x32_f16": 8,
     "v_mfma_f32_16x16x16_f16": 8,
     "v_mfma_f32_16x16x16_bf16": 8,
+    "v_mfma_f32_32x32x16_f16": 12,
     "v_mfma_f32_16x16x4_f32": 10,
 }
 _REG = re.compile(r"\b([av])\[(\d+):(\d+)\]|\b([av])(\d+)\b")
