@@ -54,6 +54,9 @@
 namespace hy {
 namespace {
 
+// fourth word of a raw buffer resource: 32-bit data format, so untyped loads
+// return data and loads past the resource's size return zero
+#define HY_BUF_DW3 0x00020000
 constexpr int GD = 128;          // d_k = d_v
 constexpr int GLK = GD + 8;      // Ks row stride (halves)
 constexpr int GLT = 64 + 8;      // KT row stride (halves)
@@ -246,13 +249,30 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
         uint4 vraw[2][MR];
         TG braw[2], araw[2];
         float vrs[2];
+        // Key and value rows through buffer loads: per chunk, a resource whose base is the
+        // chunk's first row and whose size covers only its rows inside the segment, so
+        // rows past the segment end read as zero; each lane's byte offsets inside a chunk
+        // are fixed
+        const uint32_t ldk_b = (uint32_t)(a.ldk * (int64_t)sizeof(TK));
+        uint32_t koff[MR], voff[MR];
+#pragma unroll
+        for (int q = 0; q < MR; ++q) {
+            koff[q] = (uint32_t)(row0 + q) * ldk_b + (uint32_t)(16 * r16);
+            const int t = rbase + 4 * q + g;
+            voff[q] = (uint32_t)t * ldv_b + 16 * (r16 ^ (2 * (t & 7)));
+        }
         auto fetch = [&](int c, auto pc) {
             constexpr int P = decltype(pc)::value;
             const int last = len - 1 - 64 * c;   // >= 0 for every chunk of the segment
-            const TK *kc = kb + (int64_t)(64 * c) * a.ldk;
+            const int rows = min(last + 1, 64);
+            const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(reinterpret_cast<const unsigned char *>(kb) + (int64_t)(64 * c) * ldk_b), (short)0,
+                (int)((uint32_t)rows * ldk_b), HY_BUF_DW3);
+            const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(vb + (int64_t)(64 * c) * ldv_b), (short)0, (int)((uint32_t)rows * ldv_b), HY_BUF_DW3);
 #pragma unroll
             for (int q = 0; q < MR; ++q)
-                if (q < nr) ld_raw8(kc + (__umul24(min(row0 + q, last), (unsigned)a.ldk) + 8 * r16), kraw[P][q]);
+                if (q < nr) kraw[P][q].u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, (int)koff[q], 0, 0));
             if (pw == 3) {   // the gate wave
                 const uint32_t go = __umul24(min(lane, last), (unsigned)a.h_v);
                 const int64_t gc = (int64_t)(64 * c) * a.h_v;
@@ -262,14 +282,9 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
                 else vrs[P] = 1.f;
             }
             // raw value rows rbase + 4i + g, the 16-byte piece r16 ^ 2 (t & 7) of row t
-            // (rows past the segment end repeat its last row; their factor is 0)
-            const unsigned char *vc = vb + (int64_t)(64 * c) * ldv_b;
 #pragma unroll
-            for (int i = 0; i < MR; ++i) {
-                const int t = rbase + 4 * i + g;
-                const uint32_t off = (uint32_t)min(t, last) * ldv_b + 16 * (r16 ^ (2 * (t & 7)));
-                if (i < nr) vraw[P][i] = *reinterpret_cast<const uint4 *>(vc + off);
-            }
+            for (int i = 0; i < MR; ++i)
+                if (i < nr) vraw[P][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, (int)voff[i], 0, 0));
         };
 
         double cl_lane = 0.0;
