@@ -175,25 +175,6 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // lane alone the two addresses do not overlap)
 __device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// x_r += (value of nv in lane Q of this lane's 16-lane row) * x_q: the row
-// broadcast rides on the multiply-add.  The caller keeps two wait states
-// between the last write of nv and the first use here (a lane move reads its
-// source register that late).
-template <int Q>
-__device__ __forceinline__ void fmac_rowbcast(float &acc, float nv, float xq)
-{
-    asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-                 : "+v"(acc) : "v"(nv), "v"(xq), "n"(Q));
-}
-// forward substitution steps Q..14: x_r += N_r[lane Q] x_Q for r > Q
-template <int Q>
-__device__ __forceinline__ void subst_steps(float (&x)[16], const float (&n)[16])
-{
-#pragma unroll
-    for (int r = Q + 1; r < 16; ++r) fmac_rowbcast<Q>(x[r], n[r], x[Q]);
-    if constexpr (Q < 14) subst_steps<Q + 1>(x, n);
-}
-
 static_assert(sizeof(GdnSmem) <= 160 * 1024, "the build's LDS exceeds a workgroup's 160 KiB");
 
 }  // namespace

@@ -52,6 +52,10 @@ struct KdaSmem {
 // Gram tiles on or below the diagonal of the 4x4 token-tile grid
 __constant__ int kKdaTi[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
 __constant__ int kKdaTj[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+// the eight Gram tiles that the reduced-precision build forms whole (the tiles (3,1)
+// and (3,2) go in two reduction halves each)
+__constant__ int kKdaWi[8] = {0, 1, 1, 2, 2, 2, 3, 3};
+__constant__ int kKdaWj[8] = {0, 0, 1, 0, 1, 2, 0, 3};
 
 template <int D, typename TKV, typename TG>
 __global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_kernel(const DeltaArgs a)
@@ -356,6 +360,7 @@ struct KdaHSmem {
         _Float16 Wh[64][LDW];        // then W (token rows, keys permuted)
     };
     float Mm[64][C::LDG];    // M = (I + Gm)^-1
+    float Gx[2][16][16];     // second k-halves of the Gram tiles (3,1) and (3,2)
     _Float16 Mb[64][LDK];    // M diag(b) in fp16 (token rows, columns permuted)
     _Float16 Kh[D][LDK];     // Kh^T (key rows, tokens permuted)
     float beta[64];
@@ -444,14 +449,24 @@ __global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_f16_kernel(const De
     const int dp = tid % LPR, blk = tid / LPR;
     uint32_t kraw[8], vraw[8], graw[8];
     float br = 0.f;
+    // rows through buffer loads: per chunk a resource based at its first row and
+    // sized to its rows inside the segment (rows past the end read as zero; the
+    // staging masks them anyway), offsets = this thread's row and dims plus i rows
+    const uint32_t ldk_b = (uint32_t)a.ldk * 2u, ldv_b = (uint32_t)a.ldv * 2u, ldg_b = (uint32_t)ldg * 2u;
     auto fetch = [&](int c) {
-        const int t0 = 64 * c + 8 * blk, last = len - 1;
+        const int rows = min(len - 64 * c, 64);
+        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(kp + (int64_t)(64 * c) * a.ldk), (short)0, (int)((uint32_t)rows * ldk_b), 0x00020000);
+        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(vp + (int64_t)(64 * c) * a.ldv), (short)0, (int)((uint32_t)rows * ldv_b), 0x00020000);
+        const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(gp + (int64_t)(64 * c) * ldg), (short)0, (int)((uint32_t)rows * ldg_b), 0x00020000);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int64_t t = min(t0 + i, last);
-            kraw[i] = *reinterpret_cast<const uint32_t *>(kp + t * a.ldk + 2 * dp);
-            vraw[i] = *reinterpret_cast<const uint32_t *>(vp + t * a.ldv + 2 * dp);
-            graw[i] = *reinterpret_cast<const uint32_t *>(gp + t * ldg + 2 * dp);
+            const uint32_t t = (uint32_t)(8 * blk + i);
+            kraw[i] = __builtin_amdgcn_raw_buffer_load_b32(kr, (int)(t * ldk_b + 4u * dp), 0, 0);
+            vraw[i] = __builtin_amdgcn_raw_buffer_load_b32(vr, (int)(t * ldv_b + 4u * dp), 0, 0);
+            graw[i] = __builtin_amdgcn_raw_buffer_load_b32(gr, (int)(t * ldg_b + 4u * dp), 0, 0);
         }
         if (w == 0) {
             const int t = 64 * c + lane;
@@ -537,39 +552,67 @@ __global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_f16_kernel(const De
         lds_barrier();
 
         // ---- decay-aware Gram: b_r sum_d k_r k_s 2^(cl_r - cl_s), s < r ------------
-        for (int q = w; q < 10; q += NW) {
-            const int ti = kKdaTi[q], tj = kKdaTj[q];
+        // The per-element exp2 of the operands bounds this phase, so the work is spread
+        // evenly over the SIMDs: eight whole tiles, one per wave (two per wave at
+        // NW = 4), and the tiles (3,1) and (3,2) as two reduction halves each on waves
+        // 0-3 (the second halves' partial sums are added in below, while wave 0 inverts)
+        auto gram = [&](int ti, int tj, int ks0, int ks1) {
             const int ref = ti == tj ? 16 * ti + 8 : 16 * tj + 15;
             f4 acc = zero4();
 #pragma unroll 4
-            for (int ks = 0; ks < D / 4; ++ks) {
+            for (int ks = ks0; ks < ks1; ++ks) {
                 const int k = g * (D / 4) + ks;
                 const float cr = sm.CL[k][ref];
                 const float A = sm.KT[k][16 * ti + r16] * __builtin_amdgcn_exp2f(sm.CL[k][16 * ti + r16] - cr);
                 const float B = sm.KT[k][16 * tj + r16] * __builtin_amdgcn_exp2f(cr - sm.CL[k][16 * tj + r16]);
                 acc = mma(A, B, acc);
             }
+            return acc;
+        };
+        for (int q = w; q < 8; q += NW) {
+            const int ti = kKdaWi[q], tj = kKdaWj[q];
+            const f4 acc = gram(ti, tj, 0, D / 4);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int rr = 16 * ti + 4 * g + i, cc = 16 * tj + r16;
                 sm.Gm[rr][cc] = (cc < rr) ? sm.beta[rr] * acc[i] : 0.f;
             }
         }
+        if (w < 4) {
+            const int tj = 1 + (w >> 1), hf = w & 1;
+            const f4 acc = gram(3, tj, hf * (D / 8), (hf + 1) * (D / 8));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float v = sm.beta[48 + 4 * g + i] * acc[i];
+                if (hf == 0) sm.Gm[48 + 4 * g + i][16 * tj + r16] = v;
+                else         sm.Gx[tj - 1][4 * g + i][r16] = v;
+            }
+        }
         lds_barrier();
 
         // ---- M = (I + Gm)^-1: diagonal 16x16 blocks by forward substitution ----
+        //      lane (o, c) carries column c of block o and the multipliers -Gm[o + r][o + c],
+        //      which the step for column q broadcasts from lane q along the 16-lane row
         if (w == 0) {
             const int o = 16 * (lane >> 4), cc = lane & 15;
-            float x[16];
+            float n[16], x[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float acc = (r == cc) ? 1.f : 0.f;
-#pragma unroll
-                for (int q = 0; q < r; ++q) acc -= sm.Gm[o + r][o + q] * x[q];
-                x[r] = acc;
+                n[r] = -sm.Gm[o + r][o + cc];
+                x[r] = (r == cc) ? 1.f : 0.f;
             }
 #pragma unroll
+            for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(n[r]));   // n complete here
+            asm volatile("s_nop 1");   // the two wait states before the lane moves read n
+            subst_steps<0>(x, n);
+#pragma unroll
             for (int r = 0; r < 16; ++r) sm.Mm[o + r][o + cc] = x[r];
+        } else {
+            // the second halves of the split Gram tiles (3,1) and (3,2)
+            for (int e = tid - 64; e < 2 * 256; e += C::NT - 64) {
+                const int t = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
+                sm.Gm[48 + rr][16 * (t + 1) + cc] += sm.Gx[t][rr][cc];
+            }
         }
         lds_barrier();
         for (int p = w; p < 2; p += NW) {

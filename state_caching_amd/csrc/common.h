@@ -183,6 +183,26 @@ __device__ __forceinline__ float wave_prefix_incl(float x) {
     return s + earlier;
 }
 
+// ---- 16 x 16 unit lower triangular solve, one column per lane -------------
+// x_r += (value of nv in lane Q of this lane's 16-lane row) * x_q: the row
+// broadcast rides on the multiply-add.  The caller keeps two wait states
+// between the last write of nv and the first use here (a lane move reads its
+// source register that late).
+template <int Q>
+__device__ __forceinline__ void fmac_rowbcast(float &acc, float nv, float xq)
+{
+    asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                 : "+v"(acc) : "v"(nv), "v"(xq), "n"(Q));
+}
+// forward substitution steps Q..14: x_r += N_r[lane Q] x_Q for r > Q
+template <int Q>
+__device__ __forceinline__ void subst_steps(float (&x)[16], const float (&n)[16])
+{
+#pragma unroll
+    for (int r = Q + 1; r < 16; ++r) fmac_rowbcast<Q>(x[r], n[r], x[Q]);
+    if constexpr (Q < 14) subst_steps<Q + 1>(x, n);
+}
+
 // Power-of-two exponent that brings m (>= 0) into [0.5, 1); 0 for m == 0 or non-finite.
 __device__ __forceinline__ int pow2_exponent(float m) {
     if (!(m > 0.f) || !(m < INFINITY)) return 0;
