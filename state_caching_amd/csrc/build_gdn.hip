@@ -32,17 +32,19 @@
 //                    products): P (one tile at a time; the value term scaled
 //                    from the raw rows here), the two-block substitution for E,
 //                    and X += K^T E
-//   prep waves 4-7   chunk j: the raw value rows (prefetched into registers) to LDS;
-//                    gates; 16 key rows per wave converted to fp16.  Chunk j-1:
-//                    the transposed key copy; the four Gram tiles of G_10
+//   prep waves 4-7   chunk j (waves 5-7): the raw value rows and the key rows
+//                    (prefetched into registers, keys converted to fp16) to LDS;
+//                    gates (wave 7).  Chunk j-1: the four Gram tiles of G_10
 //                    (negated; waves 5 and 6) and, on wave 4, the four 16-row
 //                    diagonal inverses (one block per lane row, the multipliers
 //                    broadcast across the row by lane moves), the M'_ii and the
 //                    blocks -M'_b G_ba M'_a that join them into 32-row inverses
-// Every matrix-core operand reaches the products through 16-byte LDS reads:
-// keys are stored with their order permuted inside each 16-key block, and the
-// transposed key copy and the M tiles permute tokens the same way, so that one
-// read yields the reduction order of the 32 x 32 accumulator layout.
+// The reduction order of a 32 x 32 accumulator tile, read as an operand, runs
+// over rows 4a + {0..3} and 8 + 4a + {0..3} of each 16-block (lane half a), so
+// every operand fragment is two runs of four: the P product reads its key
+// fragments as two 8-byte runs of a key row, and the M tiles (stored transposed,
+// token-major) and K^T (the key rows themselves) reach their products through
+// two transposing loads per fragment.
 // X is kept in power-of-two units per column tile (renormalised every 4
 // chunks, or when a chunk's values run ahead of the S unit), so every fp16
 // operand stays in range.
@@ -59,26 +61,16 @@ namespace {
 #define HY_BUF_DW3 0x00020000
 constexpr int GD = 128;          // d_k = d_v
 constexpr int GLK = GD + 8;      // Ks row stride (halves)
-constexpr int GLT = 64 + 8;      // KT row stride (halves)
 constexpr int GLM = 32 + 8;      // Mx row stride (halves)
 constexpr int GLG = 20;          // Gd row stride (floats)
 
-// Storage order inside a 16-wide block: position 8a + e holds index
-// 4a + (e & 3) + 8 (e >> 2), so the 8 halves at 8a are the reduction indices
-// that lane half a holds in the 32 x 32 accumulator layout, 4a + {0..3} and
-// 8 + 4a + {0..3}.
-__device__ __forceinline__ int perm16_index(int pos) { return (pos & ~15) + 4 * ((pos >> 3) & 1) + (pos & 3) + 8 * ((pos >> 2) & 1); }
-// position of index idx; the four indices 4b .. 4b + 3 stay contiguous
-__device__ __forceinline__ int perm16_pos(int idx) { return (idx & ~15) + 8 * ((idx >> 2) & 1) + 4 * ((idx >> 3) & 1) + (idx & 3); }
-
 struct GdnSmem {
-    _Float16 Ks[3][64][GLK];     // keys, token-major, key order permuted per 16-key block
-    _Float16 KT[2][GD][GLT];     // keys transposed (key-major), token order permuted per 16 tokens
+    _Float16 Ks[3][64][GLK];     // keys in fp16, token-major, natural key order
     unsigned short Vr[3][64][GD];   // raw value rows as stored (bf16 or fp16 bits); the 16-byte
                                     // piece p of row t sits at piece position p ^ (2 (t & 7))
-    _Float16 Mx[2][3][32][GLM];  // per chunk slot: M'_00, M'_11 and -G_10 (32 x 32 each, token
-                                 // columns permuted per 16; the upper right 16 x 16 blocks of the
-                                 // two inverses stay zero)
+    _Float16 Mx[2][3][32][GLM];  // per chunk slot: M'_00, M'_11 and -G_10 (32 x 32 each), stored
+                                 // transposed, Mx[.][.][token][row]; the upper right 16 x 16
+                                 // blocks of the two inverses stay zero
     float Gd[4][16][GLG];        // the four diagonal Gram blocks (inverting wave's scratch)
     float beta[3][64];           // b_t per slot
     float fac[3][64];            // value row factor dec_t (times the row scale of the conv
@@ -293,43 +285,18 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
 #pragma unroll
                 for (int q = 0; q < MR; ++q) mask_raw8(kraw[P][q], 64 * c + row0 + q < len);
             }
-            // keys 8 r16 .. 8 r16 + 7 = two runs of four, stored at their permuted positions
-            const int kpos0 = perm16_pos(8 * r16), kpos1 = perm16_pos(8 * r16 + 4);
+            // keys 8 r16 .. 8 r16 + 7 in fp16, one 16-byte store per row
 #pragma unroll
             for (int q = 0; q < MR; ++q) {
                 if (q >= nr) break;
                 float kx[8];
                 widen8(kraw[P][q], kx);
-                h4 k0, k1;
+                h8 k8;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    k0[e] = (_Float16)kx[e];
-                    k1[e] = (_Float16)kx[4 + e];
-                }
-                *reinterpret_cast<h4 *>(&sm.Ks[sl][row0 + q][kpos0]) = k0;
-                *reinterpret_cast<h4 *>(&sm.Ks[sl][row0 + q][kpos1]) = k1;
+                for (int e = 0; e < 8; ++e) k8[e] = (_Float16)kx[e];
+                *reinterpret_cast<h8 *>(&sm.Ks[sl][row0 + q][8 * r16]) = k8;
             }
         };
-        // keys of chunk c transposed into KT slot c & 1, by prep waves 1-3 (16-key blocks
-        // 0-3 on wave 3, 4-5 on wave 1, 6-7 on wave 2; all 64 tokens): a transposing read
-        // gives lane (g, r16) tokens 16 tb + 4g .. + 3 of stored key column 16 xb + r16,
-        // written as one run at the tokens' permuted position
-        auto store_kt = [&](int c) {
-            const int sl = c % 3, s2 = c & 1;
-            const int nb = pw == 3 ? 4 : 2, xb0 = pw == 3 ? 0 : 2 + 2 * pw;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (i < nb) {
-                    const int xb = xb0 + i;
-#pragma unroll
-                    for (int tb = 0; tb < 4; ++tb) {
-                        const h4 v = tr4(&sm.Ks[sl][0][0], GLK, 16 * tb + 4 * g, 16 * xb, lane);
-                        *reinterpret_cast<h4 *>(&sm.KT[s2][16 * xb + perm16_index(r16)][16 * tb + perm16_pos(4 * g)]) = v;
-                    }
-                }
-            }
-        };
-
         // ------------------------------------------------------- prep: Gram, M'
         // 16x16 Gram tile K_i K_j^T of slot sl (lane (g, r16), register i: row 4g + i,
         // column r16); the stored key order is the same for both operands
@@ -344,16 +311,15 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
             return acc;
         };
         // chunk c, prep waves 1 and 2: the Gram tiles (1 + pw, 0) and (1 + pw, 1) of the
-        // 16-row blocks, negated, into the -G_10 tile of the chunk's Mx slot
+        // 16-row blocks, negated, into the -G_10 tile of the chunk's Mx slot (lane (g, r16)
+        // writes its four rows of column r16 as one run of the transposed tile)
         auto prep_offgram = [&](int c) {
             const int ms = c & 1, sl = c % 3;
             const int ti = 1 + pw;
 #pragma unroll
             for (int tj = 0; tj < 2; ++tj) {
                 const f4 acc = gram_tile(sl, ti, tj);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sm.Mx[ms][2][16 * (ti - 2) + 4 * g + i][16 * tj + perm16_pos(r16)] = (_Float16)(-acc[i]);
+                *reinterpret_cast<h4 *>(&sm.Mx[ms][2][16 * tj + r16][16 * (ti - 2) + 4 * g]) = cvt4(-acc);
             }
         };
         // chunk c, prep wave 0: the four 16-row diagonal blocks.  Their Gram tiles go
@@ -409,24 +375,29 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
             asm volatile("s_nop 1");   // the two wait states before the lane moves read n
             subst_steps<0>(x, n);
             {
-                const int blk = g >> 1, off = 16 * (g & 1), cpos = off + perm16_pos(r16);
+                // column r16 of block g, rows 0..15: one contiguous run of the transposed tile
+                const int blk = g >> 1, off = 16 * (g & 1);
+                h8 lo, hi;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sm.Mx[ms][blk][off + r][cpos] = (_Float16)(x[r] * bc);
+                for (int r = 0; r < 8; ++r) {
+                    lo[r] = (_Float16)(x[r] * bc);
+                    hi[r] = (_Float16)(x[8 + r] * bc);
+                }
+                *reinterpret_cast<h8 *>(&sm.Mx[ms][blk][off + r16][off]) = lo;
+                *reinterpret_cast<h8 *>(&sm.Mx[ms][blk][off + r16][off + 8]) = hi;
             }
             wave_lds_fence();
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
-                // T = G_ba M'_a: M'_a read transposed, so lane (g, j) holds rows 4g .. 4g + 3
-                // of stored column position j (token perm16_index(j)), and so does T
-                const h4 Ma = tr4(&sm.Mx[ms][p][0][0], GLM, 4 * g, 0, lane);
+                // T = G_ba M'_a: lane (g, j) holds M'_a[4g .. 4g + 3][j], contiguous in the
+                // transposed tile, and so T
+                const h4 Ma = *reinterpret_cast<const h4 *>(&sm.Mx[ms][p][r16][4 * g]);
                 const f4 T = mma16(Gba[p], Ma, zero4());
-                // L = -M'_b T: lane (r16, g) holds M'_b[r16][4g .. 4g + 3] (contiguous, permuted
-                // only in whole runs of four); the result keeps T's column order, so lane
-                // (g, j) writes its rows at column position j
-                const h4 Mb = *reinterpret_cast<const h4 *>(&sm.Mx[ms][p][16 + r16][16 + perm16_pos(4 * g)]);
+                // L = -M'_b T: lane (r16, g) holds M'_b[r16][4g .. 4g + 3] through the
+                // transposing load; lane (g, j) writes L[4g .. 4g + 3][j] as one run
+                const h4 Mb = tr4(&sm.Mx[ms][p][0][0], GLM, 16 + 4 * g, 16, lane);
                 const f4 L = mma16(Mb, cvt4(T), zero4());
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sm.Mx[ms][p][16 + 4 * g + i][r16] = (_Float16)(-L[i]);
+                *reinterpret_cast<h4 *>(&sm.Mx[ms][p][r16][16 + 4 * g]) = cvt4(-L);
             }
         };
 
@@ -466,7 +437,6 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
                     prep_diag(j - 1);
                 } else {
                     if (pw < 3) prep_offgram(j - 1);
-                    store_kt(j - 1);
                 }
             }
         };
@@ -528,28 +498,38 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
         // interleave.
         auto state_chunk = [&](int c) {
             const int sl = c % 3, s2 = c & 1;
-            // bases: K rows (P's left operand), K^T rows (the update's left operand), the
-            // Mx rows; 16 bytes per lane each
-            lds_h *kA = lds_base(&sm.Ks[sl][l32][8 * hh]);
-            lds_h *kT = lds_base(&sm.KT[s2][l32][8 * hh]);
-            lds_h *mx = lds_base(&sm.Mx[s2][0][l32][8 * hh]);
+            // bases: K rows (P's left operand: keys 4hh .. 4hh + 3 of a 16-key block, and 8
+            // more on), the K^T and M fragments (the left operands of the update and of the
+            // substitution: in lane row G of the wave, lane j supplies the 8 bytes of row
+            // 4 hh + (j >> 2), columns 16 (G & 1) + 4 (j & 3) .. of the transposing load)
+            const int G = lane >> 4, lj = lane & 15;
+            lds_h *kA = lds_base(&sm.Ks[sl][l32][4 * hh]);
+            lds_h *kT = lds_base(&sm.Ks[sl][4 * hh + (lj >> 2)][16 * (G & 1) + 4 * (lj & 3)]);
+            lds_h *mx = lds_base(&sm.Mx[s2][0][4 * hh + (lj >> 2)][16 * (G & 1) + 4 * (lj & 3)]);
             // Software pipeline: every LDS fragment is requested one step before
             // the products that use it (the scheduling fences keep the requests
             // ahead), so a single wave keeps the matrix core fed.
             h8 Ak[2][2];   // [buffer][token tile]: K rows 32 tt + l32, keys of block ks
             auto load_k = [&](int ks, h8 (&dst)[2]) {
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt) dst[tt] = lds8h(kA + 32 * tt * GLK + 16 * ks);
+                for (int tt = 0; tt < 2; ++tt)
+                    dst[tt] = cat8(lds4h(kA + 32 * tt * GLK + 16 * ks), lds4h(kA + 32 * tt * GLK + 16 * ks + 8));
             };
             h8 Am[2];      // one 32 x 32 tile of Mx (M'_00, M'_11 or -G_10), token blocks m = 0, 1
             auto load_m = [&](int b) {
 #pragma unroll
-                for (int m = 0; m < 2; ++m) Am[m] = lds8h(mx + 32 * b * GLM + 16 * m);
+                for (int m = 0; m < 2; ++m) {
+                    lds_h *p = mx + 32 * b * GLM + 16 * m * GLM;
+                    Am[m] = cat8(__builtin_bit_cast(h4, lds_tr4s(p)), __builtin_bit_cast(h4, lds_tr4s(p + 8 * GLM)));
+                }
             };
             h8 At[2][2];   // [buffer][token block of the pair]: K^T rows 32 rt + l32
             auto load_t = [&](int rt, int kp, h8 (&dst)[2]) {
 #pragma unroll
-                for (int q = 0; q < 2; ++q) dst[q] = lds8h(kT + 32 * rt * GLT + 16 * (2 * kp + q));
+                for (int q = 0; q < 2; ++q) {
+                    lds_h *p = kT + 16 * (2 * kp + q) * GLK + 32 * rt;
+                    dst[q] = cat8(__builtin_bit_cast(h4, lds_tr4s(p)), __builtin_bit_cast(h4, lds_tr4s(p + 8 * GLK)));
+                }
             };
 
             f16v P[2][2];  // [tile][token tile 0-31, 32-63]
