@@ -804,6 +804,10 @@ __global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_f16_kernel(const De
 
     float *Tu = a.T_out + (int64_t)unit * D * D;
     float *Su = a.S0_out + (int64_t)unit * D * D;
+    // opaque lane offsets: keeps the output addresses from being formed before the
+    // chunk loop (they would be held, or spilled, across it)
+    int g4 = 4 * g, cl16 = r16;
+    asm volatile("" : "+v"(g4), "+v"(cl16));
 #pragma unroll
     for (int jn = 0; jn < 2; ++jn) {
         const int n = jn ? MT + w : w;
@@ -812,10 +816,10 @@ __global__ void __launch_bounds__((KdaCfg<D>::NT)) build_kda_f16_kernel(const De
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int row = 16 * mt + 4 * g + i;
+                const int row = 16 * mt + g4 + i;
                 const float val = ldexpf(X[mt][jn][i], (int)sig[jn]);
-                if (isS) Su[row * D + 16 * (n - MT) + r16] = val;
-                else     Tu[row * D + 16 * n + r16] = val;
+                if (isS) Su[row * D + 16 * (n - MT) + cl16] = val;
+                else     Tu[row * D + 16 * n + cl16] = val;
             }
     }
 }
