@@ -32,13 +32,13 @@
 //                    products): P (one tile at a time; the value term scaled
 //                    from the raw rows here), the two-block substitution for E,
 //                    and X += K^T E
-//   prep waves 4-7   chunk j (waves 5-7): the raw value rows and the key rows
-//                    (prefetched into registers, keys converted to fp16) to LDS;
-//                    gates (wave 7).  Chunk j-1: the four Gram tiles of G_10
-//                    (negated; waves 5 and 6) and, on wave 4, the four 16-row
-//                    diagonal inverses (one block per lane row, the multipliers
-//                    broadcast across the row by lane moves), the M'_ii and the
-//                    blocks -M'_b G_ba M'_a that join them into 32-row inverses
+//   prep waves 4-7   chunk j (waves 6 and 7, 32 rows each): the raw value rows
+//                    and the key rows (prefetched into registers, keys converted
+//                    to fp16) to LDS; gates (wave 7).  Chunk j-1: waves 4 and 5 each one
+//                    32-row inverse M'_ii (its two 16-row diagonal inverses, one
+//                    block per lane row with the multipliers broadcast across the
+//                    row by lane moves, joined by -M'_b G_ba M'_a); wave 6 the
+//                    32 x 32 block -G_10 in one 32 x 32 x 16 product
 // The reduction order of a 32 x 32 accumulator tile, read as an operand, runs
 // over rows 4a + {0..3} and 8 + 4a + {0..3} of each 16-block (lane half a), so
 // every operand fragment is two runs of four: the P product reads its key
@@ -195,15 +195,14 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
     // of a role lives inside its branch.  Both roles meet the same nch + 3 barriers.
     if (w >= 4) {
         // ------------------------------------------------------------ staging
-        // Prep waves 1-3 stage the chunk: wave 1 rows 0-23, wave 2 rows 24-47, wave 3
-        // rows 48-63 and the gates (wave 0 inverts and stages nothing).  Lane (g, r16)
-        // stages key rows rbase + nr g + q (q < nr), columns 8 r16 .. 8 r16 + 7, and value
-        // rows rbase + 4i + g (i < nr).
-        constexpr int MR = 6;
+        // Prep waves 2 and 3 stage the chunk, rows 0-31 and 32-63 (wave 3 also the
+        // gates); waves 0 and 1 form the inverses.  Lane (g, r16) stages key rows
+        // rbase + MR g + q, columns 8 r16 .. 8 r16 + 7, and value rows rbase + 4i + g.
+        constexpr int MR = 8;
         const int pw = w - 4;
-        const int nr = pw == 3 ? 4 : MR;
-        const int rbase = pw == 1 ? 0 : pw == 2 ? 24 : 48;
-        const int row0 = rbase + nr * g;
+        const bool stager = pw >= 2;
+        const int rbase = pw == 3 ? 32 : 0;
+        const int row0 = rbase + MR * g;
         // uniform row bases of the segment (64-bit) plus per-lane offsets inside a
         // chunk (32-bit: a chunk spans 64 rows)
         const TK *kb = reinterpret_cast<const TK *>(a.k) + a.tok0[s] * a.ldk + (int64_t)kh * GD;
@@ -245,7 +244,7 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
                 (void *)(vb + (int64_t)(64 * c) * ldv_b), (short)0, (int)((uint32_t)rows * ldv_b), HY_BUF_DW3);
 #pragma unroll
             for (int q = 0; q < MR; ++q)
-                if (q < nr) kraw[P][q].u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, (int)koff[q], 0, 0));
+                kraw[P][q].u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, (int)koff[q], 0, 0));
             if (pw == 3) {   // the gate wave
                 const uint32_t go = __umul24(min(lane, last), (unsigned)a.h_v);
                 const int64_t gc = (int64_t)(64 * c) * a.h_v;
@@ -257,7 +256,7 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
             // raw value rows rbase + 4i + g, the 16-byte piece r16 ^ 2 (t & 7) of row t
 #pragma unroll
             for (int i = 0; i < MR; ++i)
-                if (i < nr) vraw[P][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, (int)voff[i], 0, 0));
+                vraw[P][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, (int)voff[i], 0, 0));
         };
 
         double cl_lane = 0.0;
@@ -280,7 +279,7 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
             // value rows into slot sl: row rbase + 4i + g, piece position r16
 #pragma unroll
             for (int i = 0; i < MR; ++i)
-                if (i < nr) *reinterpret_cast<uint4 *>(&sm.Vr[sl][rbase + 4 * i + g][8 * r16]) = vraw[P][i];
+                *reinterpret_cast<uint4 *>(&sm.Vr[sl][rbase + 4 * i + g][8 * r16]) = vraw[P][i];
             if constexpr (decltype(tail)::value) {
 #pragma unroll
                 for (int q = 0; q < MR; ++q) mask_raw8(kraw[P][q], 64 * c + row0 + q < len);
@@ -288,7 +287,6 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
             // keys 8 r16 .. 8 r16 + 7 in fp16, one 16-byte store per row
 #pragma unroll
             for (int q = 0; q < MR; ++q) {
-                if (q >= nr) break;
                 float kx[8];
                 widen8(kraw[P][q], kx);
                 h8 k8;
@@ -298,75 +296,69 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
             }
         };
         // ------------------------------------------------------- prep: Gram, M'
-        // 16x16 Gram tile K_i K_j^T of slot sl (lane (g, r16), register i: row 4g + i,
-        // column r16); the stored key order is the same for both operands
-        auto gram_tile = [&](int sl, int ti, int tj) {
-            f4 acc = zero4();
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const h8 A = *reinterpret_cast<const h8 *>(&sm.Ks[sl][16 * ti + r16][32 * kb + 8 * g]);
-                const h8 B = *reinterpret_cast<const h8 *>(&sm.Ks[sl][16 * tj + r16][32 * kb + 8 * g]);
-                acc = mma(A, B, acc);
-            }
-            return acc;
-        };
-        // chunk c, prep waves 1 and 2: the Gram tiles (1 + pw, 0) and (1 + pw, 1) of the
-        // 16-row blocks, negated, into the -G_10 tile of the chunk's Mx slot (lane (g, r16)
-        // writes its four rows of column r16 as one run of the transposed tile)
-        auto prep_offgram = [&](int c) {
-            const int ms = c & 1, sl = c % 3;
-            const int ti = 1 + pw;
-#pragma unroll
-            for (int tj = 0; tj < 2; ++tj) {
-                const f4 acc = gram_tile(sl, ti, tj);
-                *reinterpret_cast<h4 *>(&sm.Mx[ms][2][16 * tj + r16][16 * (ti - 2) + 4 * g]) = cvt4(-acc);
-            }
-        };
-        // chunk c, prep wave 0: the four 16-row diagonal blocks.  Their Gram tiles go
-        // through LDS so that lane row g holds block g with one column per lane (G is
-        // symmetric); the inverse of I + A'_gg (A' = diag(b) strictlower(G)) follows by
-        // forward substitution, x_r += (-A'[r][q]) x_q, the multiplier taken from lane
-        // q of the row; M'_gg[r][c] = x_r b_c into the chunk's Mx slot (blocks 0, 1 form
-        // M'_00, blocks 2, 3 M'_11).  Then the lower left 16 x 16 block of each 32-row
-        // inverse, -M'_b G_ba M'_a for (a, b) = (0, 1) and (2, 3)
-        auto prep_diag = [&](int c) {
+        // chunk c, prep wave 2: -G_10, the 32 x 32 Gram block of tokens 32..63 against
+        // 0..31, in one 32 x 32 x 16 product (lane (l32, hh) of the result holds rows
+        // 8j + 4hh + e of column l32), written transposed, four rows per store
+        auto prep_g10 = [&](int c) {
             const int sl = c % 3, ms = c & 1;
-            h8 kf[4][4];   // [block][k block]: rows 16 b + r16 (each is both operands of its tile)
+            const int l32 = lane & 31, hh = lane >> 5;
+            f16v acc = f16v{};
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+            for (int ks = 0; ks < 8; ++ks) {
+                const h8 A = *reinterpret_cast<const h8 *>(&sm.Ks[sl][32 + l32][16 * ks + 8 * hh]);
+                const h8 B = *reinterpret_cast<const h8 *>(&sm.Ks[sl][l32][16 * ks + 8 * hh]);
+                acc = mma32(A, B, acc);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<h4 *>(&sm.Mx[ms][2][l32][8 * j + 4 * hh]) =
+                    h4{(_Float16)(-acc[4 * j]), (_Float16)(-acc[4 * j + 1]), (_Float16)(-acc[4 * j + 2]), (_Float16)(-acc[4 * j + 3])};
+        };
+        // chunk c, prep wave p (0 or 1): the 32-row inverse M'_pp from the 16-row blocks
+        // a = 2p, b = 2p + 1.  Their Gram tiles go through LDS so that lane row g holds
+        // block 2p + (g & 1) with one column per lane (G is symmetric; rows 2 and 3
+        // repeat rows 0 and 1); the inverse of I + A'_bb (A' = diag(b) strictlower(G))
+        // follows by forward substitution, x_r += (-A'[r][q]) x_q, the multiplier taken
+        // from lane q of the row; M'_bb[r][c] = x_r b_c into the chunk's Mx slot.  Then
+        // the lower left 16 x 16 block, -M'_b G_ba M'_a.
+        auto prep_diag = [&](int c) {
+            const int sl = c % 3, ms = c & 1, p = pw;
+            h8 kf[2][4];   // [block a or b][k block]: rows 16 (2p + e) + r16
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb)
-                    kf[b][kb] = *reinterpret_cast<const h8 *>(&sm.Ks[sl][16 * b + r16][32 * kb + 8 * g]);
+                    kf[e][kb] = *reinterpret_cast<const h8 *>(&sm.Ks[sl][16 * (2 * p + e) + r16][32 * kb + 8 * g]);
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
+            for (int e = 0; e < 2; ++e) {
                 f4 acc = zero4();   // lane (g, r16), register i: G_b[4g + i][r16]
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) acc = mma(kf[b][kb], kf[b][kb], acc);
-                *reinterpret_cast<float4 *>(&sm.Gd[b][r16][4 * g]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                for (int kb = 0; kb < 4; ++kb) acc = mma(kf[e][kb], kf[e][kb], acc);
+                *reinterpret_cast<float4 *>(&sm.Gd[2 * p + e][r16][4 * g]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
             }
-            // G_ab for (a, b) = (0, 1), (2, 3): lane (g, r16) holds G_ab[4g + i][r16] =
-            // G_ba[r16][4g + i], which is G_ba's operand layout on the left of a product
-            h4 Gba[2];
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
+            // G_ab: lane (g, r16) holds G_ab[4g + i][r16] = G_ba[r16][4g + i], which is
+            // G_ba's operand layout on the left of a product
+            h4 Gba;
+            {
                 f4 acc = zero4();
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) acc = mma(kf[2 * p][kb], kf[2 * p + 1][kb], acc);
-                Gba[p] = cvt4(acc);
+                for (int kb = 0; kb < 4; ++kb) acc = mma(kf[0][kb], kf[1][kb], acc);
+                Gba = cvt4(acc);
             }
             wave_lds_fence();
-            // lane (g, c): G_g[r][c] = Gd[g][c][r], r = 0..15; the rows' write strengths
+            // lane (g, c): G_blk[r][c] = Gd[blk][c][r], r = 0..15; the rows' write strengths
+            const int e = g & 1, blk = 2 * p + e;
             float n[16];
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const float4 gv = *reinterpret_cast<const float4 *>(&sm.Gd[g][r16][4 * r4]);
-                const float4 bv = *reinterpret_cast<const float4 *>(&sm.beta[sl][16 * g + 4 * r4]);
+                const float4 gv = *reinterpret_cast<const float4 *>(&sm.Gd[blk][r16][4 * r4]);
+                const float4 bv = *reinterpret_cast<const float4 *>(&sm.beta[sl][16 * blk + 4 * r4]);
                 n[4 * r4 + 0] = -bv.x * gv.x;
                 n[4 * r4 + 1] = -bv.y * gv.y;
                 n[4 * r4 + 2] = -bv.z * gv.z;
                 n[4 * r4 + 3] = -bv.w * gv.w;
             }
-            const float bc = sm.beta[sl][16 * g + r16];
+            const float bc = sm.beta[sl][16 * blk + r16];
             float x[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) x[r] = r == r16 ? 1.f : 0.f;
@@ -374,37 +366,34 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
             for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(n[r]));   // n complete here
             asm volatile("s_nop 1");   // the two wait states before the lane moves read n
             subst_steps<0>(x, n);
-            {
-                // column r16 of block g, rows 0..15: one contiguous run of the transposed tile
-                const int blk = g >> 1, off = 16 * (g & 1);
+            if (g < 2) {
+                // column r16 of block blk, rows 0..15: one contiguous run of the transposed tile
+                const int off = 16 * e;
                 h8 lo, hi;
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
                     lo[r] = (_Float16)(x[r] * bc);
                     hi[r] = (_Float16)(x[8 + r] * bc);
                 }
-                *reinterpret_cast<h8 *>(&sm.Mx[ms][blk][off + r16][off]) = lo;
-                *reinterpret_cast<h8 *>(&sm.Mx[ms][blk][off + r16][off + 8]) = hi;
+                *reinterpret_cast<h8 *>(&sm.Mx[ms][p][off + r16][off]) = lo;
+                *reinterpret_cast<h8 *>(&sm.Mx[ms][p][off + r16][off + 8]) = hi;
             }
             wave_lds_fence();
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                // T = G_ba M'_a: lane (g, j) holds M'_a[4g .. 4g + 3][j], contiguous in the
-                // transposed tile, and so T
-                const h4 Ma = *reinterpret_cast<const h4 *>(&sm.Mx[ms][p][r16][4 * g]);
-                const f4 T = mma16(Gba[p], Ma, zero4());
-                // L = -M'_b T: lane (r16, g) holds M'_b[r16][4g .. 4g + 3] through the
-                // transposing load; lane (g, j) writes L[4g .. 4g + 3][j] as one run
-                const h4 Mb = tr4(&sm.Mx[ms][p][0][0], GLM, 16 + 4 * g, 16, lane);
-                const f4 L = mma16(Mb, cvt4(T), zero4());
-                *reinterpret_cast<h4 *>(&sm.Mx[ms][p][r16][16 + 4 * g]) = cvt4(-L);
-            }
+            // T = G_ba M'_a: lane (g, j) holds M'_a[4g .. 4g + 3][j], contiguous in the
+            // transposed tile, and so T
+            const h4 Ma = *reinterpret_cast<const h4 *>(&sm.Mx[ms][p][r16][4 * g]);
+            const f4 T = mma16(Gba, Ma, zero4());
+            // L = -M'_b T: lane (r16, g) holds M'_b[r16][4g .. 4g + 3] through the
+            // transposing load; lane (g, j) writes L[4g .. 4g + 3][j] as one run
+            const h4 Mb = tr4(&sm.Mx[ms][p][0][0], GLM, 16 + 4 * g, 16, lane);
+            const f4 L = mma16(Mb, cvt4(T), zero4());
+            *reinterpret_cast<h4 *>(&sm.Mx[ms][p][r16][16 + 4 * g]) = cvt4(-L);
         };
 
         const std::false_type full;
         const std::true_type tail;
         const std::integral_constant<int, 0> p0;
-        if (pw != 0 && nch > 0) fetch(0, p0);
+        if (stager && nch > 0) fetch(0, p0);
         // iteration j: chunk j's gates, keys and value rows from the registers, then the
         // prefetch of chunk j + 1 into them (in flight across the barrier, waited for where
         // the next step first uses it), then chunk j-1's transposed keys, Gram tiles and
@@ -414,7 +403,7 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
             lds_barrier();
             // this chunk's prefetch landed before the barrier: claim its registers now,
             // so no later wait covers the loads issued below
-            if (pw != 0) {
+            if (stager) {
 #pragma unroll
                 for (int q = 0; q < MR; ++q) claim(kraw[P][q]);
 #pragma unroll
@@ -425,19 +414,16 @@ __global__ void __launch_bounds__(512) build_gdn_kernel(const DeltaArgs a)
                 claim(araw[P]);
                 claim(vrs[P]);
             }
-            if (pw != 0) {
+            if (stager) {
                 if (j < nch - 1) stage(j, pc, full);
                 else if (j == nch - 1) stage(j, pc, tail);
             }
             // the next chunk's prefetch reuses the registers just staged (one buffer:
             // the loads still have the rest of this step and the barrier to land)
-            if (pw != 0 && j + 1 < nch) fetch(j + 1, pc);
+            if (stager && j + 1 < nch) fetch(j + 1, pc);
             if (j >= 1 && j <= nch) {
-                if (pw == 0) {
-                    prep_diag(j - 1);
-                } else {
-                    if (pw < 3) prep_offgram(j - 1);
-                }
+                if (pw < 2) prep_diag(j - 1);
+                else if (pw == 2) prep_g10(j - 1);
             }
         };
         for (int j = 0; j < nch + 2; ++j) iter(j, p0);
