@@ -205,10 +205,14 @@ __global__ void __launch_bounds__((CgCfg<D, NN>::NT)) compose_group_kernel(const
                 hwq = pos >= 1;
                 const float *o = win_rec(pos);
                 const bool rin = hwq && srow < w;
-                if (do_w) Wq = *reinterpret_cast<const float4 *>(o + (int64_t)(rin ? srow : 0) * D + scol);
-                if (do_k) Kq = *reinterpret_cast<const float4 *>(o + (int64_t)wp * D + (int64_t)(rin ? srow : 0) * D + scol);
+                // this thread's offset inside a record, formed here (opaque) rather than held
+                // across the position loop
+                int ro = (rin ? srow : 0) * D + scol;
+                asm volatile("" : "+v"(ro));
+                if (do_w) Wq = *reinterpret_cast<const float4 *>(o + ro);
+                if (do_k) Kq = *reinterpret_cast<const float4 *>(o + (int64_t)wp * D + ro);
                 if constexpr (RO)
-                    if (do_w) Rq = *reinterpret_cast<const float4 *>(o + (int64_t)3 * wp * D + (int64_t)(rin ? srow : 0) * D + scol);
+                    if (do_w) Rq = *reinterpret_cast<const float4 *>(o + (int64_t)3 * wp * D + ro);
                 if (!rin) { Wq = z4; Kq = z4; Rq = z4; }
                 gwq = hwq ? o[winop_gw<D>(w, RO)] : 1.f;
             }
@@ -315,8 +319,11 @@ __global__ void __launch_bounds__((CgCfg<D, NN>::NT)) compose_group_kernel(const
                         // rows 4g + i >= 8 of P are Y rows t = 4g + i - 8 (their E rows meet
                         // zero key columns below)
                         if (hwc && g >= 2) {
-                            float *yp = Y + ((int64_t)(a.first_pos + j - 1) * a.h_v + h) * 8 * 2 * D +
-                                        (int64_t)(4 * g - WR) * 2 * D + (TH ? 0 : D) + cb + r16;
+                            // the lane's offset is formed here (opaque), so the compiler does not
+                            // hold a 64-bit lane address across the position loop
+                            int yo = (4 * g - WR) * 2 * D + (TH ? 0 : D) + cb + r16;
+                            asm volatile("" : "+v"(yo));
+                            float *yp = Y + ((int64_t)(a.first_pos + j - 1) * a.h_v + h) * 8 * 2 * D + yo;
 #pragma unroll
                             for (int q = 0; q < 2; ++q)
 #pragma unroll
