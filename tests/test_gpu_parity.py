@@ -243,6 +243,25 @@ def test_delta_key_scale(d, log2r):
     _check_build(wl, label=f"key norm 2^{log2r}")
 
 
+def test_delta_value_scale_jumps():
+    """Values whose scale jumps between 64-token chunks by exact powers of two
+    (bf16, d = 128): up 2^12 (the state's unit follows the values), down 2^20,
+    up 2^70 (far past the unit), and a segment whose first chunk is at 2^80.
+    Every change of the state's unit is an exact power-of-two rescaling, so
+    T_C and S0 stay within the contract bound of the oracle."""
+    need_gpu()
+    import dataclasses
+    base = synth.gdn(630, [1024, 300, 200], 1, 2, 128, torch.bfloat16, alpha_div=32.0)
+    ex = np.zeros(sum(base.seg_len))
+    for c, e in enumerate([0, 0, 12, 12, -8, -8, 62, 62, 62, 70, 70, 70, 70, 70, 70, 70]):
+        ex[64 * c:64 * (c + 1)] = e
+    ex[1024:1088] = 80
+    ex[1324:1524] = 20
+    f = torch.tensor(np.exp2(ex), dtype=torch.float32)[:, None, None]
+    wl = dataclasses.replace(base, v=(base.v.float() * f).to(torch.bfloat16), name="gdn-value-jumps")
+    _check_build(wl, label="value scale jumps")
+
+
 # ---------------------------------------------------------------- compose only
 
 @pytest.mark.parametrize("tform,prec", [("dense", 0), ("dense", 1), ("diag", 0), ("scalar", 0)])
